@@ -1,0 +1,233 @@
+/*
+ * dbf.h -- C ABI of the MI355X (gfx950) drafter block forward library (libdbf.so).
+ *
+ * The library runs the speculative-decoding drafter hot path in hand-written HIP
+ * kernels: the drafter block forward over M = K+1 token rows, the lm_head with a
+ * per-row argmax, the greedy accept-prefix walk, and KV-cache rollback.
+ *
+ * Sources (hf2q 0.1.1 source pages on docs.rs):
+ *   [MTP]  src/inference/models/qwen35/mtp.rs
+ *   [TENS] src/inference/spec_decode/dflash/tensors.rs
+ *   [ORCH] src/inference/spec_decode/dflash/qwen35_orchestrator.rs
+ *
+ * Conventions
+ *   - Every pointer named "device" is HIP device memory (or memory the device can
+ *     read); the caller allocates and owns every buffer. The library allocates no
+ *     device memory and keeps no pointer after a call returns; buffers must stay
+ *     alive until the stream has executed the enqueued work.
+ *   - `stream` is a hipStream_t passed as void*. Entry points enqueue on it and
+ *     never synchronize, so a caller may capture them into a HIP graph.
+ *   - All arguments are validated on the host before anything is enqueued: on an
+ *     error nothing runs and the KV cache (including seq_len) is unchanged. The
+ *     return value is 0 or a negative DBF_E* code; dbf_last_error() describes it.
+ *   - Tensors are row-major and contiguous. Projection weights are BF16 [out, in]
+ *     with no transpose ([TENS] module doc and `DFlashLayerTensors`); every RMSNorm
+ *     weight is F32 ([TENS] `DFlashLayerTensors`, "DType policy": a BF16 buffer
+ *     read by an F32 norm kernel silently corrupts and reads out of bounds, so a
+ *     norm weight of any other dtype is rejected with DBF_EDTYPE).
+ *   - Inner (input) dimensions of every projection must be multiples of 8 (the
+ *     kernels stream weights in 16-byte vectors); DBF_ESHAPE otherwise.
+ */
+#ifndef DBF_H
+#define DBF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBF_ABI_VERSION 1
+
+/* status codes */
+#define DBF_OK 0
+#define DBF_EINVAL -1    /* null pointer, or a count outside its range (M, R, K, ...) */
+#define DBF_ESHAPE -2    /* a tensor's ndim/shape disagrees with the config */
+#define DBF_EDTYPE -3    /* a tensor or cache has the wrong dtype */
+#define DBF_ERANGE -4    /* KV capacity exceeded, or a rollback larger than seq_len */
+#define DBF_EWORKSPACE -5 /* workspace missing, too small or not 256-byte aligned */
+#define DBF_EHIP -6      /* a HIP runtime call failed (message in dbf_last_error) */
+
+/* dtypes */
+#define DBF_F32 0
+#define DBF_BF16 1
+#define DBF_I32 2
+
+/* block kinds */
+#define DBF_KIND_DFLASH 0 /* DFlash drafter ([TENS] `DFlashModelTensors`) */
+#define DBF_KIND_MTP 1    /* Qwen3.5 MTP block ([MTP] `MtpWeights`) */
+
+/* FFN kinds ([MTP] `MtpFfnWeightsGpu`) */
+#define DBF_FFN_DENSE 0
+#define DBF_FFN_MOE 1
+
+#define DBF_MAX_M 16   /* block rows per call (K+1 <= 16) */
+#define DBF_MAX_R 16   /* new context rows per call */
+#define DBF_MAX_TOPK 16
+
+/* Non-owning view of a device tensor: row-major, contiguous. */
+typedef struct {
+    void *data;
+    int32_t dtype; /* DBF_F32 | DBF_BF16 | DBF_I32 */
+    int32_t ndim;
+    int64_t shape[4];
+} dbf_tensor;
+
+/* Model shape. ([MTP] `Qwen35Config` fields used by `forward_full_attention`;
+ * [TENS] `DFlashLayerTensors` shapes.) */
+typedef struct {
+    int32_t kind;            /* DBF_KIND_DFLASH | DBF_KIND_MTP */
+    int32_t n_layers;        /* decoder layers in the block (>= 1) */
+    int32_t hidden;          /* H */
+    int32_t n_q_heads;       /* nq */
+    int32_t n_kv_heads;      /* nkv, divides nq (GQA groups are contiguous) */
+    int32_t head_dim;        /* hd, even, <= 256 */
+    int32_t rotary_dim;      /* rotated lanes per head, even, <= hd; 0 means hd */
+    int32_t intermediate;    /* dense SwiGLU width I */
+    int32_t n_target_hidden; /* DFlash: target hidden states concatenated into fc */
+    int32_t vocab;           /* V (embedding rows for the token gather) */
+    int32_t ffn_kind;        /* DBF_FFN_DENSE | DBF_FFN_MOE */
+    int32_t n_experts;       /* MoE: E */
+    int32_t top_k;           /* MoE: experts kept per row, <= min(E, DBF_MAX_TOPK) */
+    int32_t expert_intermediate; /* MoE: per-expert SwiGLU width */
+    int32_t shared_intermediate; /* MoE: shared-expert SwiGLU width */
+    int32_t has_attn_gate;   /* 1: o *= sigmoid(x Wg^T) before O ([MTP] `w_gate`) */
+    double rms_eps;          /* RMSNorm eps of every norm except MTP enorm/hnorm (fixed 1e-6) */
+    double rope_theta;       /* RoPE base */
+} dbf_config;
+
+/* Per-layer weights. Unused members (by kind/ffn_kind/has_attn_gate) are ignored
+ * and may be zero. Shapes: in_norm, post_norm [H] F32; wq [nq*hd, H];
+ * wk, wv [nkv*hd, H]; attn_gate [nq*hd, H]; wo [H, nq*hd]; q_norm, k_norm [hd] F32;
+ * dense: ffn_gate, ffn_up [I, H], ffn_down [H, I];
+ * MoE: router [E, H], exp_gate, exp_up [E, Ie, H], exp_down [E, H, Ie],
+ *      sh_gate, sh_up [Is, H], sh_down [H, Is], sh_gate_inp [1, H].
+ * All projections BF16. */
+typedef struct {
+    dbf_tensor in_norm, post_norm;
+    dbf_tensor wq, wk, wv, attn_gate, wo;
+    dbf_tensor q_norm, k_norm;
+    dbf_tensor ffn_gate, ffn_up, ffn_down;
+    dbf_tensor router, exp_gate, exp_up, exp_down;
+    dbf_tensor sh_gate, sh_up, sh_down, sh_gate_inp;
+} dbf_layer_weights;
+
+/* Block weights. DFlash: fc [H, n_t*H] BF16, hidden_norm [H] F32.
+ * MTP: enorm, hnorm [H] F32, eh_embed, eh_hidden [H, H] BF16.
+ * final_norm [H] F32 (DFlash `norm`; MTP `shared_head_norm`).
+ * embed [V, H] BF16: only read when block tokens are given (shared with the
+ * target, [TENS] module doc). `layers` is a HOST array of n_layers entries. */
+typedef struct {
+    dbf_tensor fc, hidden_norm;
+    dbf_tensor enorm, hnorm, eh_embed, eh_hidden;
+    const dbf_layer_weights *layers;
+    dbf_tensor final_norm;
+    dbf_tensor embed;
+} dbf_weights;
+
+/* KV cache, caller-owned: k and v are device arrays [n_layers][n_kv_heads]
+ * [capacity][head_dim] of dtype F32 or BF16. Row p of a head holds the key/value
+ * of position p. seq_len (host metadata) is the number of valid positions. */
+typedef struct {
+    void *k;
+    void *v;
+    int32_t dtype;
+    int32_t n_layers, n_kv_heads, head_dim;
+    int64_t capacity;
+    int64_t seq_len;
+} dbf_kv_cache;
+
+/* Block inputs/outputs (device pointers).
+ *   tokens      [M] int32 or NULL. DFlash only: rows are embed[tokens[i]]
+ *               ([ORCH] per-round steps 1-2: [last_token, mask x K]). Ids are
+ *               clamped into [0, V).
+ *   x0          [M, H] F32 block rows when tokens == NULL (MTP: embed_t).
+ *   ctx         DFlash: [R, n_t*H] F32 concatenated target hidden states of the R
+ *               new context rows (may be NULL when R == 0).
+ *               MTP: prev_hidden [M, H] F32 (required).
+ *   M           block rows, 1..DBF_MAX_M.  R: new context rows, 0..DBF_MAX_R
+ *               (MTP: must be 0).
+ *   hidden_out  [M, H] F32 pre-norm hidden of the last layer, or NULL.
+ *   h_final     [M, H] F32 final-normed hidden (required).
+ *   layer_hidden [n_layers, M, H] F32 hidden after each layer, or NULL. */
+typedef struct {
+    const int32_t *tokens;
+    const float *x0;
+    const float *ctx;
+    int32_t M, R;
+    float *hidden_out;
+    float *h_final;
+    float *layer_hidden;
+} dbf_block_io;
+
+/* Drafter block forward ([MTP] `forward_draft_with_hidden` and its helpers
+ * `project_embedding_and_hidden`, `forward_full_attention`,
+ * `forward_ffn_residual`, `forward_shared_head` up to the norm; [TENS]
+ * `DFlashModelTensors` for the DFlash input projection and per-layer tensors;
+ * [ORCH] per-round step 4 for the block call with new context rows).
+ *
+ * Input: DFlash x = embed[tokens] (or x0), h_ctx = RMSNorm(ctx fc^T, hidden_norm);
+ * MTP x = RMSNorm(x0, enorm) eh_embed^T + RMSNorm(ctx, hnorm) eh_hidden^T.
+ * Each layer: RMSNorm, Q/K/V (+gate) projections, per-head RMSNorm of q and k,
+ * RoPE, K/V stored in the cache, GQA attention (q head h uses kv head
+ * h*nkv/nq) over cache rows [0, P0+R+i] for block row i (causal within the
+ * block), optional sigmoid gate, O projection + residual, RMSNorm, SwiGLU or
+ * MoE FFN + residual. Then h_final = RMSNorm(x, final_norm).
+ * DFlash context rows go through each layer's wk/wv, k_norm and RoPE (no input
+ * norm) and are stored at positions P0..P0+R-1; block rows at P0+R+i, where P0 =
+ * cache->seq_len on entry. On success cache->seq_len += R + M (a DFlash drafter
+ * that keeps only context rows calls kv_rollback(cache, M) afterwards).
+ *
+ * ws: device workspace of at least draft_block_workspace_bytes(cfg, M, R) bytes,
+ * 256-byte aligned, contents irrelevant on entry. Calls sharing a workspace must
+ * be ordered on one stream. */
+int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cache *cache,
+                        const dbf_block_io *io, void *ws, size_t ws_bytes, void *stream);
+
+size_t draft_block_workspace_bytes(const dbf_config *cfg, int32_t M, int32_t R);
+
+/* lm_head + per-row argmax ([ORCH] per-round step 5, per-position argmax over the
+ * drafter's normed hidden through the target lm_head; [MTP] `forward_shared_head`).
+ *   h          [M, H] F32 device, already normed; M in 1..DBF_MAX_M.
+ *   lm_head    BF16 [V, H].
+ *   argmax     [M] int32 device out: index of the largest logit of each row, the
+ *              lowest index among equal maxima.
+ *   logits     [M, V] F32 device out, or NULL (written only on request).
+ *   top2_margin [M] F32 device out, or NULL: largest logit minus the largest
+ *              logit at any other index (0 on a tie).
+ * Non-finite logits give an unspecified argmax.
+ * ws: at least lm_head_argmax_workspace_bytes(M, H, V) bytes, 256-byte aligned. */
+int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head,
+                   int32_t *argmax, float *logits, float *top2_margin, void *ws,
+                   size_t ws_bytes, void *stream);
+
+size_t lm_head_argmax_workspace_bytes(int32_t M, int32_t H, int32_t V);
+
+/* Greedy accept-prefix walk ([ORCH] module doc, "Greedy accept-walk consistency
+ * invariant", and per-round steps 7-8). Device pointers:
+ *   drafts [K] int32, target [K+1] int32 (the target's argmax at each position),
+ *   eos [n_eos] int32 or NULL when n_eos == 0.
+ *   result [5] int32 out: {accept_count a, free_token = target[a],
+ *          rollback = K - a, hit_eos, n_committed}.
+ *   committed [K+1] int32 out or NULL: target[0..a] (the accepted drafts then the
+ *          free token), cut after the first EOS (inclusive; hit_eos = 1 then).
+ * a is the length of the longest prefix with drafts[i] == target[i]; EOS does not
+ * change a or rollback. K in 1..1024. One wavefront; enqueued only. */
+int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const int32_t *eos,
+                  int32_t n_eos, int32_t *result, int32_t *committed, void *stream);
+
+/* KV rollback ([ORCH] per-round step 8: drop the rejected positions). Host-side
+ * metadata only: cache->seq_len -= n. DBF_ERANGE when n < 0 or n > seq_len. */
+int kv_rollback(dbf_kv_cache *cache, int32_t n);
+
+/* Description of the last error on the calling thread ("" when none). */
+const char *dbf_last_error(void);
+
+int dbf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBF_H */

@@ -1,0 +1,181 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol, and
+rejects bad arguments before anything touches the GPU (no device is used here:
+every call below fails validation before the first HIP call)."""
+import ctypes as C
+
+import pytest
+
+from verifier_block_forward_amd import configs, dbf
+
+
+def test_exports_every_declared_symbol():
+    names = dbf.declared_functions()
+    assert set(names) >= {"draft_block_forward", "lm_head_argmax", "accept_prefix", "kv_rollback",
+                          "draft_block_workspace_bytes", "lm_head_argmax_workspace_bytes",
+                          "dbf_last_error", "dbf_abi_version"}
+    for n in names:
+        assert hasattr(dbf.lib(), n), n
+    assert dbf.abi_version() == 1
+
+
+def _cfg(name="c0", **kw):
+    c = dbf.make_config(configs.get(name))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_sizes():
+    for name in ("c0", "c1", "c2", "c3"):
+        bc = configs.get(name)
+        n = dbf.draft_block_workspace_bytes(_cfg(name), bc.M, bc.R)
+        assert n > 0 and n % 256 == 0
+    assert dbf.draft_block_workspace_bytes(_cfg(), 0, 0) == 0
+    assert dbf.draft_block_workspace_bytes(_cfg(), 17, 0) == 0
+    assert dbf.draft_block_workspace_bytes(_cfg(head_dim=96), 4, 4) == 0
+    assert dbf.lm_head_argmax_workspace_bytes(16, 2816, 262144) > 0
+    assert dbf.lm_head_argmax_workspace_bytes(0, 2816, 262144) == 0
+
+
+def _fake(n=0x1000):
+    return C.c_void_p(n)
+
+
+def _call_block(cfg, io, cache=None, w=None, ws=0x100000, ws_bytes=1 << 40):
+    L = cfg.n_layers
+    if w is None:
+        w = dbf.Weights()
+    cache = cache or dbf.KVCache(k=0x2000, v=0x3000, dtype=dbf.F32, n_layers=L,
+                                 n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, capacity=100,
+                                 seq_len=10)
+    rc = dbf.lib().draft_block_forward(C.byref(cfg), C.byref(w), C.byref(cache), C.byref(io),
+                                       C.c_void_p(ws), ws_bytes, None)
+    return rc, cache
+
+
+def test_block_argument_errors():
+    cfg = _cfg()
+    h = 0x4000
+    assert _call_block(cfg, dbf.BlockIO(M=0, R=0, h_final=h, x0=h))[0] == dbf.EINVAL
+    assert _call_block(cfg, dbf.BlockIO(M=17, R=0, h_final=h, x0=h))[0] == dbf.EINVAL
+    assert _call_block(cfg, dbf.BlockIO(M=4, R=17, h_final=h, x0=h, ctx=h))[0] == dbf.EINVAL
+    assert _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=None, x0=h))[0] == dbf.EINVAL
+    assert _call_block(cfg, dbf.BlockIO(M=4, R=2, h_final=h, x0=h, ctx=None))[0] == dbf.EINVAL
+    # weights missing -> EINVAL (null data), config problems first
+    rc, cache = _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=h, x0=h))
+    assert rc == dbf.EINVAL and "null" in dbf.last_error()
+    assert cache.seq_len == 10
+    bad = _cfg(kind=7)
+    assert _call_block(bad, dbf.BlockIO(M=4, R=0, h_final=h, x0=h))[0] == dbf.EINVAL
+    assert _call_block(_cfg(n_kv_heads=3), dbf.BlockIO(M=4, R=0, h_final=h, x0=h))[0] == dbf.ESHAPE
+    assert _call_block(_cfg(hidden=260), dbf.BlockIO(M=4, R=0, h_final=h, x0=h))[0] == dbf.ESHAPE
+    mtp = _cfg("c2")
+    assert _call_block(mtp, dbf.BlockIO(M=1, R=1, h_final=h, x0=h, ctx=h))[0] == dbf.EINVAL
+
+
+def _weights_for(bc, dtype_override=None):
+    """Struct of fake device pointers with correct dtypes/shapes (never dereferenced)."""
+    w = dbf.Weights()
+    H = bc.hidden
+
+    def T(shape, dt):
+        t = dbf.Tensor()
+        t.data = 0x10000
+        t.dtype = dt
+        t.ndim = len(shape)
+        for i, s in enumerate(shape):
+            t.shape[i] = s
+        return t
+    w.fc = T((H, bc.n_target_hidden * H), dbf.BF16)
+    w.hidden_norm = T((H,), dbf.F32)
+    w.final_norm = T((H,), dbf.F32)
+    w.embed = T((bc.vocab, H), dbf.BF16)
+    layers = (dbf.LayerWeights * bc.n_layers)()
+    for i in range(bc.n_layers):
+        L = layers[i]
+        L.in_norm = T((H,), dbf.F32)
+        L.post_norm = T((H,), dbf.F32)
+        L.wq = T((bc.q_total, H), dbf.BF16)
+        L.wk = T((bc.kv_total, H), dbf.BF16)
+        L.wv = T((bc.kv_total, H), dbf.BF16)
+        L.wo = T((H, bc.q_total), dbf.BF16)
+        L.q_norm = T((bc.head_dim,), dbf.F32)
+        L.k_norm = T((bc.head_dim,), dbf.F32)
+        L.ffn_gate = T((bc.intermediate, H), dbf.BF16)
+        L.ffn_up = T((bc.intermediate, H), dbf.BF16)
+        L.ffn_down = T((H, bc.intermediate), dbf.BF16)
+    w.layers = layers
+    return w, layers
+
+
+def test_dtype_policy_rejects_bf16_norm():
+    """A BF16 norm weight is refused (the tensors.rs dtype policy: norms are F32)."""
+    bc = configs.C0
+    cfg = dbf.make_config(bc)
+    w, layers = _weights_for(bc)
+    layers[0].q_norm.dtype = dbf.BF16
+    rc, cache = _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=0x4000, x0=0x4000), w=w)
+    assert rc == dbf.EDTYPE and "q_norm" in dbf.last_error()
+    layers[0].q_norm.dtype = dbf.F32
+    layers[0].wq.dtype = dbf.F32
+    assert _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=0x4000, x0=0x4000), w=w)[0] == dbf.EDTYPE
+    layers[0].wq.dtype = dbf.BF16
+    layers[0].wk.shape[0] = 7
+    assert _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=0x4000, x0=0x4000), w=w)[0] == dbf.ESHAPE
+
+
+def test_cache_and_workspace_errors():
+    bc = configs.C0
+    cfg = dbf.make_config(bc)
+    w, layers = _weights_for(bc)
+    io = dbf.BlockIO(M=4, R=4, h_final=0x4000, x0=0x4000, ctx=0x4000)
+    full = dbf.KVCache(k=0x2000, v=0x3000, dtype=dbf.F32, n_layers=1, n_kv_heads=2, head_dim=64,
+                       capacity=40, seq_len=33)
+    rc, c = _call_block(cfg, io, cache=full, w=w)
+    assert rc == dbf.ERANGE and c.seq_len == 33
+    badt = dbf.KVCache(k=0x2000, v=0x3000, dtype=dbf.I32, n_layers=1, n_kv_heads=2, head_dim=64,
+                       capacity=100, seq_len=3)
+    assert _call_block(cfg, io, cache=badt, w=w)[0] == dbf.EDTYPE
+    shp = dbf.KVCache(k=0x2000, v=0x3000, dtype=dbf.F32, n_layers=2, n_kv_heads=2, head_dim=64,
+                      capacity=100, seq_len=3)
+    assert _call_block(cfg, io, cache=shp, w=w)[0] == dbf.ESHAPE
+    ok = dbf.KVCache(k=0x2000, v=0x3000, dtype=dbf.F32, n_layers=1, n_kv_heads=2, head_dim=64,
+                     capacity=100, seq_len=3)
+    assert _call_block(cfg, io, cache=ok, w=w, ws_bytes=16)[0] == dbf.EWORKSPACE
+    assert _call_block(cfg, io, cache=ok, w=w, ws=0x100010)[0] == dbf.EWORKSPACE
+    assert ok.seq_len == 3
+
+
+def test_head_accept_rollback_errors():
+    L = dbf.lib()
+    t = dbf.Tensor()
+    t.data = 0x1000
+    t.dtype = dbf.F32
+    t.ndim = 2
+    t.shape[0], t.shape[1] = 100, 64
+    rc = L.lm_head_argmax(C.c_void_p(0x2000), 4, 64, C.byref(t), C.c_void_p(0x3000), None, None,
+                          C.c_void_p(0x100000), 1 << 30, None)
+    assert rc == dbf.EDTYPE
+    t.dtype = dbf.BF16
+    t.shape[1] = 32
+    assert L.lm_head_argmax(C.c_void_p(0x2000), 4, 64, C.byref(t), C.c_void_p(0x3000), None, None,
+                            C.c_void_p(0x100000), 1 << 30, None) == dbf.ESHAPE
+    t.shape[1] = 64
+    assert L.lm_head_argmax(C.c_void_p(0x2000), 0, 64, C.byref(t), C.c_void_p(0x3000), None, None,
+                            C.c_void_p(0x100000), 1 << 30, None) == dbf.EINVAL
+    assert L.lm_head_argmax(C.c_void_p(0x2000), 4, 64, C.byref(t), C.c_void_p(0x3000), None, None,
+                            C.c_void_p(0x100000), 8, None) == dbf.EWORKSPACE
+    assert L.accept_prefix(C.c_void_p(1), C.c_void_p(1), 0, None, 0, C.c_void_p(1), None, None) == dbf.EINVAL
+    assert L.accept_prefix(C.c_void_p(1), C.c_void_p(1), 1025, None, 0, C.c_void_p(1), None, None) == dbf.EINVAL
+    assert L.accept_prefix(C.c_void_p(1), C.c_void_p(1), 4, None, 2, C.c_void_p(1), None, None) == dbf.EINVAL
+    assert L.accept_prefix(None, C.c_void_p(1), 4, None, 0, C.c_void_p(1), None, None) == dbf.EINVAL
+    kv = dbf.KVCache(seq_len=10, capacity=20)
+    with pytest.raises(dbf.DbfError) as e:
+        dbf.kv_rollback(kv, 11)
+    assert e.value.code == dbf.ERANGE and kv.seq_len == 10
+    with pytest.raises(dbf.DbfError):
+        dbf.kv_rollback(kv, -1)
+    dbf.kv_rollback(kv, 4)
+    assert kv.seq_len == 6
+    dbf.kv_rollback(kv, 6)
+    assert kv.seq_len == 0

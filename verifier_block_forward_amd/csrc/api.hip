@@ -1,0 +1,511 @@
+// api.hip -- the C ABI of libdbf (include/dbf.h): argument validation, workspace
+// planning and the launch sequence of the drafter block.
+//
+// Everything is validated before the first enqueue, so an error leaves the stream
+// and the cache untouched. No C++ exception crosses the ABI.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/dbf.h"
+#include "internal.hpp"
+#include "kernels.hpp"
+
+using namespace dbf;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+const char *dtname(int dt) { return dt == DBF_F32 ? "F32" : dt == DBF_BF16 ? "BF16" : dt == DBF_I32 ? "I32" : "?"; }
+
+int check_t(const dbf_tensor &t, const char *name, int dtype, int ndim, int64_t s0, int64_t s1 = -1,
+            int64_t s2 = -1) {
+    if (!t.data) return fail(DBF_EINVAL, "%s: null data pointer", name);
+    if (t.dtype != dtype)
+        return fail(DBF_EDTYPE, "%s: dtype %s, expected %s", name, dtname(t.dtype), dtname(dtype));
+    const int64_t want[3] = {s0, s1, s2};
+    if (t.ndim != ndim) return fail(DBF_ESHAPE, "%s: ndim %d, expected %d", name, t.ndim, ndim);
+    for (int i = 0; i < ndim; i++)
+        if (t.shape[i] != want[i])
+            return fail(DBF_ESHAPE, "%s: shape[%d] = %lld, expected %lld", name, i,
+                        (long long)t.shape[i], (long long)want[i]);
+    return DBF_OK;
+}
+
+#define CHECK(expr)                \
+    do {                           \
+        int rc_ = (expr);          \
+        if (rc_ != DBF_OK) return rc_; \
+    } while (0)
+
+constexpr int TARGET_UNITS = 2048;  // wave units per projection launch (256 CUs x 8)
+constexpr int GEMM_NA = 2;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// workspace plan
+// ---------------------------------------------------------------------------
+struct Plan {
+    int H, qt, kt, I, Kin, rd;
+    GemmPlan in, q, k, v, g, o, gate, up, down;
+    size_t xres, x1, xs_blk, xs_T, xs_hctx, xs_h, xs_o, xs_ff, qbuf, gbuf, attn;
+    size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_o, p_gate, p_up, p_down;
+    size_t total;
+};
+
+Plan make_plan(const dbf_config &c, int M, int R) {
+    Plan p{};
+    (void)M;
+    p.H = c.hidden;
+    p.qt = c.n_q_heads * c.head_dim;
+    p.kt = c.n_kv_heads * c.head_dim;
+    p.I = c.intermediate;
+    p.Kin = c.kind == DBF_KIND_DFLASH ? c.n_target_hidden * c.hidden : c.hidden;
+    p.rd = c.rotary_dim > 0 ? c.rotary_dim : c.head_dim;
+    const int na = GEMM_NA;
+    p.in = gemm_plan(p.H, p.Kin, na, c.kind == DBF_KIND_MTP ? TARGET_UNITS / 2 : TARGET_UNITS);
+    // Q, K, V (and gate) share one launch: split the unit budget by row counts
+    p.q = gemm_plan(p.qt, p.H, na, TARGET_UNITS / 2);
+    p.k = gemm_plan(p.kt, p.H, na, TARGET_UNITS / 4);
+    p.v = p.k;
+    p.g = p.q;
+    p.o = gemm_plan(p.H, p.qt, na, TARGET_UNITS);
+    p.gate = gemm_plan(p.I, p.H, na, TARGET_UNITS / 2);
+    p.up = p.gate;
+    p.down = gemm_plan(p.H, p.I, na, TARGET_UNITS);
+    const int rows_kv = R > 0 ? 32 : 16;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    const size_t f = sizeof(float);
+    p.xres = take((size_t)DBF_MAX_M * p.H * f);
+    p.x1 = take((size_t)DBF_MAX_M * p.H * f);
+    p.xs_blk = take(split_tile_bytes(p.H));
+    p.xs_T = take(split_tile_bytes(p.Kin));
+    p.xs_hctx = take(split_tile_bytes(p.H));
+    p.xs_h = take(split_tile_bytes(p.H));
+    p.xs_o = take(split_tile_bytes(p.qt));
+    p.xs_ff = take(split_tile_bytes(p.I > 0 ? p.I : 32));
+    p.qbuf = take((size_t)DBF_MAX_M * p.qt * f);
+    p.gbuf = take((size_t)DBF_MAX_M * p.qt * f);
+    p.attn = take((size_t)64 * DBF_MAX_M * c.n_q_heads * (c.head_dim + 2) * f);
+    p.p_in0 = take((size_t)p.in.ksplit * 16 * p.H * f);
+    p.p_in1 = take((size_t)p.in.ksplit * 16 * p.H * f);
+    p.p_q = take((size_t)p.q.ksplit * 16 * p.qt * f);
+    p.p_k = take((size_t)p.k.ksplit * rows_kv * p.kt * f);
+    p.p_v = take((size_t)p.v.ksplit * rows_kv * p.kt * f);
+    p.p_g = take((size_t)p.g.ksplit * 16 * p.qt * f);
+    p.p_o = take((size_t)p.o.ksplit * 16 * p.H * f);
+    p.p_gate = take((size_t)p.gate.ksplit * 16 * (p.I > 0 ? p.I : 1) * f);
+    p.p_up = take((size_t)p.up.ksplit * 16 * (p.I > 0 ? p.I : 1) * f);
+    p.p_down = take((size_t)p.down.ksplit * 16 * p.H * f);
+    p.total = off;
+    return p;
+}
+
+struct SegList {
+    GemmArgs a{};
+    int nbmax = 1;
+    void add(const uint16_t *W, int N, int K, const GemmPlan &pl, float *out, const uint16_t *xs0,
+             const uint16_t *xs1 = nullptr) {
+        GemmSeg &s = a.seg[a.nseg++];
+        s.W = W;
+        s.out = out;
+        s.xs0 = xs0;
+        s.xs1 = xs1;
+        s.N = N;
+        s.K = K;
+        s.nb = xs1 ? 2 : 1;
+        s.ksplit = pl.ksplit;
+        s.kslice_steps = pl.kslice_steps;
+        s.tiles = pl.tiles;
+        s.unit_begin = a.total_units;
+        a.total_units += pl.tiles * pl.ksplit;
+        if (s.nb > nbmax) nbmax = s.nb;
+    }
+    void launch(hipStream_t st) { launch_gemm(a, GEMM_NA, nbmax, st); }
+};
+
+int validate_config(const dbf_config *c) {
+    if (!c) return fail(DBF_EINVAL, "config is null");
+    if (c->kind != DBF_KIND_DFLASH && c->kind != DBF_KIND_MTP)
+        return fail(DBF_EINVAL, "config.kind %d unknown", c->kind);
+    if (c->n_layers < 1 || c->hidden < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+        c->head_dim < 2 || c->vocab < 1)
+        return fail(DBF_EINVAL, "config: non-positive dimension");
+    if (c->hidden % 8) return fail(DBF_ESHAPE, "config.hidden %d not a multiple of 8", c->hidden);
+    if (c->n_q_heads % c->n_kv_heads)
+        return fail(DBF_ESHAPE, "n_q_heads %d not a multiple of n_kv_heads %d", c->n_q_heads,
+                    c->n_kv_heads);
+    if (!attn_supported(c->head_dim))
+        return fail(DBF_ESHAPE, "head_dim %d unsupported (64, 128 or 256)", c->head_dim);
+    const int rd = c->rotary_dim > 0 ? c->rotary_dim : c->head_dim;
+    if (rd % 2 || rd > c->head_dim) return fail(DBF_ESHAPE, "rotary_dim %d invalid", rd);
+    if (c->kind == DBF_KIND_DFLASH && c->n_target_hidden < 1)
+        return fail(DBF_EINVAL, "DFlash config needs n_target_hidden >= 1");
+    if (c->ffn_kind == DBF_FFN_DENSE) {
+        if (c->intermediate < 8 || c->intermediate % 8)
+            return fail(DBF_ESHAPE, "intermediate %d must be a positive multiple of 8", c->intermediate);
+    } else if (c->ffn_kind == DBF_FFN_MOE) {
+        return fail(DBF_EINVAL, "MoE FFN not available in this build");
+    } else {
+        return fail(DBF_EINVAL, "ffn_kind %d unknown", c->ffn_kind);
+    }
+    if (!(c->rms_eps >= 0.0) || !(c->rope_theta > 0.0))
+        return fail(DBF_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
+    return DBF_OK;
+}
+
+int validate_weights(const dbf_config &c, const dbf_weights *w, bool need_embed) {
+    if (!w) return fail(DBF_EINVAL, "weights are null");
+    const int H = c.hidden, qt = c.n_q_heads * c.head_dim, kt = c.n_kv_heads * c.head_dim;
+    const int hd = c.head_dim;
+    if (c.kind == DBF_KIND_DFLASH) {
+        CHECK(check_t(w->fc, "fc", DBF_BF16, 2, H, (int64_t)c.n_target_hidden * H));
+        CHECK(check_t(w->hidden_norm, "hidden_norm", DBF_F32, 1, H));
+        if (need_embed) CHECK(check_t(w->embed, "embed", DBF_BF16, 2, c.vocab, H));
+    } else {
+        CHECK(check_t(w->enorm, "enorm", DBF_F32, 1, H));
+        CHECK(check_t(w->hnorm, "hnorm", DBF_F32, 1, H));
+        CHECK(check_t(w->eh_embed, "eh_embed", DBF_BF16, 2, H, H));
+        CHECK(check_t(w->eh_hidden, "eh_hidden", DBF_BF16, 2, H, H));
+    }
+    CHECK(check_t(w->final_norm, "final_norm", DBF_F32, 1, H));
+    if (!w->layers) return fail(DBF_EINVAL, "weights.layers is null");
+    for (int l = 0; l < c.n_layers; l++) {
+        const dbf_layer_weights &L = w->layers[l];
+        char nm[64];
+#define T(field, ...)                                              \
+    snprintf(nm, sizeof nm, "layers[%d]." #field, l);              \
+    CHECK(check_t(L.field, nm, __VA_ARGS__));
+        T(in_norm, DBF_F32, 1, H);
+        T(post_norm, DBF_F32, 1, H);
+        T(wq, DBF_BF16, 2, qt, H);
+        T(wk, DBF_BF16, 2, kt, H);
+        T(wv, DBF_BF16, 2, kt, H);
+        T(wo, DBF_BF16, 2, H, qt);
+        T(q_norm, DBF_F32, 1, hd);
+        T(k_norm, DBF_F32, 1, hd);
+        if (c.has_attn_gate) { T(attn_gate, DBF_BF16, 2, qt, H); }
+        if (c.ffn_kind == DBF_FFN_DENSE) {
+            T(ffn_gate, DBF_BF16, 2, c.intermediate, H);
+            T(ffn_up, DBF_BF16, 2, c.intermediate, H);
+            T(ffn_down, DBF_BF16, 2, H, c.intermediate);
+        }
+#undef T
+    }
+    return DBF_OK;
+}
+
+int hip_check(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DBF_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return DBF_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return (T *)((char *)ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dbf_abi_version(void) { return DBF_ABI_VERSION; }
+
+const char *dbf_last_error(void) { return g_err.c_str(); }
+
+size_t draft_block_workspace_bytes(const dbf_config *cfg, int32_t M, int32_t R) {
+    if (validate_config(cfg) != DBF_OK) return 0;
+    if (M < 1 || M > DBF_MAX_M || R < 0 || R > DBF_MAX_R) return 0;
+    return make_plan(*cfg, M, R).total;
+}
+
+int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cache *cache,
+                        const dbf_block_io *io, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    CHECK(validate_config(cfg));
+    const dbf_config &c = *cfg;
+    if (!io) return fail(DBF_EINVAL, "io is null");
+    const int M = io->M, R = io->R;
+    if (M < 1 || M > DBF_MAX_M) return fail(DBF_EINVAL, "M = %d outside [1, %d]", M, DBF_MAX_M);
+    if (R < 0 || R > DBF_MAX_R) return fail(DBF_EINVAL, "R = %d outside [0, %d]", R, DBF_MAX_R);
+    if (c.kind == DBF_KIND_MTP && R != 0) return fail(DBF_EINVAL, "MTP block takes no context rows (R = %d)", R);
+    if (!io->h_final) return fail(DBF_EINVAL, "io.h_final is null");
+    if (c.kind == DBF_KIND_DFLASH) {
+        if (!io->tokens && !io->x0) return fail(DBF_EINVAL, "io: neither tokens nor x0 given");
+        if (R > 0 && !io->ctx) return fail(DBF_EINVAL, "io.ctx is null with R = %d", R);
+    } else {
+        if (!io->x0) return fail(DBF_EINVAL, "io.x0 (embed_t) is null");
+        if (!io->ctx) return fail(DBF_EINVAL, "io.ctx (prev_hidden) is null");
+    }
+    CHECK(validate_weights(c, w, c.kind == DBF_KIND_DFLASH && io->tokens));
+    if (!cache || !cache->k || !cache->v) return fail(DBF_EINVAL, "cache or its buffers are null");
+    if (cache->dtype != DBF_F32 && cache->dtype != DBF_BF16)
+        return fail(DBF_EDTYPE, "cache dtype %s (F32 or BF16)", dtname(cache->dtype));
+    if (cache->n_layers != c.n_layers || cache->n_kv_heads != c.n_kv_heads ||
+        cache->head_dim != c.head_dim)
+        return fail(DBF_ESHAPE, "cache shape [%d, %d, *, %d] does not match the config",
+                    cache->n_layers, cache->n_kv_heads, cache->head_dim);
+    if (cache->seq_len < 0 || cache->capacity < 0)
+        return fail(DBF_ERANGE, "cache seq_len/capacity negative");
+    if (cache->seq_len + R + M > cache->capacity)
+        return fail(DBF_ERANGE, "cache overflow: seq_len %lld + R %d + M %d > capacity %lld",
+                    (long long)cache->seq_len, R, M, (long long)cache->capacity);
+    const Plan p = make_plan(c, M, R);
+    if (!ws) return fail(DBF_EWORKSPACE, "workspace is null");
+    if ((uintptr_t)ws % 256) return fail(DBF_EWORKSPACE, "workspace not 256-byte aligned");
+    if (ws_bytes < p.total)
+        return fail(DBF_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const int H = p.H, qt = p.qt, kt = p.kt, hd = c.head_dim;
+    const float eps = (float)c.rms_eps;
+    const long long P0 = cache->seq_len;
+    float *xres = at<float>(ws, p.xres), *x1 = at<float>(ws, p.x1);
+    uint16_t *xs_blk = at<uint16_t>(ws, p.xs_blk), *xs_T = at<uint16_t>(ws, p.xs_T);
+    uint16_t *xs_hctx = at<uint16_t>(ws, p.xs_hctx), *xs_h = at<uint16_t>(ws, p.xs_h);
+    uint16_t *xs_o = at<uint16_t>(ws, p.xs_o), *xs_ff = at<uint16_t>(ws, p.xs_ff);
+    float *qbuf = at<float>(ws, p.qbuf), *gbuf = at<float>(ws, p.gbuf);
+    float *attn_part = at<float>(ws, p.attn);
+    const dbf_layer_weights *Ls = w->layers;
+
+    // ---- input projection
+    if (c.kind == DBF_KIND_DFLASH) {
+        launch_input_dflash(io->tokens, io->x0, (const uint16_t *)w->embed.data, c.vocab, M, H,
+                            (const float *)Ls[0].in_norm.data, eps, xres, xs_blk, st);
+        if (R > 0) {
+            launch_split_rows(io->ctx, R, p.Kin, p.Kin, xs_T, st);
+            SegList sl;
+            sl.add((const uint16_t *)w->fc.data, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
+            sl.launch(st);
+            launch_hctx(at<float>(ws, p.p_in0), p.in.ksplit, R, H, (const float *)w->hidden_norm.data,
+                        eps, xs_hctx, st);
+        }
+    } else {
+        launch_mtp_input(io->x0, io->ctx, M, H, (const float *)w->enorm.data,
+                         (const float *)w->hnorm.data, xs_blk, xs_h, st);
+        SegList sl;
+        sl.add((const uint16_t *)w->eh_embed.data, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
+        sl.add((const uint16_t *)w->eh_hidden.data, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
+        sl.launch(st);
+        SumNormArgs sn{};
+        sn.p0 = at<float>(ws, p.p_in0);
+        sn.ks0 = p.in.ksplit;
+        sn.rows0 = 16;
+        sn.p1 = at<float>(ws, p.p_in1);
+        sn.ks1 = p.in.ksplit;
+        sn.rows1 = 16;
+        sn.out = xres;
+        sn.w = (const float *)Ls[0].in_norm.data;
+        sn.eps = eps;
+        sn.xs = xs_blk;
+        sn.M = M;
+        sn.H = H;
+        launch_sum_norm_split(sn, st);
+    }
+
+    int chunk = 0, n_chunks = 0;
+    attn_plan(P0 + R + M, &chunk, &n_chunks);
+    const size_t elt = cache->dtype == DBF_BF16 ? 2 : 4;
+    const size_t layer_stride = (size_t)c.n_kv_heads * cache->capacity * hd * elt;
+
+    for (int l = 0; l < c.n_layers; l++) {
+        const dbf_layer_weights &L = Ls[l];
+        float *pq = at<float>(ws, p.p_q), *pk = at<float>(ws, p.p_k), *pv = at<float>(ws, p.p_v);
+        float *pg = at<float>(ws, p.p_g);
+        {
+            SegList sl;
+            sl.add((const uint16_t *)L.wq.data, qt, H, p.q, pq, xs_blk);
+            if (R > 0) {
+                sl.add((const uint16_t *)L.wk.data, kt, H, p.k, pk, xs_hctx, xs_blk);
+                sl.add((const uint16_t *)L.wv.data, kt, H, p.v, pv, xs_hctx, xs_blk);
+            } else {
+                sl.add((const uint16_t *)L.wk.data, kt, H, p.k, pk, xs_blk);
+                sl.add((const uint16_t *)L.wv.data, kt, H, p.v, pv, xs_blk);
+            }
+            if (c.has_attn_gate) sl.add((const uint16_t *)L.attn_gate.data, qt, H, p.g, pg, xs_blk);
+            sl.launch(st);
+        }
+        void *ck = (char *)cache->k + l * layer_stride;
+        void *cv = (char *)cache->v + l * layer_stride;
+        {
+            QkvPostArgs qa{};
+            qa.pq = pq;
+            qa.pk = pk;
+            qa.pv = pv;
+            qa.pg = c.has_attn_gate ? pg : nullptr;
+            qa.ksq = p.q.ksplit;
+            qa.ksk = p.k.ksplit;
+            qa.ksv = p.v.ksplit;
+            qa.ksg = p.g.ksplit;
+            qa.rows_kv = R > 0 ? 32 : 16;
+            qa.kv_block_row0 = R > 0 ? 16 : 0;
+            qa.q_norm = (const float *)L.q_norm.data;
+            qa.k_norm = (const float *)L.k_norm.data;
+            qa.eps = eps;
+            qa.theta = c.rope_theta;
+            qa.rotary_dim = p.rd;
+            qa.M = M;
+            qa.R = R;
+            qa.nq = c.n_q_heads;
+            qa.nkv = c.n_kv_heads;
+            qa.hd = hd;
+            qa.P0 = P0;
+            qa.q_out = qbuf;
+            qa.g_out = c.has_attn_gate ? gbuf : nullptr;
+            qa.cache_k = ck;
+            qa.cache_v = cv;
+            qa.kv_bf16 = cache->dtype == DBF_BF16;
+            qa.capacity = cache->capacity;
+            launch_qkv_post(qa, st);
+        }
+        {
+            AttnArgs aa{};
+            aa.q = qbuf;
+            aa.cache_k = ck;
+            aa.cache_v = cv;
+            aa.kv_bf16 = cache->dtype == DBF_BF16;
+            aa.capacity = cache->capacity;
+            aa.n_ctx = P0 + R;
+            aa.M = M;
+            aa.nq = c.n_q_heads;
+            aa.nkv = c.n_kv_heads;
+            aa.hd = hd;
+            aa.chunk = chunk;
+            aa.n_chunks = n_chunks;
+            aa.part = attn_part;
+            launch_attn(aa, st);
+            CombineArgs ca{};
+            ca.part = attn_part;
+            ca.n_chunks = n_chunks;
+            ca.M = M;
+            ca.nq = c.n_q_heads;
+            ca.hd = hd;
+            ca.g = c.has_attn_gate ? gbuf : nullptr;
+            ca.xs = xs_o;
+            launch_attn_combine(ca, st);
+        }
+        {
+            SegList sl;
+            sl.add((const uint16_t *)L.wo.data, H, qt, p.o, at<float>(ws, p.p_o), xs_o);
+            sl.launch(st);
+            SumNormArgs sn{};
+            sn.base = xres;
+            sn.p0 = at<float>(ws, p.p_o);
+            sn.ks0 = p.o.ksplit;
+            sn.rows0 = 16;
+            sn.out = x1;
+            sn.w = (const float *)L.post_norm.data;
+            sn.eps = eps;
+            sn.xs = xs_blk;
+            sn.M = M;
+            sn.H = H;
+            launch_sum_norm_split(sn, st);
+        }
+        {
+            SegList sl;
+            sl.add((const uint16_t *)L.ffn_gate.data, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
+            sl.add((const uint16_t *)L.ffn_up.data, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
+            sl.launch(st);
+            launch_swiglu_split(at<float>(ws, p.p_gate), p.gate.ksplit, at<float>(ws, p.p_up),
+                                p.up.ksplit, M, p.I, xs_ff, st);
+            SegList sd;
+            sd.add((const uint16_t *)L.ffn_down.data, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
+            sd.launch(st);
+        }
+        {
+            const bool last = l == c.n_layers - 1;
+            SumNormArgs sn{};
+            sn.base = x1;
+            sn.p0 = at<float>(ws, p.p_down);
+            sn.ks0 = p.down.ksplit;
+            sn.rows0 = 16;
+            sn.out = xres;
+            sn.copy0 = io->layer_hidden ? io->layer_hidden + (size_t)l * M * H : nullptr;
+            sn.copy1 = last ? io->hidden_out : nullptr;
+            sn.w = last ? (const float *)w->final_norm.data : (const float *)Ls[l + 1].in_norm.data;
+            sn.eps = eps;
+            sn.normed = last ? io->h_final : nullptr;
+            sn.xs = xs_blk;
+            sn.M = M;
+            sn.H = H;
+            launch_sum_norm_split(sn, st);
+        }
+    }
+    CHECK(hip_check("draft_block_forward launch"));
+    cache->seq_len = P0 + R + M;
+    return DBF_OK;
+}
+
+size_t lm_head_argmax_workspace_bytes(int32_t M, int32_t H, int32_t V) {
+    if (M < 1 || M > DBF_MAX_M || H < 8 || V < 1) return 0;
+    return align256(split_tile_bytes(H)) + align256((size_t)head_units(V) * 16 * sizeof(float4));
+}
+
+int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, int32_t *argmax,
+                   float *logits, float *top2_margin, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!h || !lm_head || !argmax) return fail(DBF_EINVAL, "h, lm_head and argmax are required");
+    if (M < 1 || M > DBF_MAX_M) return fail(DBF_EINVAL, "M = %d outside [1, %d]", M, DBF_MAX_M);
+    if (H < 8 || H % 8) return fail(DBF_ESHAPE, "H = %d must be a positive multiple of 8", H);
+    if (lm_head->ndim != 2 || lm_head->shape[1] != H || lm_head->shape[0] < 1)
+        return fail(DBF_ESHAPE, "lm_head must be [V, %d]", H);
+    if (lm_head->dtype != DBF_BF16) return fail(DBF_EDTYPE, "lm_head dtype %s, expected BF16", dtname(lm_head->dtype));
+    if (!lm_head->data) return fail(DBF_EINVAL, "lm_head data is null");
+    if (lm_head->shape[0] > 0x7fffffffLL) return fail(DBF_ESHAPE, "vocabulary too large");
+    const int V = (int)lm_head->shape[0];
+    const size_t need = lm_head_argmax_workspace_bytes(M, H, V);
+    if (!ws) return fail(DBF_EWORKSPACE, "workspace is null");
+    if ((uintptr_t)ws % 256) return fail(DBF_EWORKSPACE, "workspace not 256-byte aligned");
+    if (ws_bytes < need) return fail(DBF_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    uint16_t *xs = (uint16_t *)ws;
+    float4 *part = at<float4>(ws, align256(split_tile_bytes(H)));
+    launch_split_rows(h, M, H, H, xs, st);
+    launch_head((const uint16_t *)lm_head->data, xs, V, H, M, logits, part, st);
+    launch_head_reduce(part, head_units(V), M, argmax, top2_margin, st);
+    return hip_check("lm_head_argmax launch");
+}
+
+int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const int32_t *eos,
+                  int32_t n_eos, int32_t *result, int32_t *committed, void *stream) {
+    g_err.clear();
+    if (!drafts || !target || !result) return fail(DBF_EINVAL, "drafts, target and result are required");
+    if (K < 1 || K > 1024) return fail(DBF_EINVAL, "K = %d outside [1, 1024]", K);
+    if (n_eos < 0 || (n_eos > 0 && !eos)) return fail(DBF_EINVAL, "eos list invalid (n_eos = %d)", n_eos);
+    (void)hipGetLastError();
+    launch_accept(drafts, target, K, eos, n_eos, result, committed, (hipStream_t)stream);
+    return hip_check("accept_prefix launch");
+}
+
+int kv_rollback(dbf_kv_cache *cache, int32_t n) {
+    g_err.clear();
+    if (!cache) return fail(DBF_EINVAL, "cache is null");
+    if (n < 0 || (int64_t)n > cache->seq_len)
+        return fail(DBF_ERANGE, "rollback of %d rows from seq_len %lld", n, (long long)cache->seq_len);
+    cache->seq_len -= n;
+    return DBF_OK;
+}
+
+}  // extern "C"

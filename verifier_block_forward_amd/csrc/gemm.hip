@@ -1,0 +1,311 @@
+// gemm.hip -- skinny BF16-weight projections on the gfx950 matrix cores.
+//
+// Y[m, o] = sum_k X[m, k] W[o, k]: BF16 weights [out, in] times F32 activations
+// with F32 accumulation (the weight/activation dtype policy of the hf2q 0.1.1
+// page spec_decode/dflash/tensors.rs, `DFlashLayerTensors`). The block has at most
+// 16 (or 32, with context rows) activation rows, so every projection is a weight
+// stream: bytes, not flops, set its speed.
+//
+// Mapping: a wavefront owns 16*NA consecutive weight rows and a slice of the
+// input dimension. Per k-step of 32 columns, lane l loads 16 bytes of row
+// (l % 16) at columns 8*(l/16)..+7 of each of its NA row tiles (each row gets 64
+// contiguous bytes per step, 128 per pair of steps), plus the pre-split
+// activation hi/lo halves (two coalesced 1 KiB reads shared by all NA tiles), and
+// issues 2*NA*NB v_mfma_f32_16x16x32_bf16. MFMA A = weights (16 rows x 32 k),
+// B = activations (32 k x 16 rows), D[4*(l/16)+j][l%16] = Y[row, m].
+#include "internal.hpp"
+#include "kernels.hpp"
+
+namespace dbf {
+
+__device__ __forceinline__ bf16x8 ld16(const uint16_t *p) {
+    return __builtin_bit_cast(bf16x8, *(const uint4 *)p);
+}
+
+__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16((a), (b), (c), 0, 0, 0)
+
+// Accumulate the NA x NB tile product over k-steps [s0, s1).
+template <int NA, int NB>
+__device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA],
+                                                const uint16_t *const xs[NB], int K, int s0,
+                                                int s1, int lane, f32x4 acc[NA][NB]) {
+    const int g = lane >> 4;
+    const int full = K >> 5;  // k-steps fully inside K
+    int s = s0;
+    const int s_end_full = s1 < full ? s1 : full;
+    // main part: two k-steps per iteration (128 contiguous bytes per weight row)
+    for (; s + 1 < s_end_full; s += 2) {
+        bf16x8 w0[NA], w1[NA], xh0[NB], xl0[NB], xh1[NB], xl1[NB];
+#pragma unroll
+        for (int a = 0; a < NA; a++) {
+            w0[a] = ld16(wrow[a] + 32 * s);
+            w1[a] = ld16(wrow[a] + 32 * s + 32);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const uint16_t *x = xs[b] + ((size_t)s * 2 * 64 + lane) * 8;
+            xh0[b] = ld16(x);
+            xl0[b] = ld16(x + 64 * 8);
+            xh1[b] = ld16(x + 2 * 64 * 8);
+            xl1[b] = ld16(x + 3 * 64 * 8);
+        }
+#pragma unroll
+        for (int a = 0; a < NA; a++)
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                acc[a][b] = MFMA(w0[a], xh0[b], acc[a][b]);
+                acc[a][b] = MFMA(w0[a], xl0[b], acc[a][b]);
+                acc[a][b] = MFMA(w1[a], xh1[b], acc[a][b]);
+                acc[a][b] = MFMA(w1[a], xl1[b], acc[a][b]);
+            }
+    }
+    // remaining steps one at a time; the last one may run past K (K % 32 != 0)
+    for (; s < s1; s++) {
+        const bool in = (32 * s + 8 * g) < K;
+        bf16x8 w0[NA], xh[NB], xl[NB];
+#pragma unroll
+        for (int a = 0; a < NA; a++) w0[a] = in ? ld16(wrow[a] + 32 * s) : zero8();
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const uint16_t *x = xs[b] + ((size_t)s * 2 * 64 + lane) * 8;
+            xh[b] = ld16(x);
+            xl[b] = ld16(x + 64 * 8);
+        }
+#pragma unroll
+        for (int a = 0; a < NA; a++)
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                acc[a][b] = MFMA(w0[a], xh[b], acc[a][b]);
+                acc[a][b] = MFMA(w0[a], xl[b], acc[a][b]);
+            }
+    }
+}
+
+template <int NA, int NB>
+__global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
+    const int lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= args.total_units) return;
+    int si = 0;
+#pragma unroll 1
+    for (int i = 1; i < args.nseg; i++)
+        if (unit >= args.seg[i].unit_begin) si = i;
+    const GemmSeg &sg = args.seg[si];
+    const int local = unit - sg.unit_begin;
+    const int tile = local % sg.tiles;
+    const int ks = local / sg.tiles;
+    const int N = sg.N, K = sg.K;
+    const int S = (K + 31) >> 5;
+    const int s0 = ks * sg.kslice_steps;
+    int s1 = s0 + sg.kslice_steps;
+    if (s1 > S) s1 = S;
+    const int r = lane & 15, g = lane >> 4;
+    const int row0 = tile * 16 * NA;
+
+    const uint16_t *wrow[NA];
+#pragma unroll
+    for (int a = 0; a < NA; a++) {
+        int row = row0 + 16 * a + r;
+        if (row > N - 1) row = N - 1;  // ragged last tile: re-read a valid row, result dropped
+        wrow[a] = sg.W + (size_t)row * K + 8 * g;
+    }
+    const uint16_t *xs[NB];
+    xs[0] = sg.xs0;
+    if (NB > 1) xs[NB - 1] = sg.nb > 1 ? sg.xs1 : sg.xs0;
+
+    f32x4 acc[NA][NB];
+#pragma unroll
+    for (int a = 0; a < NA; a++)
+#pragma unroll
+        for (int b = 0; b < NB; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (NB == 2 && sg.nb == 1) {
+        const uint16_t *xs1[1] = {sg.xs0};
+        f32x4 acc1[NA][1];
+#pragma unroll
+        for (int a = 0; a < NA; a++) acc1[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        skinny_mainloop<NA, 1>(wrow, xs1, K, s0, s1, lane, acc1);
+#pragma unroll
+        for (int a = 0; a < NA; a++) acc[a][0] = acc1[a][0];
+    } else {
+        skinny_mainloop<NA, NB>(wrow, xs, K, s0, s1, lane, acc);
+    }
+
+    const int nb = NB == 1 ? 1 : sg.nb;
+    float *out = sg.out + (size_t)ks * 16 * nb * N;
+#pragma unroll
+    for (int a = 0; a < NA; a++)
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            if (b >= nb) continue;
+            const int m = 16 * b + r;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int o = row0 + 16 * a + 4 * g + j;
+                if (o < N) out[(size_t)m * N + o] = acc[a][b][j];
+            }
+        }
+}
+
+GemmPlan gemm_plan(int N, int K, int na, int target_units) {
+    GemmPlan p;
+    p.tiles = (N + 16 * na - 1) / (16 * na);
+    const int S = (K + 31) / 32;
+    int ks = (target_units + p.tiles - 1) / p.tiles;
+    int max_ks = S / 4;  // keep at least 4 k-steps (128 columns) per slice
+    if (max_ks < 1) max_ks = 1;
+    if (ks > max_ks) ks = max_ks;
+    if (ks < 1) ks = 1;
+    int steps = (S + ks - 1) / ks;
+    steps = (steps + 1) & ~1;  // even: slices start on 128-byte boundaries
+    p.kslice_steps = steps;
+    p.ksplit = (S + steps - 1) / steps;
+    return p;
+}
+
+template <int NA, int NB>
+static void go(const GemmArgs &a, hipStream_t s) {
+    const int blocks = (a.total_units + 3) / 4;
+    hipLaunchKernelGGL((k_gemm_splitk<NA, NB>), dim3(blocks), dim3(256), 0, s, a);
+}
+
+void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s) {
+    if (a.total_units <= 0) return;
+    if (nbmax == 1) {
+        if (na == 1) go<1, 1>(a, s);
+        else if (na == 2) go<2, 1>(a, s);
+        else go<4, 1>(a, s);
+    } else {
+        if (na == 1) go<1, 2>(a, s);
+        else if (na == 2) go<2, 2>(a, s);
+        else go<4, 2>(a, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// lm_head with a top-2 epilogue. Each wave unit covers 64 vocabulary rows over the
+// full hidden dimension and emits, for each of the 16 activation rows, the best
+// (value, index) and the second-best value among its rows. Ties keep the lower
+// index. Optional logits are written row-major [M][V].
+// ---------------------------------------------------------------------------
+struct Top2 {
+    float v1;
+    int i1;
+    float v2;
+};
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ Top2 merge(Top2 a, Top2 b) {
+    Top2 r;
+    if (better(a.v1, a.i1, b.v1, b.i1)) {
+        r.v1 = a.v1;
+        r.i1 = a.i1;
+        r.v2 = fmaxf(a.v2, b.v1);
+    } else {
+        r.v1 = b.v1;
+        r.i1 = b.i1;
+        r.v2 = fmaxf(b.v2, a.v1);
+    }
+    return r;
+}
+
+__device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
+    Top2 o;
+    o.v1 = __shfl_xor(t.v1, mask, 64);
+    o.i1 = __shfl_xor(t.i1, mask, 64);
+    o.v2 = __shfl_xor(t.v2, mask, 64);
+    return o;
+}
+
+__global__ __launch_bounds__(256) void k_head(const uint16_t *__restrict__ W,
+                                              const uint16_t *__restrict__ xs, int V, int K,
+                                              int M, float *__restrict__ logits,
+                                              float4 *__restrict__ part, int units) {
+    constexpr int NA = HEAD_NA;
+    const int lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= units) return;
+    const int r = lane & 15, g = lane >> 4;
+    const int row0 = unit * 16 * NA;
+    const uint16_t *wrow[NA];
+#pragma unroll
+    for (int a = 0; a < NA; a++) {
+        int row = row0 + 16 * a + r;
+        if (row > V - 1) row = V - 1;
+        wrow[a] = W + (size_t)row * K + 8 * g;
+    }
+    const uint16_t *xsp[1] = {xs};
+    f32x4 acc[NA][1];
+#pragma unroll
+    for (int a = 0; a < NA; a++) acc[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    skinny_mainloop<NA, 1>(wrow, xsp, K, 0, (K + 31) >> 5, lane, acc);
+
+    // lane holds rows o = row0 + 16a + 4g + j for activation row m = r
+    Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+    for (int a = 0; a < NA; a++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int o = row0 + 16 * a + 4 * g + j;
+            if (o < V) {
+                Top2 c{acc[a][0][j], o, -INFINITY};
+                t = merge(t, c);
+            }
+        }
+    if (logits && r < M) {
+#pragma unroll
+        for (int a = 0; a < NA; a++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int o = row0 + 16 * a + 4 * g + j;
+                if (o < V) logits[(size_t)r * V + o] = acc[a][0][j];
+            }
+    }
+    t = merge(t, shfl_top2(t, 16));
+    t = merge(t, shfl_top2(t, 32));
+    if (g == 0) part[(size_t)unit * 16 + r] = make_float4(t.v1, __int_as_float(t.i1), t.v2, 0.f);
+}
+
+int head_units(int V) { return (V + 16 * HEAD_NA - 1) / (16 * HEAD_NA); }
+
+void launch_head(const uint16_t *W, const uint16_t *xs, int V, int K, int M, float *logits,
+                 float4 *part, hipStream_t s) {
+    const int units = head_units(V);
+    hipLaunchKernelGGL(k_head, dim3((units + 3) / 4), dim3(256), 0, s, W, xs, V, K, M, logits,
+                       part, units);
+}
+
+// one block per activation row: fold every unit's top-2 record
+__global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ part, int units,
+                                                     int32_t *__restrict__ argmax,
+                                                     float *__restrict__ margin) {
+    const int m = blockIdx.x;
+    Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+    for (int u = threadIdx.x; u < units; u += 256) {
+        float4 p = part[(size_t)u * 16 + m];
+        Top2 c{p.x, __float_as_int(p.y), p.z};
+        t = merge(t, c);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) t = merge(t, shfl_top2(t, o));
+    __shared__ Top2 sh[4];
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Top2 r = merge(merge(sh[0], sh[1]), merge(sh[2], sh[3]));
+        argmax[m] = r.i1;
+        if (margin) margin[m] = r.v1 - r.v2;
+    }
+}
+
+void launch_head_reduce(const float4 *part, int units, int M, int32_t *argmax, float *margin,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, s, part, units, argmax, margin);
+}
+
+}  // namespace dbf

@@ -1,0 +1,82 @@
+// internal.hpp -- device helpers and launch declarations shared by the libdbf kernels.
+//
+// Activation "split" layout. Every projection in the block multiplies BF16 weights
+// by F32 activations. The kernels run these products on the gfx950 matrix cores
+// (v_mfma_f32_16x16x32_bf16) by splitting each F32 activation a into two BF16
+// terms, hi = rne(a) and lo = rne(a - hi), so that a = hi + lo + r with
+// |r| <= 2^-16 |a|; each BF16*BF16 product is exact in the F32 accumulator. This
+// is the multi-word BF16 splitting of Henry, Tang and Heinecke ("Leveraging the
+// bfloat16 artificial intelligence datatype for higher-precision computations",
+// ARITH 2019).
+//
+// A split buffer holds up to 16 activation rows ("one tile") of length K, padded
+// to a multiple of 32 columns, in the order the MFMA B operand is read: for k-step
+// s (columns 32s..32s+31), half h (0 = hi, 1 = lo) and lane l of a wavefront,
+// 8 consecutive BF16 at element offset ((s*2 + h)*64 + l)*8. Lane l carries
+// activation row (l % 16) and columns 32s + 8*(l/16) .. +7. A wave therefore reads
+// each half of a k-step as one contiguous, fully coalesced 1 KiB line.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// F32 -> BF16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// bytes of one split tile for K columns
+__host__ __device__ inline size_t split_tile_bytes(int K) {
+    return (size_t)((K + 31) / 32) * 2 * 64 * 8 * sizeof(uint16_t);
+}
+
+// element offset (in uint16 units) of activation (row r < 16, column k), half h
+__device__ __forceinline__ size_t split_index(int r, int k, int h) {
+    int s = k >> 5, g = (k & 31) >> 3, j = k & 7;
+    return ((size_t)(s * 2 + h) * 64 + (g * 16 + r)) * 8 + j;
+}
+
+__device__ __forceinline__ void split_store(uint16_t *tile, int r, int k, float a) {
+    uint16_t hi = f32_to_bf16(a);
+    float rem = a - bf16_to_f32(hi);
+    tile[split_index(r, k, 0)] = hi;
+    tile[split_index(r, k, 1)] = f32_to_bf16(rem);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+// Sum over a 256-thread block in a fixed order (wave sums, then waves 0..3).
+__device__ __forceinline__ float block_sum_256(float v, float *sh4) {
+    v = wave_sum(v);
+    int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh4[w] = v;
+    __syncthreads();
+    return (sh4[0] + sh4[1]) + (sh4[2] + sh4[3]);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+}  // namespace dbf

@@ -1,0 +1,251 @@
+"""ctypes binding of libdbf.so (include/dbf.h): argument marshalling only.
+
+Every step of the drafter block runs in the library's HIP kernels; this module
+only turns torch tensors (device memory) and the current HIP stream into the C
+structs and pointers the ABI takes. Importing it fails loudly when the built
+library is missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdbf.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "dbf.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libdbf.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+# torch first: its bundled HIP runtime has the same soname (libamdhip64.so.7) as the
+# one libdbf.so links against, so the loader then binds libdbf.so to torch's copy and
+# the process holds a single HIP runtime (two runtimes do not share devices/streams).
+import torch  # noqa: E402,F401
+
+_lib = C.CDLL(LIB_PATH)
+
+OK, EINVAL, ESHAPE, EDTYPE, ERANGE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16, I32 = 0, 1, 2
+KIND_DFLASH, KIND_MTP = 0, 1
+FFN_DENSE, FFN_MOE = 0, 1
+MAX_M = 16
+MAX_R = 16
+
+
+class DbfError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dbf error {code}: {msg}")
+        self.code = code
+
+
+class Tensor(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int32), ("ndim", C.c_int32),
+                ("shape", C.c_int64 * 4)]
+
+
+class Config(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("n_layers", C.c_int32), ("hidden", C.c_int32),
+                ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("rotary_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("n_target_hidden", C.c_int32), ("vocab", C.c_int32), ("ffn_kind", C.c_int32),
+                ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("expert_intermediate", C.c_int32), ("shared_intermediate", C.c_int32),
+                ("has_attn_gate", C.c_int32), ("rms_eps", C.c_double), ("rope_theta", C.c_double)]
+
+
+LAYER_FIELDS = ["in_norm", "post_norm", "wq", "wk", "wv", "attn_gate", "wo", "q_norm", "k_norm",
+                "ffn_gate", "ffn_up", "ffn_down", "router", "exp_gate", "exp_up", "exp_down",
+                "sh_gate", "sh_up", "sh_down", "sh_gate_inp"]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(f, Tensor) for f in LAYER_FIELDS]
+
+
+class Weights(C.Structure):
+    _fields_ = [("fc", Tensor), ("hidden_norm", Tensor), ("enorm", Tensor), ("hnorm", Tensor),
+                ("eh_embed", Tensor), ("eh_hidden", Tensor), ("layers", C.POINTER(LayerWeights)),
+                ("final_norm", Tensor), ("embed", Tensor)]
+
+
+class KVCache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("dtype", C.c_int32),
+                ("n_layers", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("capacity", C.c_int64), ("seq_len", C.c_int64)]
+
+
+class BlockIO(C.Structure):
+    _fields_ = [("tokens", C.c_void_p), ("x0", C.c_void_p), ("ctx", C.c_void_p),
+                ("M", C.c_int32), ("R", C.c_int32), ("hidden_out", C.c_void_p),
+                ("h_final", C.c_void_p), ("layer_hidden", C.c_void_p)]
+
+
+_lib.draft_block_forward.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(KVCache),
+                                     C.POINTER(BlockIO), C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.draft_block_forward.restype = C.c_int
+_lib.draft_block_workspace_bytes.argtypes = [C.POINTER(Config), C.c_int32, C.c_int32]
+_lib.draft_block_workspace_bytes.restype = C.c_size_t
+_lib.lm_head_argmax.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(Tensor), C.c_void_p,
+                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.lm_head_argmax.restype = C.c_int
+_lib.lm_head_argmax_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+_lib.lm_head_argmax_workspace_bytes.restype = C.c_size_t
+_lib.accept_prefix.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+                               C.c_void_p, C.c_void_p, C.c_void_p]
+_lib.accept_prefix.restype = C.c_int
+_lib.kv_rollback.argtypes = [C.POINTER(KVCache), C.c_int32]
+_lib.kv_rollback.restype = C.c_int
+_lib.dbf_last_error.restype = C.c_char_p
+_lib.dbf_abi_version.restype = C.c_int
+
+
+def lib():
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of every function include/dbf.h declares."""
+    with open(HEADER) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       txt, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "return")))
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DbfError(rc, _lib.dbf_last_error().decode())
+
+
+def last_error() -> str:
+    return _lib.dbf_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def tensor(t) -> Tensor:
+    """dbf_tensor view of a contiguous torch tensor (or an empty view for None)."""
+    out = Tensor()
+    if t is None:
+        return out
+    torch = _torch()
+    if not t.is_contiguous():
+        raise ValueError("dbf tensors must be contiguous")
+    dt = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}.get(t.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    out.data = t.data_ptr()
+    out.dtype = dt
+    out.ndim = t.dim()
+    for i, s in enumerate(t.shape):
+        out.shape[i] = s
+    return out
+
+
+def make_config(bc) -> Config:
+    """dbf_config from a configs.BlockConfig."""
+    return Config(kind=KIND_DFLASH if bc.kind == "dflash" else KIND_MTP, n_layers=bc.n_layers,
+                  hidden=bc.hidden, n_q_heads=bc.n_q_heads, n_kv_heads=bc.n_kv_heads,
+                  head_dim=bc.head_dim, rotary_dim=bc.rotary_dim, intermediate=bc.intermediate,
+                  n_target_hidden=bc.n_target_hidden, vocab=bc.vocab,
+                  ffn_kind=FFN_MOE if bc.ffn_kind == "moe" else FFN_DENSE,
+                  n_experts=bc.n_experts, top_k=bc.top_k,
+                  expert_intermediate=bc.expert_intermediate,
+                  shared_intermediate=bc.shared_intermediate,
+                  has_attn_gate=1 if bc.has_attn_gate else 0, rms_eps=bc.rms_eps,
+                  rope_theta=bc.rope_theta)
+
+
+class BlockWeights:
+    """dbf_weights over a dict of device tensors named as in synth.manifest()."""
+
+    def __init__(self, bc, t: dict):
+        self.t = t  # keep the tensors alive
+        L = bc.n_layers
+        self.layers = (LayerWeights * L)()
+        for i in range(L):
+            for f in LAYER_FIELDS:
+                setattr(self.layers[i], f, tensor(t.get(f"layers.{i}.{f}")))
+        self.w = Weights(fc=tensor(t.get("fc")), hidden_norm=tensor(t.get("hidden_norm")),
+                         enorm=tensor(t.get("enorm")), hnorm=tensor(t.get("hnorm")),
+                         eh_embed=tensor(t.get("eh_embed")), eh_hidden=tensor(t.get("eh_hidden")),
+                         layers=self.layers, final_norm=tensor(t.get("final_norm")),
+                         embed=tensor(t.get("embed")))
+
+
+def make_cache(k, v, seq_len: int) -> KVCache:
+    torch = _torch()
+    dt = BF16 if k.dtype == torch.bfloat16 else F32 if k.dtype == torch.float32 else -1
+    L, nkv, cap, hd = k.shape
+    return KVCache(k=k.data_ptr(), v=v.data_ptr(), dtype=dt, n_layers=L, n_kv_heads=nkv,
+                   head_dim=hd, capacity=cap, seq_len=seq_len)
+
+
+def make_io(M, R, h_final, tokens=None, x0=None, ctx=None, hidden_out=None,
+            layer_hidden=None) -> BlockIO:
+    return BlockIO(tokens=_ptr(tokens), x0=_ptr(x0), ctx=_ptr(ctx), M=M, R=R,
+                   hidden_out=_ptr(hidden_out), h_final=_ptr(h_final),
+                   layer_hidden=_ptr(layer_hidden))
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def draft_block_workspace_bytes(cfg: Config, M: int, R: int) -> int:
+    return int(_lib.draft_block_workspace_bytes(C.byref(cfg), M, R))
+
+
+def draft_block_forward(cfg: Config, w: BlockWeights, cache: KVCache, io: BlockIO, ws,
+                        stream=None) -> None:
+    _check(_lib.draft_block_forward(C.byref(cfg), C.byref(w.w), C.byref(cache), C.byref(io),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lm_head_argmax_workspace_bytes(M: int, H: int, V: int) -> int:
+    return int(_lib.lm_head_argmax_workspace_bytes(M, H, V))
+
+
+def lm_head_argmax(h, lm_head, argmax, logits=None, top2_margin=None, ws=None, stream=None) -> None:
+    M, H = h.shape
+    lt = tensor(lm_head)
+    _check(_lib.lm_head_argmax(_ptr(h), M, H, C.byref(lt), _ptr(argmax), _ptr(logits),
+                               _ptr(top2_margin), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream)))
+
+
+def accept_prefix(drafts, target, result, eos=None, committed=None, stream=None) -> None:
+    K = drafts.numel()
+    n_eos = 0 if eos is None else eos.numel()
+    _check(_lib.accept_prefix(_ptr(drafts), _ptr(target), K, _ptr(eos), n_eos, _ptr(result),
+                              _ptr(committed), _stream(stream)))
+
+
+def kv_rollback(cache: KVCache, n: int) -> None:
+    _check(_lib.kv_rollback(C.byref(cache), n))
+
+
+def abi_version() -> int:
+    return int(_lib.dbf_abi_version())
