@@ -63,6 +63,8 @@ struct Plan {
     int H, qt, kt, I, Kin, rd;
     GemmPlan in, q, k, v, g, o, gate, up, down;
     size_t xres, x1, xs_blk, xs_T, xs_hctx, xs_h, xs_o, xs_ff, qbuf, gbuf, attn;
+    size_t ssp_x, ssp_x1, ssp_ctx, ssp_e, ssp_h;
+    int ncb;
     size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_o, p_gate, p_up, p_down;
     size_t total;
 };
@@ -103,6 +105,12 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.xs_h = take(split_tile_bytes(p.H));
     p.xs_o = take(split_tile_bytes(p.qt));
     p.xs_ff = take(split_tile_bytes(p.I > 0 ? p.I : 32));
+    p.ncb = (p.H + 63) / 64;
+    p.ssp_x = take((size_t)16 * p.ncb * f);
+    p.ssp_x1 = take((size_t)16 * p.ncb * f);
+    p.ssp_ctx = take((size_t)16 * p.ncb * f);
+    p.ssp_e = take((size_t)16 * p.ncb * f);
+    p.ssp_h = take((size_t)16 * p.ncb * f);
     p.qbuf = take((size_t)DBF_MAX_M * p.qt * f);
     p.gbuf = take((size_t)DBF_MAX_M * p.qt * f);
     p.attn = take((size_t)64 * DBF_MAX_M * c.n_q_heads * (c.head_dim + 2) * f);
@@ -289,39 +297,92 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     float *attn_part = at<float>(ws, p.attn);
     const dbf_layer_weights *Ls = w->layers;
 
+    float *ssp_x = at<float>(ws, p.ssp_x), *ssp_x1 = at<float>(ws, p.ssp_x1);
+    float *ssp_ctx = at<float>(ws, p.ssp_ctx);
+    const int ncb = p.ncb;
+    auto col = [&]() {
+        ColArgs a{};
+        a.H = H;
+        a.ncb_in = ncb;
+        a.ncb_out = ncb;
+        return a;
+    };
+
     // ---- input projection
     if (c.kind == DBF_KIND_DFLASH) {
-        launch_input_dflash(io->tokens, io->x0, (const uint16_t *)w->embed.data, c.vocab, M, H,
-                            (const float *)Ls[0].in_norm.data, eps, xres, xs_blk, st);
+        // x = embed[tokens] (or x0); split(x (.) in_norm_0) for the first layer
+        ColArgs a = col();
+        a.M = M;
+        a.tokens = io->tokens;
+        a.embed = (const uint16_t *)w->embed.data;
+        a.V = c.vocab;
+        a.base = io->x0;
+        a.ldb = H;
+        a.out = xres;
+        a.w = (const float *)Ls[0].in_norm.data;
+        a.xs = xs_blk;
+        a.ssp_out = ssp_x;
+        launch_colsum(a, st);
         if (R > 0) {
-            launch_split_rows(io->ctx, R, p.Kin, p.Kin, xs_T, st);
+            // h_ctx = RMSNorm(T fc^T, hidden_norm): split T, project, split(proj (.) hidden_norm)
+            ColArgs t = col();
+            t.M = R;
+            t.H = p.Kin;
+            t.base = io->ctx;
+            t.ldb = p.Kin;
+            t.xs = xs_T;
+            launch_colsum(t, st);
             SegList sl;
             sl.add((const uint16_t *)w->fc.data, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
             sl.launch(st);
-            launch_hctx(at<float>(ws, p.p_in0), p.in.ksplit, R, H, (const float *)w->hidden_norm.data,
-                        eps, xs_hctx, st);
+            ColArgs h = col();
+            h.M = R;
+            h.p0 = at<float>(ws, p.p_in0);
+            h.ks0 = p.in.ksplit;
+            h.rows0 = 16;
+            h.w = (const float *)w->hidden_norm.data;
+            h.xs = xs_hctx;
+            h.ssp_out = ssp_ctx;
+            launch_colsum(h, st);
         }
     } else {
-        launch_mtp_input(io->x0, io->ctx, M, H, (const float *)w->enorm.data,
-                         (const float *)w->hnorm.data, xs_blk, xs_h, st);
+        // x = RMSNorm(e, enorm) eh_embed^T + RMSNorm(h, hnorm) eh_hidden^T (eps 1e-6)
+        float *ssp_e = at<float>(ws, p.ssp_e), *ssp_h = at<float>(ws, p.ssp_h);
+        ColArgs e = col();
+        e.M = M;
+        e.base = io->x0;
+        e.ldb = H;
+        e.w = (const float *)w->enorm.data;
+        e.xs = xs_blk;
+        e.ssp_out = ssp_e;
+        launch_colsum(e, st);
+        ColArgs h = e;
+        h.base = io->ctx;
+        h.w = (const float *)w->hnorm.data;
+        h.xs = xs_h;
+        h.ssp_out = ssp_h;
+        launch_colsum(h, st);
         SegList sl;
         sl.add((const uint16_t *)w->eh_embed.data, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
         sl.add((const uint16_t *)w->eh_hidden.data, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
         sl.launch(st);
-        SumNormArgs sn{};
-        sn.p0 = at<float>(ws, p.p_in0);
-        sn.ks0 = p.in.ksplit;
-        sn.rows0 = 16;
-        sn.p1 = at<float>(ws, p.p_in1);
-        sn.ks1 = p.in.ksplit;
-        sn.rows1 = 16;
-        sn.out = xres;
-        sn.w = (const float *)Ls[0].in_norm.data;
-        sn.eps = eps;
-        sn.xs = xs_blk;
-        sn.M = M;
-        sn.H = H;
-        launch_sum_norm_split(sn, st);
+        ColArgs x = col();
+        x.M = M;
+        x.p0 = at<float>(ws, p.p_in0);
+        x.ks0 = p.in.ksplit;
+        x.rows0 = 16;
+        x.ssp0 = ssp_e;
+        x.eps0 = 1e-6f;
+        x.p1 = at<float>(ws, p.p_in1);
+        x.ks1 = p.in.ksplit;
+        x.rows1 = 16;
+        x.ssp1 = ssp_h;
+        x.eps1 = 1e-6f;
+        x.out = xres;
+        x.w = (const float *)Ls[0].in_norm.data;
+        x.xs = xs_blk;
+        x.ssp_out = ssp_x;
+        launch_colsum(x, st);
     }
 
     int chunk = 0, n_chunks = 0;
@@ -331,6 +392,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
 
     for (int l = 0; l < c.n_layers; l++) {
         const dbf_layer_weights &L = Ls[l];
+        const bool last = l == c.n_layers - 1;
         float *pq = at<float>(ws, p.p_q), *pk = at<float>(ws, p.p_k), *pv = at<float>(ws, p.p_v);
         float *pg = at<float>(ws, p.p_g);
         {
@@ -360,6 +422,10 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             qa.ksg = p.g.ksplit;
             qa.rows_kv = R > 0 ? 32 : 16;
             qa.kv_block_row0 = R > 0 ? 16 : 0;
+            qa.ssp_x = ssp_x;
+            qa.ssp_ctx = ssp_ctx;
+            qa.ncb = ncb;
+            qa.H = H;
             qa.q_norm = (const float *)L.q_norm.data;
             qa.k_norm = (const float *)L.k_norm.data;
             qa.eps = eps;
@@ -409,47 +475,61 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             SegList sl;
             sl.add((const uint16_t *)L.wo.data, H, qt, p.o, at<float>(ws, p.p_o), xs_o);
             sl.launch(st);
-            SumNormArgs sn{};
-            sn.base = xres;
-            sn.p0 = at<float>(ws, p.p_o);
-            sn.ks0 = p.o.ksplit;
-            sn.rows0 = 16;
-            sn.out = x1;
-            sn.w = (const float *)L.post_norm.data;
-            sn.eps = eps;
-            sn.xs = xs_blk;
-            sn.M = M;
-            sn.H = H;
-            launch_sum_norm_split(sn, st);
+            // x1 = x + o Wo^T; split(x1 (.) post_norm) for the FFN
+            ColArgs a = col();
+            a.M = M;
+            a.base = xres;
+            a.ldb = H;
+            a.p0 = at<float>(ws, p.p_o);
+            a.ks0 = p.o.ksplit;
+            a.rows0 = 16;
+            a.out = x1;
+            a.w = (const float *)L.post_norm.data;
+            a.xs = xs_blk;
+            a.ssp_out = ssp_x1;
+            launch_colsum(a, st);
         }
         {
             SegList sl;
             sl.add((const uint16_t *)L.ffn_gate.data, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
             sl.add((const uint16_t *)L.ffn_up.data, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
             sl.launch(st);
-            launch_swiglu_split(at<float>(ws, p.p_gate), p.gate.ksplit, at<float>(ws, p.p_up),
-                                p.up.ksplit, M, p.I, xs_ff, st);
+            SwigluArgs sa{};
+            sa.pg = at<float>(ws, p.p_gate);
+            sa.pu = at<float>(ws, p.p_up);
+            sa.ksg = p.gate.ksplit;
+            sa.ksu = p.up.ksplit;
+            sa.ssp = ssp_x1;
+            sa.ncb = ncb;
+            sa.H = H;
+            sa.eps = eps;
+            sa.M = M;
+            sa.I = p.I;
+            sa.xs = xs_ff;
+            launch_swiglu(sa, st);
             SegList sd;
             sd.add((const uint16_t *)L.ffn_down.data, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
             sd.launch(st);
         }
         {
-            const bool last = l == c.n_layers - 1;
-            SumNormArgs sn{};
-            sn.base = x1;
-            sn.p0 = at<float>(ws, p.p_down);
-            sn.ks0 = p.down.ksplit;
-            sn.rows0 = 16;
-            sn.out = xres;
-            sn.copy0 = io->layer_hidden ? io->layer_hidden + (size_t)l * M * H : nullptr;
-            sn.copy1 = last ? io->hidden_out : nullptr;
-            sn.w = last ? (const float *)w->final_norm.data : (const float *)Ls[l + 1].in_norm.data;
-            sn.eps = eps;
-            sn.normed = last ? io->h_final : nullptr;
-            sn.xs = xs_blk;
-            sn.M = M;
-            sn.H = H;
-            launch_sum_norm_split(sn, st);
+            // x = x1 + FFN; split(x (.) next in_norm), or the final norm after the last layer
+            ColArgs a = col();
+            a.M = M;
+            a.base = x1;
+            a.ldb = H;
+            a.p0 = at<float>(ws, p.p_down);
+            a.ks0 = p.down.ksplit;
+            a.rows0 = 16;
+            a.out = xres;
+            a.copy0 = io->layer_hidden ? io->layer_hidden + (size_t)l * M * H : nullptr;
+            a.copy1 = last ? io->hidden_out : nullptr;
+            a.w = last ? nullptr : (const float *)Ls[l + 1].in_norm.data;
+            a.xs = last ? nullptr : xs_blk;
+            a.ssp_out = ssp_x;
+            launch_colsum(a, st);
+            if (last)
+                launch_final_norm(xres, ssp_x, M, H, (const float *)w->final_norm.data, eps,
+                                  io->h_final, st);
         }
     }
     CHECK(hip_check("draft_block_forward launch"));
@@ -482,7 +562,13 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
     (void)hipGetLastError();
     uint16_t *xs = (uint16_t *)ws;
     float4 *part = at<float4>(ws, align256(split_tile_bytes(H)));
-    launch_split_rows(h, M, H, H, xs, st);
+    ColArgs a{};
+    a.M = M;
+    a.H = H;
+    a.base = h;
+    a.ldb = H;
+    a.xs = xs;
+    launch_colsum(a, st);
     launch_head((const uint16_t *)lm_head->data, xs, V, H, M, logits, part, st);
     launch_head_reduce(part, head_units(V), M, argmax, top2_margin, st);
     return hip_check("lm_head_argmax launch");

@@ -49,37 +49,33 @@ void launch_head_reduce(const float4 *part, int units, int M, int32_t *argmax, f
                         hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// row kernels (elementwise / norms / splits)
+// row kernels (column-parallel; see rows.hip for the split-RMSNorm convention)
 // ---------------------------------------------------------------------------
-void launch_split_rows(const float *X, int rows, int K, int ldx, uint16_t *tile, hipStream_t s);
-
-void launch_input_dflash(const int32_t *tokens, const float *x0, const uint16_t *embed, int V,
-                         int M, int H, const float *norm_w, float eps, float *xres,
-                         uint16_t *xs, hipStream_t s);
-
-void launch_mtp_input(const float *e, const float *hp, int M, int H, const float *enorm,
-                      const float *hnorm, uint16_t *xs_e, uint16_t *xs_h, hipStream_t s);
-
-// out = base + sum_{set} sum_{ks} P_set[ks][prow0_set + m][:]; optional copies;
-// norm_out = RMSNorm(out, w); split into xs (tile rows 0..15, zero for m >= M).
-struct SumNormArgs {
-    const float *base;     // [M][H] or null
-    const float *p0;       // partial set 0: [ks0][rows0][H]
+struct ColArgs {
+    int M, H;                 // valid rows, columns
+    const int32_t *tokens;    // gather embed[tokens[m]] (BF16) as the base, or null
+    const uint16_t *embed;
+    int V;
+    const float *base;        // [M][ldb] base rows, or null
+    int ldb;
+    const float *p0;          // split-K partials [ks0][rows0][H], or null
     int ks0, rows0;
-    const float *p1;       // partial set 1 or null
+    const float *ssp0;        // row-scale source for set 0 ([16][ncb_in]) or null (scale 1)
+    float eps0;
+    const float *p1;
     int ks1, rows1;
-    float *out;            // [M][H] (may alias base)
-    float *copy0, *copy1;  // optional extra copies of out
-    const float *w;        // norm weight [H]
-    float eps;
-    float *normed;         // optional f32 normed rows [M][H]
-    uint16_t *xs;          // split tile (K = H), required
-    int M, H;
+    const float *ssp1;
+    float eps1;
+    int ncb_in;
+    float *out, *copy0, *copy1;  // [M][H] copies of the summed rows, each optional
+    const float *w;           // multiply before the split (norm weight) or null
+    uint16_t *xs;             // split tile (K = H) or null
+    float *ssp_out;           // [16][ncb_out] partial sums of squares, or null
+    int ncb_out;
 };
-void launch_sum_norm_split(const SumNormArgs &a, hipStream_t s);
-
-void launch_hctx(const float *p, int ks, int R, int H, const float *w, float eps, uint16_t *xs,
-                 hipStream_t s);
+void launch_colsum(const ColArgs &a, hipStream_t s);
+void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
+                       float *out, hipStream_t s);
 
 struct QkvPostArgs {
     const float *pq;   // [ksq][16][qt]
@@ -87,6 +83,9 @@ struct QkvPostArgs {
     const float *pv;   // [ksv][rows_kv][kt]
     const float *pg;   // [ksg][16][qt] or null
     int ksq, ksk, ksv, ksg, rows_kv, kv_block_row0;
+    const float *ssp_x;    // block rows' norm partials [16][ncb]
+    const float *ssp_ctx;  // context rows' norm partials [16][ncb]
+    int ncb, H;
     const float *q_norm, *k_norm;
     float eps;
     double theta;
@@ -100,6 +99,17 @@ struct QkvPostArgs {
     long long capacity;
 };
 void launch_qkv_post(const QkvPostArgs &a, hipStream_t s);
+
+struct SwigluArgs {
+    const float *pg, *pu;
+    int ksg, ksu;
+    const float *ssp;  // FFN input rows' norm partials [16][ncb]
+    int ncb, H;
+    float eps;
+    int M, I;
+    uint16_t *xs;
+};
+void launch_swiglu(const SwigluArgs &a, hipStream_t s);
 
 struct AttnArgs {
     const float *q;        // [M][nq*hd], normed + rotated
@@ -122,9 +132,6 @@ struct CombineArgs {
     uint16_t *xs;          // split tile (K = nq*hd)
 };
 void launch_attn_combine(const CombineArgs &a, hipStream_t s);
-
-void launch_swiglu_split(const float *pg, int ksg, const float *pu, int ksu, int M, int I,
-                         uint16_t *xs, hipStream_t s);
 
 void launch_accept(const int32_t *drafts, const int32_t *target, int K, const int32_t *eos,
                    int n_eos, int32_t *result, int32_t *committed, hipStream_t s);

@@ -1,296 +1,243 @@
-// rows.hip -- per-row kernels of the drafter block: input gathers, the fused
-// "sum split-K partials + residual + RMSNorm + activation split" epilogues, the
-// Q/K/V post-processing (per-head RMSNorm, RoPE, KV store) and SwiGLU.
+// rows.hip -- the column-parallel row kernels of the drafter block.
 //
-// One 256-thread block per activation row; every reduction runs in a fixed order
-// (thread-strided partial sums, then a fixed wave/block tree), so results are
-// bit-reproducible run to run.
+// RMSNorm (hf2q qwen35/mtp.rs `rms_norm_with_weight`: y = x / sqrt(mean(x^2)+eps) * w)
+// is applied in two halves. Its row scale s_m = 1/sqrt(mean_k x_mk^2 + eps) is a
+// per-row scalar, and a projection is linear, so
+//     Linear(x_m * s_m (.) w, W) = s_m * Linear(x_m (.) w, W).
+// The producer of a normalized input therefore only writes x (.) w (split for the
+// matrix cores) plus per-64-column partial sums of x^2 ("ssp", [16][ncb]); the
+// consumer of the projection's output applies s_m. No kernel needs a whole row,
+// so every row kernel runs one wavefront per (row, 64 columns): many blocks, no
+// serial row loop. All sums run in a fixed order.
 #include "internal.hpp"
 #include "kernels.hpp"
 
 namespace dbf {
 
-// RMSNorm scale of a row held in `v` (n elements, strided over the block):
-// 1 / sqrt(mean(v^2) + eps), hf2q qwen35/mtp.rs `rms_norm_with_weight`.
-__device__ __forceinline__ float rms_scale(float ss, int n, float eps, float *sh4) {
-    float tot = block_sum_256(ss, sh4);
-    return 1.0f / sqrtf(tot / (float)n + eps);
+// Row scale from the per-column-block partial sums of squares; called by a whole
+// wavefront (lane-strided sum, then a fixed xor tree).
+__device__ __forceinline__ float row_scale(const float *ssp_row, int ncb, int H, float eps) {
+    const int lane = threadIdx.x & 63;
+    float s = 0.f;
+    for (int i = lane; i < ncb; i += 64) s += ssp_row[i];
+    s = wave_sum(s);
+    return 1.0f / sqrtf(s / (float)H + eps);
 }
 
-// Write row r of a split tile from a shared/global row buffer (zeros when !valid).
-__device__ __forceinline__ void split_row(uint16_t *tile, int r, const float *row, int K,
-                                          bool valid, float scale, const float *w) {
-    const int Kp = (K + 31) & ~31;
-    for (int k = threadIdx.x; k < Kp; k += blockDim.x) {
-        float a = 0.f;
-        if (valid && k < K) a = row[k] * scale * (w ? w[k] : 1.0f);
-        split_store(tile, r, k, a);
+// sum over ks split-K partials of element (row, col) in a [ks][rows][N] buffer
+__device__ __forceinline__ float sum_partials(const float *p, int ks, int rows, int N, int row,
+                                              int col) {
+    const size_t stride = (size_t)rows * N;
+    const float *q = p + (size_t)row * N + col;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int t = 0;
+    for (; t + 3 < ks; t += 4) {
+        a0 += q[(t + 0) * stride];
+        a1 += q[(t + 1) * stride];
+        a2 += q[(t + 2) * stride];
+        a3 += q[(t + 3) * stride];
     }
+    for (; t < ks; t++) a0 += q[t * stride];
+    return (a0 + a1) + (a2 + a3);
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_split_rows(const float *X, int rows, int K, int ldx,
-                                                    uint16_t *tile) {
-    const int r = blockIdx.x;
-    split_row(tile, r, X + (size_t)r * ldx, K, r < rows, 1.0f, nullptr);
-}
-
-void launch_split_rows(const float *X, int rows, int K, int ldx, uint16_t *tile, hipStream_t s) {
-    hipLaunchKernelGGL(k_split_rows, dim3(16), dim3(256), 0, s, X, rows, K, ldx, tile);
-}
-
-// ---------------------------------------------------------------------------
-// DFlash block input: x = embed[token] (BF16 -> F32 exact) or x0; xres = x;
-// split(RMSNorm(x, in_norm of layer 0)).
-__global__ __launch_bounds__(256) void k_input_dflash(const int32_t *tokens, const float *x0,
-                                                      const uint16_t *embed, int V, int M, int H,
-                                                      const float *w, float eps, float *xres,
-                                                      uint16_t *xs) {
-    __shared__ float sh4[4];
-    extern __shared__ float row[];
-    const int m = blockIdx.x;
-    const bool valid = m < M;
-    float ss = 0.f;
-    if (valid) {
-        if (tokens) {
-            int t = tokens[m];
-            t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-            const uint16_t *e = embed + (size_t)t * H;
-            for (int k = threadIdx.x; k < H; k += 256) row[k] = bf16_to_f32(e[k]);
-        } else {
-            for (int k = threadIdx.x; k < H; k += 256) row[k] = x0[(size_t)m * H + k];
-        }
-        for (int k = threadIdx.x; k < H; k += 256) {
-            xres[(size_t)m * H + k] = row[k];
-            ss += row[k] * row[k];
-        }
-    }
-    float sc = rms_scale(ss, H, eps, sh4);
-    split_row(xs, m, row, H, valid, sc, w);
-}
-
-void launch_input_dflash(const int32_t *tokens, const float *x0, const uint16_t *embed, int V,
-                         int M, int H, const float *norm_w, float eps, float *xres, uint16_t *xs,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(k_input_dflash, dim3(16), dim3(256), H * sizeof(float), s, tokens, x0,
-                       embed, V, M, H, norm_w, eps, xres, xs);
-}
-
-// ---------------------------------------------------------------------------
-// MTP input halves: split(RMSNorm(e, enorm, 1e-6)) and split(RMSNorm(h, hnorm, 1e-6))
-// (qwen35/mtp.rs `project_embedding_and_hidden`, eps fixed at 1e-6 there).
-__global__ __launch_bounds__(256) void k_mtp_input(const float *e, const float *hp, int M, int H,
-                                                   const float *enorm, const float *hnorm,
-                                                   uint16_t *xs_e, uint16_t *xs_h) {
-    __shared__ float sh4[4];
-    const int m = blockIdx.x % 16;
-    const bool second = blockIdx.x >= 16;
-    const float *src = second ? hp : e;
-    const float *w = second ? hnorm : enorm;
-    uint16_t *xs = second ? xs_h : xs_e;
-    const bool valid = m < M;
-    const float *row = src + (size_t)(valid ? m : 0) * H;
-    float ss = 0.f;
-    if (valid)
-        for (int k = threadIdx.x; k < H; k += 256) ss += row[k] * row[k];
-    float sc = rms_scale(ss, H, 1e-6f, sh4);
-    split_row(xs, m, row, H, valid, sc, w);
-}
-
-void launch_mtp_input(const float *e, const float *hp, int M, int H, const float *enorm,
-                      const float *hnorm, uint16_t *xs_e, uint16_t *xs_h, hipStream_t s) {
-    hipLaunchKernelGGL(k_mtp_input, dim3(32), dim3(256), 0, s, e, hp, M, H, enorm, hnorm, xs_e,
-                       xs_h);
-}
-
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_sum_norm_split(SumNormArgs a) {
-    __shared__ float sh4[4];
-    extern __shared__ float row[];
-    const int m = blockIdx.x;
-    const int H = a.H;
-    const bool valid = m < a.M;
-    float ss = 0.f;
-    if (valid) {
-        for (int k = threadIdx.x; k < H; k += 256) {
-            float v = a.base ? a.base[(size_t)m * H + k] : 0.f;
-            float p = 0.f;
-            for (int t = 0; t < a.ks0; t++) p += a.p0[((size_t)t * a.rows0 + m) * H + k];
-            if (a.p1) {
-                float p1 = 0.f;
-                for (int t = 0; t < a.ks1; t++) p1 += a.p1[((size_t)t * a.rows1 + m) * H + k];
-                p += p1;
+// Generic column kernel. Grid (ncb = ceil(H/64), 4), 256 threads: wave w handles
+// row m = 4*blockIdx.y + w, lane the column blockIdx.x*64 + lane.
+//   v = [gather embed row | base] + scale0 * sum P0 + scale1 * sum P1
+//   out/copies <- v;  xs <- split(v (.) w);  ssp_out[m][cb] <- sum over the 64 columns of v^2
+// Rows m >= M and padding columns write zeros into the split tile.
+__global__ __launch_bounds__(256) void k_colsum(ColArgs a) {
+    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int k = blockIdx.x * 64 + lane;
+    const bool row_ok = m < a.M;
+    const bool ok = row_ok && k < a.H;
+    float v = 0.f;
+    if (row_ok) {
+        float sc0 = 1.f, sc1 = 1.f;
+        if (a.p0 && a.ssp0) sc0 = row_scale(a.ssp0 + (size_t)m * a.ncb_in, a.ncb_in, a.H, a.eps0);
+        if (a.p1 && a.ssp1) sc1 = row_scale(a.ssp1 + (size_t)m * a.ncb_in, a.ncb_in, a.H, a.eps1);
+        if (ok) {
+            if (a.tokens) {
+                int t = a.tokens[m];
+                t = t < 0 ? 0 : (t >= a.V ? a.V - 1 : t);
+                v = bf16_to_f32(a.embed[(size_t)t * a.H + k]);
+            } else if (a.base) {
+                v = a.base[(size_t)m * a.ldb + k];
             }
-            v += p;
-            row[k] = v;
-            ss += v * v;
+            if (a.p0) v += sc0 * sum_partials(a.p0, a.ks0, a.rows0, a.H, m, k);
+            if (a.p1) v += sc1 * sum_partials(a.p1, a.ks1, a.rows1, a.H, m, k);
+            if (a.out) a.out[(size_t)m * a.H + k] = v;
+            if (a.copy0) a.copy0[(size_t)m * a.H + k] = v;
+            if (a.copy1) a.copy1[(size_t)m * a.H + k] = v;
         }
-        for (int k = threadIdx.x; k < H; k += 256) {
-            float v = row[k];
-            a.out[(size_t)m * H + k] = v;
-            if (a.copy0) a.copy0[(size_t)m * H + k] = v;
-            if (a.copy1) a.copy1[(size_t)m * H + k] = v;
+        if (a.ssp_out) {
+            float ss = wave_sum(v * v);
+            if (lane == 0) a.ssp_out[(size_t)m * a.ncb_out + blockIdx.x] = ss;
         }
     }
-    float sc = rms_scale(ss, H, a.eps, sh4);
-    if (valid && a.normed)
-        for (int k = threadIdx.x; k < H; k += 256) a.normed[(size_t)m * H + k] = row[k] * sc * a.w[k];
-    split_row(a.xs, m, row, H, valid, sc, a.w);
+    if (a.xs && k < ((a.H + 31) & ~31)) split_store(a.xs, m, k, ok ? v * (a.w ? a.w[k] : 1.f) : 0.f);
 }
 
-void launch_sum_norm_split(const SumNormArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_sum_norm_split, dim3(16), dim3(256), a.H * sizeof(float), s, a);
-}
-
-// ---------------------------------------------------------------------------
-// DFlash context rows: h_ctx = RMSNorm(sum_ks P_fc, hidden_norm), split once and
-// reused as the K/V input of every layer.
-__global__ __launch_bounds__(256) void k_hctx(const float *p, int ks, int R, int H, const float *w,
-                                              float eps, uint16_t *xs) {
-    __shared__ float sh4[4];
-    extern __shared__ float row[];
-    const int r = blockIdx.x;
-    const bool valid = r < R;
-    float ss = 0.f;
-    if (valid)
-        for (int k = threadIdx.x; k < H; k += 256) {
-            float v = 0.f;
-            for (int t = 0; t < ks; t++) v += p[((size_t)t * 16 + r) * H + k];
-            row[k] = v;
-            ss += v * v;
-        }
-    float sc = rms_scale(ss, H, eps, sh4);
-    split_row(xs, r, row, H, valid, sc, w);
-}
-
-void launch_hctx(const float *p, int ks, int R, int H, const float *w, float eps, uint16_t *xs,
-                 hipStream_t s) {
-    hipLaunchKernelGGL(k_hctx, dim3(16), dim3(256), H * sizeof(float), s, p, ks, R, H, w, eps, xs);
+void launch_colsum(const ColArgs &a, hipStream_t s) {
+    const int ncb = (a.H + 63) / 64;
+    const int rg = a.xs ? 4 : (a.M + 3) / 4;  // split tiles need all 16 rows written
+    hipLaunchKernelGGL(k_colsum, dim3(ncb, rg), dim3(256), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
-// Q/K/V post-processing for one row (block row or DFlash context row):
-// sum partials; per-head RMSNorm of q (q_norm) and k (k_norm); rotate-half RoPE on
-// the first rotary_dim lanes of every head with angle pos * theta^(-2j/rotary_dim)
-// formed in F64 (at 32k positions an F32 product errs by ~1e-3 rad); store q (block
-// rows), the raw gate, and k/v into the cache row `pos` (F32, or BF16 with RNE).
-// (qwen35/mtp.rs `forward_full_attention`: q/k per-head norms, IMROPE with four
-// equal text positions = RoPE, SDPA-with-KV-cache append.)
-__global__ __launch_bounds__(256) void k_qkv_post(QkvPostArgs a) {
-    extern __shared__ float smem[];
+// Final norm: h_final = x * s_m (.) w.
+__global__ __launch_bounds__(256) void k_final_norm(const float *x, const float *ssp, int ncb, int M,
+                                                    int H, const float *w, float eps, float *out) {
+    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int k = blockIdx.x * 64 + (threadIdx.x & 63);
+    if (m >= M) return;
+    const float s = row_scale(ssp + (size_t)m * ncb, ncb, H, eps);
+    if (k < H) out[(size_t)m * H + k] = x[(size_t)m * H + k] * s * w[k];
+}
+
+void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
+                       float *out, hipStream_t s) {
+    const int ncb = (H + 63) / 64;
+    hipLaunchKernelGGL(k_final_norm, dim3(ncb, (M + 3) / 4), dim3(256), 0, s, x, ssp, ncb, M, H, w,
+                       eps, out);
+}
+
+// ---------------------------------------------------------------------------
+// Q/K/V post-processing, one wavefront per head vector (qwen35/mtp.rs
+// `forward_full_attention`): sum split-K partials and apply the row's RMSNorm
+// scale; per-head RMSNorm (q_norm / k_norm); rotate-half RoPE over the first
+// rotary_dim lanes with angle pos * theta^(-2j/rotary_dim) formed in F64 (an F32
+// product is off by ~1e-3 rad at 32k positions); store q (block rows) and the raw
+// gate, or the key and value rows of the cache (F32, or BF16 with RNE).
+// Blocks [0, M*nq) are q heads of block rows; then (R+M)*nkv k/v heads, context
+// rows first. DFlash context rows sit at positions P0+r, block rows at P0+R+m.
+__global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
+    __shared__ float vec[256];
+    const int lane = threadIdx.x;
     const int hd = a.hd, qt = a.nq * hd, kt = a.nkv * hd;
-    const bool is_ctx = (int)blockIdx.x < a.R;
-    const int m = is_ctx ? (int)blockIdx.x : (int)blockIdx.x - a.R;  // row in its group
-    const long long pos = is_ctx ? a.P0 + m : a.P0 + a.R + m;
-    const int kvrow = is_ctx ? m : a.kv_block_row0 + m;
-    float *qs = smem;                 // [qt] (block rows only)
-    float *ksb = smem + qt;           // [kt]
-    float *vs = ksb + kt;             // [kt]
-    float *hscale = vs + kt;          // [nq + nkv]
-    const int nscale = a.nq + a.nkv;
-    double *angle_base = (double *)(hscale + nscale + ((qt + 2 * kt + nscale) & 1));  // [rotary_dim/2]
-
-    const int half = a.rotary_dim / 2;
-    for (int j = threadIdx.x; j < half; j += 256)
-        angle_base[j] = pow(a.theta, -2.0 * (double)j / (double)a.rotary_dim);
-
-    // 1. sums of split-K partials
-    for (int i = threadIdx.x; i < kt; i += 256) {
-        float k = 0.f, v = 0.f;
-        for (int t = 0; t < a.ksk; t++) k += a.pk[((size_t)t * a.rows_kv + kvrow) * kt + i];
-        for (int t = 0; t < a.ksv; t++) v += a.pv[((size_t)t * a.rows_kv + kvrow) * kt + i];
-        ksb[i] = k;
-        vs[i] = v;
+    const int b = blockIdx.x;
+    const bool isq = b < a.M * a.nq;
+    int row, head;         // row within its group (block rows or all kv rows), head index
+    long long pos;
+    float s;               // RMSNorm scale of the source row
+    const float *src, *wn; // partial buffer, head-norm weight
+    int ks, prow, N;
+    if (isq) {
+        row = b / a.nq;
+        head = b % a.nq;
+        pos = a.P0 + a.R + row;
+        s = row_scale(a.ssp_x + (size_t)row * a.ncb, a.ncb, a.H, a.eps);
+        src = a.pq;
+        ks = a.ksq;
+        prow = row;
+        N = qt;
+        wn = a.q_norm;
+    } else {
+        const int idx = b - a.M * a.nq;
+        row = idx / a.nkv;  // 0..R+M-1, context rows first
+        head = idx % a.nkv;
+        const bool ctx = row < a.R;
+        const int m = ctx ? row : row - a.R;
+        pos = ctx ? a.P0 + row : a.P0 + a.R + m;
+        s = ctx ? row_scale(a.ssp_ctx + (size_t)m * a.ncb, a.ncb, a.H, a.eps)
+                : row_scale(a.ssp_x + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
+        src = a.pk;
+        ks = a.ksk;
+        prow = ctx ? m : a.kv_block_row0 + m;
+        N = kt;
+        wn = a.k_norm;
     }
-    if (!is_ctx) {
-        for (int i = threadIdx.x; i < qt; i += 256) {
-            float q = 0.f;
-            for (int t = 0; t < a.ksq; t++) q += a.pq[((size_t)t * 16 + m) * qt + i];
-            qs[i] = q;
-            if (a.pg) {
-                float g = 0.f;
-                for (int t = 0; t < a.ksg; t++) g += a.pg[((size_t)t * 16 + m) * qt + i];
-                a.g_out[(size_t)m * qt + i] = g;
-            }
+    const int rows = isq ? 16 : a.rows_kv;
+    float raw[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int d = lane + 64 * i;
+        raw[i] = 0.f;
+        if (d < hd) {
+            raw[i] = s * sum_partials(src, ks, rows, N, prow, head * hd + d);
+            ss += raw[i] * raw[i];
         }
     }
-    __syncthreads();
-    // 2. per-head mean squares: wave w takes heads w, w+4, ...
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nh_q = is_ctx ? 0 : a.nq;
-    for (int h = wv; h < nh_q + a.nkv; h += 4) {
-        const float *src = h < nh_q ? qs + h * hd : ksb + (h - nh_q) * hd;
-        float ss = 0.f;
-        for (int d = lane; d < hd; d += 64) ss += src[d] * src[d];
-        ss = wave_sum(ss);
-        if (lane == 0) hscale[h] = 1.0f / sqrtf(ss / (float)hd + a.eps);
+    const float hs = 1.0f / sqrtf(wave_sum(ss) / (float)hd + a.eps);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int d = lane + 64 * i;
+        if (d < hd) vec[d] = raw[i] * hs * wn[d];
     }
     __syncthreads();
-    // 3. normalize, rotate, store
-    const int nel = (nh_q + a.nkv) * hd;
-    for (int i = threadIdx.x; i < nel; i += 256) {
-        const int h = i / hd, d = i - h * hd;
-        const bool isq = h < nh_q;
-        const float *src = isq ? qs + h * hd : ksb + (h - nh_q) * hd;
-        const float *w = isq ? a.q_norm : a.k_norm;
-        const float sc = hscale[h];
-        float val = src[d] * sc * w[d];
+    const int half = a.rotary_dim / 2;
+    const size_t cache_off = ((size_t)head * a.capacity + pos) * hd;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int d = lane + 64 * i;
+        if (d >= hd) continue;
+        float val = vec[d];
         if (d < 2 * half) {
             const int j = d < half ? d : d - half;
-            const int pd = d < half ? d + half : d - half;
-            const float pv = src[pd] * sc * w[pd];
-            double ang = (double)pos * angle_base[j];
+            const float pv = vec[d < half ? d + half : d - half];
+            const double ang = (double)pos * pow(a.theta, -2.0 * (double)j / (double)a.rotary_dim);
             double sn, cs;
             sincos(ang, &sn, &cs);
-            const float c = (float)cs, s = (float)sn;
-            val = d < half ? val * c - pv * s : pv * s + val * c;
+            const float c = (float)cs, sv = (float)sn;
+            val = d < half ? val * c - pv * sv : pv * sv + val * c;
         }
         if (isq) {
-            a.q_out[(size_t)m * qt + h * hd + d] = val;
+            a.q_out[(size_t)row * qt + head * hd + d] = val;
         } else {
-            const int kh = h - nh_q;
-            const size_t off = ((size_t)kh * a.capacity + pos) * hd + d;
-            if (a.kv_bf16) ((uint16_t *)a.cache_k)[off] = f32_to_bf16(val);
-            else ((float *)a.cache_k)[off] = val;
+            if (a.kv_bf16) ((uint16_t *)a.cache_k)[cache_off + d] = f32_to_bf16(val);
+            else ((float *)a.cache_k)[cache_off + d] = val;
         }
     }
-    for (int i = threadIdx.x; i < kt; i += 256) {
-        const int kh = i / hd, d = i - kh * hd;
-        const size_t off = ((size_t)kh * a.capacity + pos) * hd + d;
-        if (a.kv_bf16) ((uint16_t *)a.cache_v)[off] = f32_to_bf16(vs[i]);
-        else ((float *)a.cache_v)[off] = vs[i];
+    // the gate (q blocks) and the value row (k blocks): same source row, no head norm
+    if (isq && a.pg) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int d = lane + 64 * i;
+            if (d < hd)
+                a.g_out[(size_t)row * qt + head * hd + d] =
+                    s * sum_partials(a.pg, a.ksg, 16, qt, row, head * hd + d);
+        }
+    }
+    if (!isq) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int d = lane + 64 * i;
+            if (d >= hd) continue;
+            const float v = s * sum_partials(a.pv, a.ksv, a.rows_kv, kt, prow, head * hd + d);
+            if (a.kv_bf16) ((uint16_t *)a.cache_v)[cache_off + d] = f32_to_bf16(v);
+            else ((float *)a.cache_v)[cache_off + d] = v;
+        }
     }
 }
 
 void launch_qkv_post(const QkvPostArgs &a, hipStream_t s) {
-    const int qt = a.nq * a.hd, kt = a.nkv * a.hd;
-    size_t sm = (size_t)(qt + 2 * kt + a.nq + a.nkv + 1) * sizeof(float) +
-                (size_t)(a.rotary_dim / 2 + 1) * sizeof(double);
-    hipLaunchKernelGGL(k_qkv_post, dim3(a.R + a.M), dim3(256), sm, s, a);
+    hipLaunchKernelGGL(k_qkv_post, dim3(a.M * a.nq + (a.R + a.M) * a.nkv), dim3(64), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
-// SwiGLU: h = silu(sum P_gate) * (sum P_up), split for the down projection.
-__global__ __launch_bounds__(256) void k_swiglu_split(const float *pg, int ksg, const float *pu,
-                                                      int ksu, int M, int I, uint16_t *xs) {
-    const int m = blockIdx.x;
-    const bool valid = m < M;
-    const int Ip = (I + 31) & ~31;
-    for (int k = threadIdx.x; k < Ip; k += 256) {
-        float h = 0.f;
-        if (valid && k < I) {
-            float g = 0.f, u = 0.f;
-            for (int t = 0; t < ksg; t++) g += pg[((size_t)t * 16 + m) * I + k];
-            for (int t = 0; t < ksu; t++) u += pu[((size_t)t * 16 + m) * I + k];
+// SwiGLU: h = silu(s_m * sum P_gate) * (s_m * sum P_up), split for the down
+// projection (s_m: RMSNorm scale of the FFN input row).
+__global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
+    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int k = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int Ip = (a.I + 31) & ~31;
+    float h = 0.f;
+    if (m < a.M) {
+        const float s = row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
+        if (k < a.I) {
+            const float g = s * sum_partials(a.pg, a.ksg, 16, a.I, m, k);
+            const float u = s * sum_partials(a.pu, a.ksu, 16, a.I, m, k);
             h = g / (1.0f + expf(-g)) * u;
         }
-        split_store(xs, m, k, h);
     }
+    if (k < Ip) split_store(a.xs, m, k, h);
 }
 
-void launch_swiglu_split(const float *pg, int ksg, const float *pu, int ksu, int M, int I,
-                         uint16_t *xs, hipStream_t s) {
-    hipLaunchKernelGGL(k_swiglu_split, dim3(16), dim3(256), 0, s, pg, ksg, pu, ksu, M, I, xs);
+void launch_swiglu(const SwigluArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_swiglu, dim3((a.I + 63) / 64, 4), dim3(256), 0, s, a);
 }
 
 }  // namespace dbf
