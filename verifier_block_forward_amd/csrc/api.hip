@@ -113,7 +113,7 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.ssp_h = take((size_t)16 * p.ncb * f);
     p.qbuf = take((size_t)DBF_MAX_M * p.qt * f);
     p.gbuf = take((size_t)DBF_MAX_M * p.qt * f);
-    p.attn = take((size_t)64 * DBF_MAX_M * c.n_q_heads * (c.head_dim + 2) * f);
+    p.attn = take((size_t)ATT_CHUNKS_MAX * DBF_MAX_M * c.n_q_heads * (c.head_dim + ATT_PART_EXTRA) * f);
     p.p_in0 = take((size_t)p.in.ksplit * 16 * p.H * f);
     p.p_in1 = take((size_t)p.in.ksplit * 16 * p.H * f);
     p.p_q = take((size_t)p.q.ksplit * 16 * p.qt * f);
@@ -386,7 +386,11 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     }
 
     int chunk = 0, n_chunks = 0;
-    attn_plan(P0 + R + M, &chunk, &n_chunks);
+    {
+        const int nq_group = (c.n_q_heads / c.n_kv_heads) * M;
+        const int qt = attn_qtiles(hd, nq_group);
+        attn_plan(P0 + R + M, nq_group < 16 * qt ? nq_group : 16 * qt, &chunk, &n_chunks);
+    }
     const size_t elt = cache->dtype == DBF_BF16 ? 2 : 4;
     const size_t layer_stride = (size_t)c.n_kv_heads * cache->capacity * hd * elt;
 

@@ -14,179 +14,356 @@
 
 namespace dbf {
 
-constexpr int ATT_MAX_CHUNKS = 64;
+constexpr int ATT_KT = 16;     // keys per sub-tile
+constexpr int ATT_WAVES = 4;   // waves per workgroup, each on a quarter of the chunk
 
-void attn_plan(long long n_keys, int *chunk, int *n_chunks) {
-    long long per = (n_keys + ATT_MAX_CHUNKS - 1) / ATT_MAX_CHUNKS;
-    long long c = ((per + 63) / 64) * 64;
-    if (c < 64) c = 64;
-    *chunk = (int)c;
-    *n_chunks = (int)((n_keys + c - 1) / c);
+// Keys per wave: at least 16 and as many as the queries a wave serves (so the
+// (acc, m, l) partial of a 4-wave chunk stays ~1/8 of its K/V bytes), grown until
+// there are at most ATT_CHUNKS_MAX chunks.
+void attn_plan(long long n_keys, int nq_per_wave, int *chunk, int *n_chunks) {
+    long long pw = (nq_per_wave + ATT_KT - 1) / ATT_KT * ATT_KT;
+    if (pw < ATT_KT) pw = ATT_KT;
+    long long per = (n_keys + ATT_CHUNKS_MAX - 1) / ATT_CHUNKS_MAX;           // keys per chunk
+    long long pw_min = (per + ATT_WAVES * ATT_KT - 1) / (ATT_WAVES * ATT_KT) * ATT_KT;
+    if (pw < pw_min) pw = pw_min;
+    *chunk = (int)(ATT_WAVES * pw);
+    *n_chunks = (int)((n_keys + *chunk - 1) / *chunk);
 }
 
-// HD head_dim, QB queries per block, KT keys per LDS tile; TPQ = 256/QB threads
-// share one query: each scores KT/TPQ keys and accumulates HD/TPQ output lanes.
-template <int HD, int QB, int KT>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-    constexpr int TPQ = 256 / QB, KPT = KT / TPQ, DPT = HD / TPQ, HDP = HD + 1;
-    static_assert(KPT >= 1 && DPT >= 1, "tile shape");
-    __shared__ float Qs[QB * HDP];   // pre-scaled queries
-    __shared__ float Ks[KT * HDP];
-    __shared__ float Vs[KT * HD];
-    __shared__ float Ps[QB * (KT + 1)];
+int attn_qtiles(int hd, int nq_group) {
+    const int need = (nq_group + 15) / 16;
+    const int cap = hd == 256 ? 2 : 4;
+    return need < cap ? (need <= 1 ? 1 : (need <= 2 ? 2 : 4)) : cap;
+}
 
-    const int c = blockIdx.x, kvh = blockIdx.y, qg = blockIdx.z;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const __bf16 h = (__bf16)v[j];
+        hi[j] = h;
+        lo[j] = (__bf16)(v[j] - (float)h);
+    }
+}
+
+template <int HD, int QT, bool KVB>
+struct AttnLds {
+    static constexpr int S = HD / 32, DT = HD / 16, VTW = 22;
+    static constexpr int Q_BYTES = QT * S * 2 * 64 * 16;
+    static constexpr int VPLANE = HD * VTW * 2;  // bytes of one V^T plane
+    static constexpr int V_BYTES = ATT_WAVES * VPLANE * (KVB ? 1 : 2);
+    static constexpr int LOOP = Q_BYTES + V_BYTES;
+    static constexpr int ACC_BYTES = (ATT_WAVES - 1) * QT * DT * 64 * 16;
+    static constexpr int ML_BYTES = ATT_WAVES * QT * 64 * 8;
+    static constexpr int MERGE = ACC_BYTES + ML_BYTES;
+    static constexpr int BYTES = LOOP > MERGE ? LOOP : MERGE;
+};
+
+// One workgroup (4 waves) per (key chunk, kv head, group of up to 16*QT queries);
+// wave w takes the w-th quarter of the chunk and the four online-softmax states are
+// merged through LDS at the end, so the chunk writes a single (acc, m, l) partial.
+// Scores are formed transposed, S^T[key][q] = K Q^T (v_mfma_f32_16x16x32_bf16,
+// A = 16 keys x 32 dims straight from the cache rows, B = pre-scaled queries split
+// hi/lo in LDS). That accumulator layout (lane: keys 4g..4g+3 of query l%16) is the
+// B operand of v_mfma_f32_16x16x16_bf16 for O^T[d][q] += V^T[d][key] P^T[key][q],
+// so the probabilities never leave their lanes; V is transposed through LDS.
+// F32 caches are split hi/lo (three products: hh, hl, lh); BF16 caches are exact
+// (two products: h*K, l*K).
+template <int HD, int QT, bool KVB>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+    using L = AttnLds<HD, QT, KVB>;
+    constexpr int S = L::S, DT = L::DT, VTW = L::VTW;
+    __shared__ __align__(16) unsigned char smem[L::BYTES];
+    uint4 *qsm = (uint4 *)smem;
+
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    uint16_t *vth = (uint16_t *)(smem + L::Q_BYTES + w * L::VPLANE * (KVB ? 1 : 2));
+    uint16_t *vtl = vth + HD * VTW;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int c = blockIdx.x, kvh = blockIdx.y;
     const int G = a.nq / a.nkv;
     const int NQ = G * a.M;
-    const int q0 = qg * QB;
-    const int t = threadIdx.x, qi = t / TPQ, sub = t % TPQ;
+    const int q0 = blockIdx.z * 16 * QT;
     const long long n_all = a.n_ctx + a.M;
-    const long long k_lo = (long long)c * a.chunk;
-    long long k_hi = k_lo + a.chunk;
-    if (k_hi > n_all) k_hi = n_all;
+    const int pw = a.chunk / ATT_WAVES;
+    const long long c_hi = (long long)(c + 1) * a.chunk < n_all ? (long long)(c + 1) * a.chunk : n_all;
+    const long long k_lo = (long long)c * a.chunk + (long long)w * pw;
+    const long long k_hi = k_lo + pw < c_hi ? k_lo + pw : c_hi;  // may be <= k_lo: wave idle
     const float scale = 1.0f / sqrtf((float)HD);
 
-    const bool qvalid = q0 + qi < NQ;
-    const int gq = qvalid ? q0 + qi : NQ - 1;  // padding slots recompute a valid query
-    const int qm = gq / G, qh = kvh * G + gq % G;
-    const long long qlim = a.n_ctx + qm;  // last visible key position
-
-    for (int i = t; i < QB * HD; i += 256) {
-        const int r = i / HD, d = i - r * HD;
-        const int g2 = q0 + r < NQ ? q0 + r : NQ - 1;
-        const int m2 = g2 / G, h2 = kvh * G + g2 % G;
-        Qs[r * HDP + d] = a.q[(size_t)m2 * a.nq * HD + (size_t)h2 * HD + d] * scale;
+    int qm[QT];
+    bool qv[QT];
+#pragma unroll
+    for (int t = 0; t < QT; t++) {
+        const int gq = q0 + 16 * t + r16;
+        qv[t] = gq < NQ;
+        qm[t] = (qv[t] ? gq : NQ - 1) / G;
+    }
+    // B operand of the score MFMA, written cooperatively: lane holds dims 32s+8g..+7
+    for (int idx = w; idx < QT * S; idx += ATT_WAVES) {
+        const int t = idx / S, st = idx % S;
+        const int gq = q0 + 16 * t + r16;
+        const int gqc = gq < NQ ? gq : NQ - 1;
+        const int h = kvh * G + gqc % G;
+        float v[8];
+        const float *src = a.q + (size_t)(gqc / G) * a.nq * HD + (size_t)h * HD + 32 * st + 8 * g;
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = src[j] * scale;
+        bf16x8 hi, lo;
+        split8(v, hi, lo);
+        qsm[(idx * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4, hi);
+        qsm[(idx * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo);
     }
 
-    const size_t head_off = (size_t)kvh * a.capacity * HD;
-    float m_run = -INFINITY, l_run = 0.f;
-    float acc[DPT];
+    float m_run[QT], l_run[QT];
+    f32x4 acc[QT][DT];
 #pragma unroll
-    for (int i = 0; i < DPT; i++) acc[i] = 0.f;
+    for (int t = 0; t < QT; t++) {
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+#pragma unroll
+        for (int d = 0; d < DT; d++) acc[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const size_t head_off = (size_t)kvh * a.capacity * HD;
+    const int n_sub = pw / ATT_KT;  // same trip count in every wave (block barriers)
 
-    for (long long kb = k_lo; kb < k_hi; kb += KT) {
-        __syncthreads();
-        const int nk = (int)((k_hi - kb) < KT ? (k_hi - kb) : KT);
-        for (int i = t; i < KT * HD; i += 256) {
-            const int r = i / HD, d = i - r * HD;
-            float kv = 0.f, vv = 0.f;
-            if (r < nk) {
-                const size_t off = head_off + (size_t)(kb + r) * HD + d;
-                if (a.kv_bf16) {
-                    kv = bf16_to_f32(((const uint16_t *)a.cache_k)[off]);
-                    vv = bf16_to_f32(((const uint16_t *)a.cache_v)[off]);
-                } else {
-                    kv = ((const float *)a.cache_k)[off];
-                    vv = ((const float *)a.cache_v)[off];
+    for (int it = 0; it < n_sub; it++) {
+        const long long kb = k_lo + (long long)it * ATT_KT;
+        long long krow = kb + r16;  // this lane's key row, clamped to a valid row
+        if (krow > n_all - 1) krow = n_all - 1;
+        bf16x8 kh[S], kl[S];
+        __syncthreads();  // Q written / previous sub-tile's V^T reads done
+#pragma unroll
+        for (int st = 0; st < S; st++) {
+            const int d0 = 32 * st + 8 * g;
+            const size_t off = head_off + (size_t)krow * HD + d0;
+            if (KVB) {
+                kh[st] = __builtin_bit_cast(bf16x8, *(const uint4 *)((const uint16_t *)a.cache_k + off));
+                const uint4 vraw = *(const uint4 *)((const uint16_t *)a.cache_v + off);
+                const uint16_t *vv = (const uint16_t *)&vraw;
+#pragma unroll
+                for (int j = 0; j < 8; j++) vth[(d0 + j) * VTW + r16] = vv[j];
+            } else {
+                const float4 *kp = (const float4 *)((const float *)a.cache_k + off);
+                const float4 *vp = (const float4 *)((const float *)a.cache_v + off);
+                const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+                const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                split8(kf, kh[st], kl[st]);
+                // V^T planes, converted element by element through scalars
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const uint16_t hb = f32_to_bf16(vf[j]);
+                    vth[(d0 + j) * VTW + r16] = hb;
+                    vtl[(d0 + j) * VTW + r16] = f32_to_bf16(vf[j] - bf16_to_f32(hb));
                 }
             }
-            Ks[r * HDP + d] = kv;
-            Vs[r * HD + d] = vv;
         }
-        __syncthreads();
-        float s[KPT];
+        f32x4 sc[QT];
 #pragma unroll
-        for (int u = 0; u < KPT; u++) s[u] = 0.f;
-        const float *qr = Qs + qi * HDP;
-        for (int d = 0; d < HD; d++) {
-            const float qv = qr[d];
+        for (int t = 0; t < QT; t++) {
+            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < KPT; u++) s[u] += qv * Ks[(sub + TPQ * u) * HDP + d];
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < KPT; u++) {
-            const int j = sub + TPQ * u;
-            if (!(j < nk && kb + j <= qlim)) s[u] = -INFINITY;
-            tmax = fmaxf(tmax, s[u]);
-        }
-#pragma unroll
-        for (int o = 1; o < TPQ; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.f, psum = 0.f;
-        if (m_new != -INFINITY) {
-            alpha = expf(m_run - m_new);
-#pragma unroll
-            for (int u = 0; u < KPT; u++) {
-                s[u] = expf(s[u] - m_new);
-                psum += s[u];
+            for (int st = 0; st < S; st++) {
+                const bf16x8 qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
+                const bf16x8 ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], qh, sc[t], 0, 0, 0);
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], ql, sc[t], 0, 0, 0);
+                if (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[st], qh, sc[t], 0, 0, 0);
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < KPT; u++) s[u] = 0.f;
         }
+        s16x4 ph[QT], pl[QT];
+        float alpha[QT];
 #pragma unroll
-        for (int o = 1; o < TPQ; o <<= 1) psum += __shfl_xor(psum, o, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        for (int t = 0; t < QT; t++) {
+            const long long lim = a.n_ctx + qm[t];  // last key visible to this query
+            float v[4];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < KPT; u++) Ps[qi * (KT + 1) + sub + TPQ * u] = s[u];
-        __syncthreads();
+            for (int i = 0; i < 4; i++) {
+                const long long kp = kb + 4 * g + i;
+                v[i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
+                mx = fmaxf(mx, v[i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run[t], mx);
+            float al = 1.f, ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < DPT; i++) acc[i] *= alpha;
-        for (int j = 0; j < KT; j++) {
-            const float p = Ps[qi * (KT + 1) + j];
+            for (int i = 0; i < 4; i++) {
+                const float p = m_new == -INFINITY ? 0.f : expf(v[i] - m_new);
+                ps += p;
+                const __bf16 h = (__bf16)p;
+                ph[t][i] = __builtin_bit_cast(short, h);
+                pl[t][i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
+            }
+            if (m_new != -INFINITY) al = expf(m_run[t] - m_new);
+            ps += __shfl_xor(ps, 16, 64);
+            ps += __shfl_xor(ps, 32, 64);
+            l_run[t] = l_run[t] * al + ps;
+            m_run[t] = m_new;
+            alpha[t] = al;
+        }
+        __syncthreads();  // V^T of this sub-tile is in LDS
 #pragma unroll
-            for (int i = 0; i < DPT; i++) acc[i] += p * Vs[j * HD + sub + TPQ * i];
+        for (int d = 0; d < DT; d++) {
+            const int row = (16 * d + r16) * VTW + 4 * g;
+            const uint32_t *vr = (const uint32_t *)(vth + row);
+            const s16x4 vh = __builtin_bit_cast(s16x4, make_uint2(vr[0], vr[1]));
+            s16x4 vl;
+            if (!KVB) {
+                const uint32_t *vq = (const uint32_t *)(vtl + row);
+                vl = __builtin_bit_cast(s16x4, make_uint2(vq[0], vq[1]));
+            }
+#pragma unroll
+            for (int t = 0; t < QT; t++) {
+                f32x4 o = acc[t][d] * alpha[t];
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, ph[t], o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, pl[t], o, 0, 0, 0);
+                if (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vl, ph[t], o, 0, 0, 0);
+                acc[t][d] = o;
+            }
         }
     }
-    if (qvalid) {
-        const size_t qidx = (size_t)qm * a.nq + qh;
-        float *o = a.part + ((size_t)c * a.M * a.nq + qidx) * (HD + 2);
+
+    // merge the four waves' (m, l, acc) through LDS (the loop buffers are dead now)
+    __syncthreads();
+    float4 *accb = (float4 *)smem;                       // [3][QT][DT][64]
+    float2 *mlb = (float2 *)(smem + L::ACC_BYTES);      // [4][QT][64]
 #pragma unroll
-        for (int i = 0; i < DPT; i++) o[sub + TPQ * i] = acc[i];
-        if (sub == 0) {
-            o[HD] = m_run;
-            o[HD + 1] = l_run;
+    for (int t = 0; t < QT; t++) {
+        mlb[(w * QT + t) * 64 + lane] = make_float2(m_run[t], l_run[t]);
+        if (w > 0)
+#pragma unroll
+            for (int d = 0; d < DT; d++)
+                accb[(((w - 1) * QT + t) * DT + d) * 64 + lane] =
+                    make_float4(acc[t][d][0], acc[t][d][1], acc[t][d][2], acc[t][d][3]);
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int t = 0; t < QT; t++) {
+        float mw[ATT_WAVES], lw[ATT_WAVES];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < ATT_WAVES; v++) {
+            const float2 ml = mlb[(v * QT + t) * 64 + lane];
+            mw[v] = ml.x;
+            lw[v] = ml.y;
+            if (ml.y > 0.f) mx = fmaxf(mx, ml.x);
+        }
+        float e[ATT_WAVES], lsum = 0.f;
+#pragma unroll
+        for (int v = 0; v < ATT_WAVES; v++) {
+            e[v] = lw[v] > 0.f ? expf(mw[v] - mx) : 0.f;
+            lsum += lw[v] * e[v];
+        }
+        if (!qv[t]) continue;
+        const int gq = q0 + 16 * t + r16;
+        const int h = kvh * G + gq % G;
+        const size_t qidx = (size_t)qm[t] * a.nq + h;
+        float *o = a.part + ((size_t)c * a.M * a.nq + qidx) * (HD + ATT_PART_EXTRA);
+#pragma unroll
+        for (int d = 0; d < DT; d++) {
+            f32x4 s4 = acc[t][d] * e[0];
+#pragma unroll
+            for (int v = 1; v < ATT_WAVES; v++) {
+                const float4 q4 = accb[(((v - 1) * QT + t) * DT + d) * 64 + lane];
+                s4 += f32x4{q4.x, q4.y, q4.z, q4.w} * e[v];
+            }
+            *(float4 *)(o + 16 * d + 4 * g) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+        }
+        if (g == 0) {
+            o[HD] = lsum > 0.f ? mx : -INFINITY;
+            o[HD + 1] = lsum;
         }
     }
 }
 
 bool attn_supported(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 
+template <int HD, bool KVB>
+static void go_attn(const AttnArgs &a, int qt, dim3 grid, hipStream_t s) {
+    if (qt == 1) hipLaunchKernelGGL((k_attn<HD, 1, KVB>), grid, dim3(256), 0, s, a);
+    else if (qt == 2) hipLaunchKernelGGL((k_attn<HD, 2, KVB>), grid, dim3(256), 0, s, a);
+    else if (HD != 256) hipLaunchKernelGGL((k_attn<HD, (HD == 256 ? 2 : 4), KVB>), grid, dim3(256), 0, s, a);
+}
+
 void launch_attn(const AttnArgs &a, hipStream_t s) {
     const int G = a.nq / a.nkv;
     const int NQ = G * a.M;
-    const int QB = a.hd == 256 ? 16 : 32;
-    dim3 grid(a.n_chunks, a.nkv, (NQ + QB - 1) / QB);
-    if (a.hd == 64) hipLaunchKernelGGL((k_attn<64, 32, 32>), grid, dim3(256), 0, s, a);
-    else if (a.hd == 128) hipLaunchKernelGGL((k_attn<128, 32, 32>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<256, 16, 16>), grid, dim3(256), 0, s, a);
+    const int qt = attn_qtiles(a.hd, NQ);
+    dim3 grid(a.n_chunks, a.nkv, (NQ + 16 * qt - 1) / (16 * qt));
+    if (a.kv_bf16) {
+        if (a.hd == 64) go_attn<64, true>(a, qt, grid, s);
+        else if (a.hd == 128) go_attn<128, true>(a, qt, grid, s);
+        else go_attn<256, true>(a, qt, grid, s);
+    } else {
+        if (a.hd == 64) go_attn<64, false>(a, qt, grid, s);
+        else if (a.hd == 128) go_attn<128, false>(a, qt, grid, s);
+        else go_attn<256, false>(a, qt, grid, s);
+    }
 }
 
-// Merge chunk partials of query (m, h), apply the optional sigmoid gate and write
-// the attention output row into the split tile of the O projection. Rows m >= M
-// and the padding columns are written as zeros.
+// Merge the chunk partials of query (m, h), apply the optional sigmoid gate and
+// write the attention output row into the split tile of the O projection. The
+// chunk weights exp(m_c - max) are formed once per query in LDS; the weighted sums
+// then read all chunks with independent loads. Rows m >= M and the padding columns
+// are written as zeros.
 __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
-    const int m = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-    const int hd = a.hd, K = a.nq * hd;
-    if (d < hd) {
+    __shared__ float wgt[ATT_CHUNKS_MAX];
+    __shared__ float red[8];
+    const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int hd = a.hd, K = a.nq * hd, rec = hd + ATT_PART_EXTRA;
+    const bool valid = m < a.M;
+    float lsum = 0.f;
+    if (valid) {
+        const size_t q = (size_t)m * a.nq + h;
+        const size_t stride = (size_t)a.M * a.nq * rec;
+        float mc = -INFINITY, lc = 0.f;
+        if (tid < a.n_chunks) {
+            const float *p = a.part + tid * stride + q * rec;
+            mc = p[hd];
+            lc = p[hd + 1];
+            if (!(lc > 0.f)) mc = -INFINITY;
+        }
+        float mx = wave_max(mc);
+        if ((tid & 63) == 0) red[tid >> 6] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        const float e = (tid < a.n_chunks && lc > 0.f) ? expf(mc - mx) : 0.f;
+        if (tid < ATT_CHUNKS_MAX) wgt[tid] = e;
+        float ls = wave_sum(lc * e);
+        __syncthreads();
+        if ((tid & 63) == 0) red[4 + (tid >> 6)] = ls;
+        __syncthreads();
+        lsum = (red[4] + red[5]) + (red[6] + red[7]);
+    }
+    for (int d = tid; d < hd; d += blockDim.x) {
         float o = 0.f;
-        if (m < a.M) {
+        if (valid) {
             const size_t q = (size_t)m * a.nq + h;
-            const size_t stride = (size_t)a.M * a.nq * (hd + 2);
-            float mx = -INFINITY;
-            for (int c = 0; c < a.n_chunks; c++) {
-                const float *p = a.part + c * stride + q * (hd + 2);
-                if (p[hd + 1] > 0.f) mx = fmaxf(mx, p[hd]);
+            const size_t stride = (size_t)a.M * a.nq * rec;
+            const float *p = a.part + q * rec + d;
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+            int c = 0;
+            for (; c + 3 < a.n_chunks; c += 4) {
+                s0 += p[(c + 0) * stride] * wgt[c + 0];
+                s1 += p[(c + 1) * stride] * wgt[c + 1];
+                s2 += p[(c + 2) * stride] * wgt[c + 2];
+                s3 += p[(c + 3) * stride] * wgt[c + 3];
             }
-            float l = 0.f, acc = 0.f;
-            for (int c = 0; c < a.n_chunks; c++) {
-                const float *p = a.part + c * stride + q * (hd + 2);
-                if (p[hd + 1] > 0.f) {
-                    const float e = expf(p[hd] - mx);
-                    l += p[hd + 1] * e;
-                    acc += p[d] * e;
-                }
-            }
-            o = acc / l;
+            for (; c < a.n_chunks; c++) s0 += p[c * stride] * wgt[c];
+            o = ((s0 + s1) + (s2 + s3)) / lsum;
             if (a.g) o *= sigmoidf_(a.g[(size_t)m * K + h * hd + d]);
         }
         split_store(a.xs, m, h * hd + d, o);
     }
     if (h == a.nq - 1) {
         const int Kp = (K + 31) & ~31;
-        for (int k = K + d; k < Kp; k += blockDim.x) split_store(a.xs, m, k, 0.f);
+        for (int k = K + tid; k < Kp; k += blockDim.x) split_store(a.xs, m, k, 0.f);
     }
 }
 

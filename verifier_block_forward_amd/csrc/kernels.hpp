@@ -119,9 +119,12 @@ struct AttnArgs {
     long long n_ctx;       // keys visible to block row 0 minus one: P0 + R
     int M, nq, nkv, hd;
     int chunk, n_chunks;
-    float *part;           // [n_chunks][M*nq][hd + 2]
+    float *part;           // [n_chunks][M*nq][hd + 4]
 };
-void attn_plan(long long n_keys, int *chunk, int *n_chunks);
+constexpr int ATT_PART_EXTRA = 4;  // partial record: acc[hd], m, l, 2 pad floats
+constexpr int ATT_CHUNKS_MAX = 256;
+void attn_plan(long long n_keys, int nq_per_wave, int *chunk, int *n_chunks);
+int attn_qtiles(int hd, int nq_group);
 bool attn_supported(int hd);
 void launch_attn(const AttnArgs &a, hipStream_t s);
 
