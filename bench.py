@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--row-major", action="store_true",
+                    help="keep projection weights row-major instead of the tiled layout")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after the timed region (counter scale)")
     args = ap.parse_args()
@@ -128,6 +130,12 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     w_dev = {k: up(v) for k, v in w_host.items()}
+    if not args.row_major:
+        # weights resident in the tiled matrix-core layout (packed once, at upload)
+        for k in list(w_dev):
+            if w_dev[k].dtype == torch.bfloat16 and k != "embed":
+                w_dev[k] = dbf.tile_weight(w_dev[k])
+        torch.cuda.synchronize()
     inp = {k: up(v) for k, v in in_host.items() if isinstance(v, np.ndarray) and v.size}
     bw = dbf.BlockWeights(cfg, w_dev)
     ccfg = dbf.make_config(cfg)
@@ -214,7 +222,8 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.description}", "layers": cfg.n_layers,
                    "hidden": H, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "vocab": V, "M": M, "R": R, "context": cfg.C, "kv_dtype": cfg.kv_dtype,
-                   "weights": "bf16", "parallelism": "single GPU"},
+                   "weights": "bf16 row-major" if args.row_major else "bf16 tiled",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": f"{HEAD_KERNEL} (lm_head_argmax call)",
                      "achieved": round(head_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(head_gbps / PEAK_HBM_GBPS, 4),

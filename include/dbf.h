@@ -27,6 +27,11 @@
  *     norm weight of any other dtype is rejected with DBF_EDTYPE).
  *   - Inner (input) dimensions of every projection must be multiples of 8 (the
  *     kernels stream weights in 16-byte vectors); DBF_ESHAPE otherwise.
+ *   - Every projection weight (and lm_head, embed excepted) may instead be given in
+ *     the tiled layout DBF_BF16_T16 produced once at upload time by
+ *     dbf_tile_weight: same logical shape, stored in the order the gfx950 matrix
+ *     cores consume it, which streams ~1.35x faster than row-major. Layouts may be
+ *     mixed freely across tensors.
  */
 #ifndef DBF_H
 #define DBF_H
@@ -53,6 +58,7 @@ extern "C" {
 #define DBF_F32 0
 #define DBF_BF16 1
 #define DBF_I32 2
+#define DBF_BF16_T16 3 /* BF16 weight tiled for the matrix cores (dbf_tile_weight) */
 
 /* block kinds */
 #define DBF_KIND_DFLASH 0 /* DFlash drafter ([TENS] `DFlashModelTensors`) */
@@ -220,6 +226,18 @@ int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const
 /* KV rollback ([ORCH] per-round step 8: drop the rejected positions). Host-side
  * metadata only: cache->seq_len -= n. DBF_ERANGE when n < 0 or n > seq_len. */
 int kv_rollback(dbf_kv_cache *cache, int32_t n);
+
+/* Tiled weight layout. For a row-major BF16 weight [N, K] (or a batch [B, N, K] of
+ * them, e.g. MoE experts), the tiled copy holds ceil(N/16) x ceil(K/32) blocks of
+ * 1 KiB; element (n, k) sits at BF16 offset
+ *   ((n/16 * ceil(K/32) + k/32) * 64 + ((k % 32) / 8) * 16 + n % 16) * 8 + k % 8
+ * and padding rows/columns are zero. Matrices of a batch follow one another.
+ * dbf_tiled_bytes: bytes of one tiled [N, K] matrix.
+ * dbf_tile_weight: enqueue the repack of src (BF16, ndim 2 or 3, device) into dst
+ * (device, batch * dbf_tiled_bytes bytes, caller-owned; must not overlap src).
+ * Pass the result as a dbf_tensor {dst, DBF_BF16_T16, same ndim and shape}. */
+size_t dbf_tiled_bytes(int64_t N, int64_t K);
+int dbf_tile_weight(const dbf_tensor *src, void *dst, void *stream);
 
 /* Description of the last error on the calling thread ("" when none). */
 const char *dbf_last_error(void);

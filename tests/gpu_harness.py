@@ -58,13 +58,19 @@ def decode_bf16(u16):
 class Prepared:
     """Device copies of one workload's weights and inputs."""
 
-    def __init__(self, cfg, weights=None, inputs=None):
+    def __init__(self, cfg, weights=None, inputs=None, tiled=False):
+        """tiled: True (every projection + lm_head tiled), False, or a set of names."""
         from verifier_block_forward_amd import dbf
         t = torch()
         self.cfg = cfg
         self.w_host = weights if weights is not None else synth.make_weights(cfg)
         self.in_host = inputs if inputs is not None else synth.make_inputs(cfg)
         self.w_dev = {k: to_dev(v) for k, v in self.w_host.items()}
+        if tiled:
+            for k, v in list(self.w_dev.items()):
+                if v.dtype == t.bfloat16 and k != "embed" and (tiled is True or k in tiled):
+                    self.w_dev[k] = dbf.tile_weight(v)
+            t.cuda.synchronize()
         self.bw = dbf.BlockWeights(cfg, self.w_dev)
         self.ccfg = dbf.make_config(cfg)
         self.inp = {k: to_dev(v) for k, v in self.in_host.items()

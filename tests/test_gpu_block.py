@@ -106,3 +106,57 @@ def test_block_incremental_context(orc):
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
 def test_block_full_size(orc, name):
     run_case(orc, configs.get(name))
+
+
+# ---------------------------------------------------------------------------
+# tiled weight layout
+# ---------------------------------------------------------------------------
+
+def tiled_reference(w: np.ndarray) -> np.ndarray:
+    """The tiled layout written out element by element from its definition in dbf.h."""
+    B = w.shape[0] if w.ndim == 3 else 1
+    w3 = w.reshape(B, w.shape[-2], w.shape[-1])
+    N, K = w3.shape[1:]
+    T, S = (N + 15) // 16, (K + 31) // 32
+    out = np.zeros((B, T * S * 512), np.uint16)
+    n, k = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+    off = ((n // 16 * S + k // 32) * 64 + ((k % 32) // 8) * 16 + n % 16) * 8 + k % 8
+    for b in range(B):
+        out[b, off.ravel()] = w3[b].ravel()
+    return out.ravel()
+
+
+@pytest.mark.parametrize("shape", [(37, 200), (16, 32), (1, 8), (3, 33, 72), (300, 2816)])
+def test_tile_weight_layout(shape):
+    from verifier_block_forward_amd import dbf
+    from tests.gpu_harness import to_dev, torch
+    w = synth.normal_bf16(9, len(shape), shape)
+    tw = dbf.tile_weight(to_dev(w))
+    torch().cuda.synchronize()
+    got = tw.data.view(torch().int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, tiled_reference(w))
+
+
+@pytest.mark.parametrize("cfg", [small(), small(name="small_mtp_t", kind="mtp", R=0, M=2,
+                                                has_attn_gate=True, n_layers=1, n_target_hidden=0)],
+                         ids=lambda c: c.name)
+def test_block_tiled_weights(orc, cfg):
+    prep = Prepared(cfg, tiled=True)
+    got = prep.run()
+    want = orc.block_forward(cfg, prep.w_host, prep.in_host)
+    gk, gv = prep.cache_host(*got["cache"])
+    s0 = cfg.C
+    compare_block(cfg, got, want, s0, s0 + cfg.R + cfg.M, (gk, gv), (want["cache_k"], want["cache_v"]))
+
+
+def test_block_mixed_layouts_bitwise():
+    """Tiled and row-major weights give bit-identical block outputs (same sums)."""
+    cfg = small()
+    a = Prepared(cfg).run()
+    b = Prepared(cfg, tiled={"layers.0.wq", "layers.1.ffn_down", "fc", "layers.0.wv"}).run()
+    assert np.array_equal(a["h_final"], b["h_final"])
+
+
+@pytest.mark.slow
+def test_block_c1_tiled(orc):
+    run_case(orc, configs.C1, prep=Prepared(configs.C1, tiled=True))

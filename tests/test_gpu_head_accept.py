@@ -12,12 +12,14 @@ def _dec(u16):
     return (np.asarray(u16, np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run_head(h, W, want_logits=True):
+def run_head(h, W, want_logits=True, tiled=False):
     from verifier_block_forward_amd import dbf
     t = torch()
     M, H = h.shape
     V = W.shape[0]
     hd, Wd = to_dev(h.astype(np.float32)), to_dev(W)
+    if tiled:
+        Wd = dbf.tile_weight(Wd)
     am = t.empty(M, dtype=t.int32, device="cuda")
     mg = t.empty(M, dtype=t.float32, device="cuda")
     lg = t.empty((M, V), dtype=t.float32, device="cuda") if want_logits else None
@@ -38,14 +40,15 @@ def check_argmax(name, am, lg_oracle, am_o, mg_o):
 
 @pytest.mark.parametrize("M,H,V", [(3, 264, 1000), (4, 256, 4096), (16, 200, 777), (1, 8, 65),
                                    (16, 2816, 262144), (1, 5120, 248320), (4, 2048, 248320)])
-def test_lm_head_argmax_parity(orc, M, H, V):
-    print(f"\n[lm_head] M={M} H={H} V={V}", flush=True)
+@pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
+def test_lm_head_argmax_parity(orc, M, H, V, tiled):
+    print(f"\n[lm_head] M={M} H={H} V={V} tiled={tiled}", flush=True)
     rng = np.random.default_rng(M * 1000 + H)
     W = synth.normal_bf16(77, H, (V, H))
     h = rng.standard_normal((M, H)).astype(np.float32)
     # normed-hidden scale: logits ~ N(0, 0.02^2 H)
     lg_o, am_o, mg_o = orc.lm_head(h.astype(np.float64), W)
-    lg, am, mg = run_head(h, W)
+    lg, am, mg = run_head(h, W, tiled=tiled)
     check_close(f"logits M{M} H{H} V{V}", lg, lg_o)
     check_argmax(f"argmax M{M} V{V}", am, lg_o, am_o, mg_o)
     check_close(f"margin M{M} V{V}", mg, mg_o)

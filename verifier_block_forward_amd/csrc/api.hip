@@ -29,12 +29,16 @@ int fail(int code, const char *fmt, ...) {
     return code;
 }
 
-const char *dtname(int dt) { return dt == DBF_F32 ? "F32" : dt == DBF_BF16 ? "BF16" : dt == DBF_I32 ? "I32" : "?"; }
+const char *dtname(int dt) {
+    return dt == DBF_F32 ? "F32" : dt == DBF_BF16 ? "BF16" : dt == DBF_I32 ? "I32" : dt == DBF_BF16_T16 ? "BF16_T16" : "?";
+}
 
 int check_t(const dbf_tensor &t, const char *name, int dtype, int ndim, int64_t s0, int64_t s1 = -1,
             int64_t s2 = -1) {
     if (!t.data) return fail(DBF_EINVAL, "%s: null data pointer", name);
-    if (t.dtype != dtype)
+    // projections (requested as BF16) may be row-major BF16 or tiled BF16_T16
+    const bool ok = t.dtype == dtype || (dtype == DBF_BF16 && t.dtype == DBF_BF16_T16);
+    if (!ok)
         return fail(DBF_EDTYPE, "%s: dtype %s, expected %s", name, dtname(t.dtype), dtname(dtype));
     const int64_t want[3] = {s0, s1, s2};
     if (t.ndim != ndim) return fail(DBF_ESHAPE, "%s: ndim %d, expected %d", name, t.ndim, ndim);
@@ -131,10 +135,11 @@ Plan make_plan(const dbf_config &c, int M, int R) {
 struct SegList {
     GemmArgs a{};
     int nbmax = 1;
-    void add(const uint16_t *W, int N, int K, const GemmPlan &pl, float *out, const uint16_t *xs0,
+    void add(const dbf_tensor &t, int N, int K, const GemmPlan &pl, float *out, const uint16_t *xs0,
              const uint16_t *xs1 = nullptr) {
         GemmSeg &s = a.seg[a.nseg++];
-        s.W = W;
+        s.W = (const uint16_t *)t.data;
+        s.tiled = t.dtype == DBF_BF16_T16;
         s.out = out;
         s.xs0 = xs0;
         s.xs1 = xs1;
@@ -188,7 +193,10 @@ int validate_weights(const dbf_config &c, const dbf_weights *w, bool need_embed)
     if (c.kind == DBF_KIND_DFLASH) {
         CHECK(check_t(w->fc, "fc", DBF_BF16, 2, H, (int64_t)c.n_target_hidden * H));
         CHECK(check_t(w->hidden_norm, "hidden_norm", DBF_F32, 1, H));
-        if (need_embed) CHECK(check_t(w->embed, "embed", DBF_BF16, 2, c.vocab, H));
+        if (need_embed) {
+            CHECK(check_t(w->embed, "embed", DBF_BF16, 2, c.vocab, H));
+            if (w->embed.dtype != DBF_BF16) return fail(DBF_EDTYPE, "embed must be row-major BF16");
+        }
     } else {
         CHECK(check_t(w->enorm, "enorm", DBF_F32, 1, H));
         CHECK(check_t(w->hnorm, "hnorm", DBF_F32, 1, H));
@@ -333,7 +341,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             t.xs = xs_T;
             launch_colsum(t, st);
             SegList sl;
-            sl.add((const uint16_t *)w->fc.data, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
+            sl.add(w->fc, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
             sl.launch(st);
             ColArgs h = col();
             h.M = R;
@@ -363,8 +371,8 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         h.ssp_out = ssp_h;
         launch_colsum(h, st);
         SegList sl;
-        sl.add((const uint16_t *)w->eh_embed.data, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
-        sl.add((const uint16_t *)w->eh_hidden.data, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
+        sl.add(w->eh_embed, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
+        sl.add(w->eh_hidden, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
         sl.launch(st);
         ColArgs x = col();
         x.M = M;
@@ -401,15 +409,15 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         float *pg = at<float>(ws, p.p_g);
         {
             SegList sl;
-            sl.add((const uint16_t *)L.wq.data, qt, H, p.q, pq, xs_blk);
+            sl.add(L.wq, qt, H, p.q, pq, xs_blk);
             if (R > 0) {
-                sl.add((const uint16_t *)L.wk.data, kt, H, p.k, pk, xs_hctx, xs_blk);
-                sl.add((const uint16_t *)L.wv.data, kt, H, p.v, pv, xs_hctx, xs_blk);
+                sl.add(L.wk, kt, H, p.k, pk, xs_hctx, xs_blk);
+                sl.add(L.wv, kt, H, p.v, pv, xs_hctx, xs_blk);
             } else {
-                sl.add((const uint16_t *)L.wk.data, kt, H, p.k, pk, xs_blk);
-                sl.add((const uint16_t *)L.wv.data, kt, H, p.v, pv, xs_blk);
+                sl.add(L.wk, kt, H, p.k, pk, xs_blk);
+                sl.add(L.wv, kt, H, p.v, pv, xs_blk);
             }
-            if (c.has_attn_gate) sl.add((const uint16_t *)L.attn_gate.data, qt, H, p.g, pg, xs_blk);
+            if (c.has_attn_gate) sl.add(L.attn_gate, qt, H, p.g, pg, xs_blk);
             sl.launch(st);
         }
         void *ck = (char *)cache->k + l * layer_stride;
@@ -477,7 +485,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         }
         {
             SegList sl;
-            sl.add((const uint16_t *)L.wo.data, H, qt, p.o, at<float>(ws, p.p_o), xs_o);
+            sl.add(L.wo, H, qt, p.o, at<float>(ws, p.p_o), xs_o);
             sl.launch(st);
             // x1 = x + o Wo^T; split(x1 (.) post_norm) for the FFN
             ColArgs a = col();
@@ -495,8 +503,8 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         }
         {
             SegList sl;
-            sl.add((const uint16_t *)L.ffn_gate.data, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
-            sl.add((const uint16_t *)L.ffn_up.data, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
+            sl.add(L.ffn_gate, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
+            sl.add(L.ffn_up, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
             sl.launch(st);
             SwigluArgs sa{};
             sa.pg = at<float>(ws, p.p_gate);
@@ -512,7 +520,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             sa.xs = xs_ff;
             launch_swiglu(sa, st);
             SegList sd;
-            sd.add((const uint16_t *)L.ffn_down.data, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
+            sd.add(L.ffn_down, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
             sd.launch(st);
         }
         {
@@ -554,7 +562,8 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
     if (H < 8 || H % 8) return fail(DBF_ESHAPE, "H = %d must be a positive multiple of 8", H);
     if (lm_head->ndim != 2 || lm_head->shape[1] != H || lm_head->shape[0] < 1)
         return fail(DBF_ESHAPE, "lm_head must be [V, %d]", H);
-    if (lm_head->dtype != DBF_BF16) return fail(DBF_EDTYPE, "lm_head dtype %s, expected BF16", dtname(lm_head->dtype));
+    if (lm_head->dtype != DBF_BF16 && lm_head->dtype != DBF_BF16_T16)
+        return fail(DBF_EDTYPE, "lm_head dtype %s, expected BF16 or BF16_T16", dtname(lm_head->dtype));
     if (!lm_head->data) return fail(DBF_EINVAL, "lm_head data is null");
     if (lm_head->shape[0] > 0x7fffffffLL) return fail(DBF_ESHAPE, "vocabulary too large");
     const int V = (int)lm_head->shape[0];
@@ -573,7 +582,8 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
     a.ldb = H;
     a.xs = xs;
     launch_colsum(a, st);
-    launch_head((const uint16_t *)lm_head->data, xs, V, H, M, logits, part, st);
+    launch_head((const uint16_t *)lm_head->data, lm_head->dtype == DBF_BF16_T16, xs, V, H, M, logits,
+                part, st);
     launch_head_reduce(part, head_units(V), M, argmax, top2_margin, st);
     return hip_check("lm_head_argmax launch");
 }
@@ -587,6 +597,28 @@ int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const
     (void)hipGetLastError();
     launch_accept(drafts, target, K, eos, n_eos, result, committed, (hipStream_t)stream);
     return hip_check("accept_prefix launch");
+}
+
+size_t dbf_tiled_bytes(int64_t N, int64_t K) {
+    if (N < 1 || K < 1) return 0;
+    return tiled_elems(N, K) * sizeof(uint16_t);
+}
+
+int dbf_tile_weight(const dbf_tensor *src, void *dst, void *stream) {
+    g_err.clear();
+    if (!src || !src->data || !dst) return fail(DBF_EINVAL, "src, src->data and dst are required");
+    if (src->dtype != DBF_BF16) return fail(DBF_EDTYPE, "tiling takes a row-major BF16 weight");
+    if (src->ndim != 2 && src->ndim != 3) return fail(DBF_ESHAPE, "tiling takes [N, K] or [B, N, K]");
+    const int64_t B = src->ndim == 3 ? src->shape[0] : 1;
+    const int64_t N = src->shape[src->ndim - 2], K = src->shape[src->ndim - 1];
+    if (B < 1 || N < 1 || K < 8 || K % 8 || N > 0x7fffffff || K > 0x7fffffff)
+        return fail(DBF_ESHAPE, "tiling shape invalid (K must be a positive multiple of 8)");
+    const char *s0 = (const char *)src->data, *d0 = (const char *)dst;
+    const size_t sb = (size_t)B * N * K * 2, db = (size_t)B * tiled_elems(N, K) * 2;
+    if (d0 < s0 + sb && s0 < d0 + db) return fail(DBF_EINVAL, "dst overlaps src");
+    (void)hipGetLastError();
+    launch_tile((const uint16_t *)src->data, (uint16_t *)dst, B, (int)N, (int)K, (hipStream_t)stream);
+    return hip_check("dbf_tile_weight launch");
 }
 
 int kv_rollback(dbf_kv_cache *cache, int32_t n) {

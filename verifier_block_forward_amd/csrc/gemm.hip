@@ -6,6 +6,16 @@
 // 16 (or 32, with context rows) activation rows, so every projection is a weight
 // stream: bytes, not flops, set its speed.
 //
+// Weight layouts. Row-major [out, in] (as stored on disk): per 32-column k-step a
+// lane reads 16 bytes of row (l % 16) at columns 8*(l/16)..+7, i.e. 64-byte runs
+// per row per load instruction, which streams at ~4.6 TB/s on MI355X. Tiled
+// (DBF_BF16_T16, written once by dbf_tile_weight): rows in tiles of 16, each
+// (tile, k-step) block stored as the 64 lanes' 16-byte A operands back to back,
+// so every load instruction reads one contiguous 1 KiB (~6.2 TB/s, the read
+// ceiling measured with a plain streaming kernel). Element (n, k) of a tiled
+// [N, K] weight sits at ((n/16 * S + k/32) * 64 + ((k%32)/8) * 16 + n%16) * 8 + k%8,
+// S = ceil(K/32); padding rows and columns are zero.
+//
 // Mapping: a wavefront owns 16*NA consecutive weight rows and a slice of the
 // input dimension. Per k-step of 32 columns, lane l loads 16 bytes of row
 // (l % 16) at columns 8*(l/16)..+7 of each of its NA row tiles (each row gets 64
@@ -26,62 +36,57 @@ __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, ma
 
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16((a), (b), (c), 0, 0, 0)
 
-// Accumulate the NA x NB tile product over k-steps [s0, s1).
-template <int NA, int NB>
-__device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA],
-                                                const uint16_t *const xs[NB], int K, int s0,
-                                                int s1, int lane, f32x4 acc[NA][NB]) {
+// Accumulate the NA x NB tile product over k-steps [s0, s1), software-pipelined:
+// a ring of PIPE register stages holds the loads of k-steps s+1..s+PIPE while
+// step s feeds the matrix cores, so every wave keeps PIPE*(NA + 2*NB) 16-byte
+// loads in flight. Stages past s1 (or columns past K) re-read a valid address and
+// are zeroed or ignored, so the loop has no control flow around its loads.
+template <int NA, int NB, int PIPE>
+__device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], int wstep,
+                                                bool tiled, const uint16_t *const xs[NB], int K,
+                                                int s0, int s1, int lane, f32x4 acc[NA][NB]) {
     const int g = lane >> 4;
-    const int full = K >> 5;  // k-steps fully inside K
-    int s = s0;
-    const int s_end_full = s1 < full ? s1 : full;
-    // main part: two k-steps per iteration (128 contiguous bytes per weight row)
-    for (; s + 1 < s_end_full; s += 2) {
-        bf16x8 w0[NA], w1[NA], xh0[NB], xl0[NB], xh1[NB], xl1[NB];
+    bf16x8 wb[PIPE][NA], xh[PIPE][NB], xl[PIPE][NB];
+    const int n = s1 - s0;
+#define DBF_LOAD_STAGE(u, step)                                                 \
+    do {                                                                        \
+        const int sc_ = (step) < s1 ? (step) : s1 - 1;                          \
+        const bool in_ = tiled || 32 * sc_ + 8 * g < K;                         \
+        const int col_ = in_ ? wstep * sc_ : 0;                                 \
+        _Pragma("unroll") for (int a = 0; a < NA; a++) {                        \
+            const bf16x8 v_ = ld16(wrow[a] + col_);                             \
+            wb[u][a] = in_ ? v_ : zero8();                                      \
+        }                                                                       \
+        _Pragma("unroll") for (int b = 0; b < NB; b++) {                        \
+            const uint16_t *x_ = xs[b] + ((size_t)sc_ * 2 * 64 + lane) * 8;     \
+            xh[u][b] = ld16(x_);                                                \
+            xl[u][b] = ld16(x_ + 64 * 8);                                       \
+        }                                                                       \
+    } while (0)
 #pragma unroll
-        for (int a = 0; a < NA; a++) {
-            w0[a] = ld16(wrow[a] + 32 * s);
-            w1[a] = ld16(wrow[a] + 32 * s + 32);
-        }
+    for (int u = 0; u < PIPE; u++) DBF_LOAD_STAGE(u, s0 + u);
+    for (int base = 0; base < n; base += PIPE) {
 #pragma unroll
-        for (int b = 0; b < NB; b++) {
-            const uint16_t *x = xs[b] + ((size_t)s * 2 * 64 + lane) * 8;
-            xh0[b] = ld16(x);
-            xl0[b] = ld16(x + 64 * 8);
-            xh1[b] = ld16(x + 2 * 64 * 8);
-            xl1[b] = ld16(x + 3 * 64 * 8);
-        }
+        for (int u = 0; u < PIPE; u++) {
+            if (base + u < n) {
 #pragma unroll
-        for (int a = 0; a < NA; a++)
+                for (int a = 0; a < NA; a++)
 #pragma unroll
-            for (int b = 0; b < NB; b++) {
-                acc[a][b] = MFMA(w0[a], xh0[b], acc[a][b]);
-                acc[a][b] = MFMA(w0[a], xl0[b], acc[a][b]);
-                acc[a][b] = MFMA(w1[a], xh1[b], acc[a][b]);
-                acc[a][b] = MFMA(w1[a], xl1[b], acc[a][b]);
+                    for (int b = 0; b < NB; b++) {
+                        acc[a][b] = MFMA(wb[u][a], xh[u][b], acc[a][b]);
+                        acc[a][b] = MFMA(wb[u][a], xl[u][b], acc[a][b]);
+                    }
             }
-    }
-    // remaining steps one at a time; the last one may run past K (K % 32 != 0)
-    for (; s < s1; s++) {
-        const bool in = (32 * s + 8 * g) < K;
-        bf16x8 w0[NA], xh[NB], xl[NB];
-#pragma unroll
-        for (int a = 0; a < NA; a++) w0[a] = in ? ld16(wrow[a] + 32 * s) : zero8();
-#pragma unroll
-        for (int b = 0; b < NB; b++) {
-            const uint16_t *x = xs[b] + ((size_t)s * 2 * 64 + lane) * 8;
-            xh[b] = ld16(x);
-            xl[b] = ld16(x + 64 * 8);
+            DBF_LOAD_STAGE(u, s0 + base + u + PIPE);
         }
-#pragma unroll
-        for (int a = 0; a < NA; a++)
-#pragma unroll
-            for (int b = 0; b < NB; b++) {
-                acc[a][b] = MFMA(w0[a], xh[b], acc[a][b]);
-                acc[a][b] = MFMA(w0[a], xl[b], acc[a][b]);
-            }
     }
+#undef DBF_LOAD_STAGE
 }
+
+#ifndef DBF_GEMM_PIPE
+#define DBF_GEMM_PIPE 4
+#endif
+constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
 
 template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
@@ -105,11 +110,19 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     const int row0 = tile * 16 * NA;
 
     const uint16_t *wrow[NA];
+    const int wstep = sg.tiled ? 512 : 32;
 #pragma unroll
     for (int a = 0; a < NA; a++) {
-        int row = row0 + 16 * a + r;
-        if (row > N - 1) row = N - 1;  // ragged last tile: re-read a valid row, result dropped
-        wrow[a] = sg.W + (size_t)row * K + 8 * g;
+        if (sg.tiled) {
+            int t = tile * NA + a;
+            const int T = (N + 15) >> 4;
+            if (t > T - 1) t = T - 1;  // tile past the padded rows: re-read, result dropped
+            wrow[a] = sg.W + ((size_t)t * S * 64 + lane) * 8;
+        } else {
+            int row = row0 + 16 * a + r;
+            if (row > N - 1) row = N - 1;  // ragged last tile: re-read a valid row, result dropped
+            wrow[a] = sg.W + (size_t)row * K + 8 * g;
+        }
     }
     const uint16_t *xs[NB];
     xs[0] = sg.xs0;
@@ -126,11 +139,11 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
         f32x4 acc1[NA][1];
 #pragma unroll
         for (int a = 0; a < NA; a++) acc1[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        skinny_mainloop<NA, 1>(wrow, xs1, K, s0, s1, lane, acc1);
+        skinny_mainloop<NA, 1, GEMM_PIPE>(wrow, wstep, sg.tiled, xs1, K, s0, s1, lane, acc1);
 #pragma unroll
         for (int a = 0; a < NA; a++) acc[a][0] = acc1[a][0];
     } else {
-        skinny_mainloop<NA, NB>(wrow, xs, K, s0, s1, lane, acc);
+        skinny_mainloop<NA, NB, GEMM_PIPE>(wrow, wstep, sg.tiled, xs, K, s0, s1, lane, acc);
     }
 
     const int nb = NB == 1 ? 1 : sg.nb;
@@ -222,7 +235,7 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
     return o;
 }
 
-__global__ __launch_bounds__(256) void k_head(const uint16_t *__restrict__ W,
+__global__ __launch_bounds__(256) void k_head(const uint16_t *__restrict__ W, int tiled,
                                               const uint16_t *__restrict__ xs, int V, int K,
                                               int M, float *__restrict__ logits,
                                               float4 *__restrict__ part, int units) {
@@ -233,17 +246,25 @@ __global__ __launch_bounds__(256) void k_head(const uint16_t *__restrict__ W,
     const int r = lane & 15, g = lane >> 4;
     const int row0 = unit * 16 * NA;
     const uint16_t *wrow[NA];
+    const int S = (K + 31) >> 5;
 #pragma unroll
     for (int a = 0; a < NA; a++) {
-        int row = row0 + 16 * a + r;
-        if (row > V - 1) row = V - 1;
-        wrow[a] = W + (size_t)row * K + 8 * g;
+        if (tiled) {
+            int t = unit * NA + a;
+            const int T = (V + 15) >> 4;
+            if (t > T - 1) t = T - 1;
+            wrow[a] = W + ((size_t)t * S * 64 + lane) * 8;
+        } else {
+            int row = row0 + 16 * a + r;
+            if (row > V - 1) row = V - 1;
+            wrow[a] = W + (size_t)row * K + 8 * g;
+        }
     }
     const uint16_t *xsp[1] = {xs};
     f32x4 acc[NA][1];
 #pragma unroll
     for (int a = 0; a < NA; a++) acc[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    skinny_mainloop<NA, 1>(wrow, xsp, K, 0, (K + 31) >> 5, lane, acc);
+    skinny_mainloop<NA, 1, GEMM_PIPE>(wrow, tiled ? 512 : 32, tiled != 0, xsp, K, 0, S, lane, acc);
 
     // lane holds rows o = row0 + 16a + 4g + j for activation row m = r
     Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
@@ -273,11 +294,42 @@ __global__ __launch_bounds__(256) void k_head(const uint16_t *__restrict__ W,
 
 int head_units(int V) { return (V + 16 * HEAD_NA - 1) / (16 * HEAD_NA); }
 
-void launch_head(const uint16_t *W, const uint16_t *xs, int V, int K, int M, float *logits,
-                 float4 *part, hipStream_t s) {
+void launch_head(const uint16_t *W, int tiled, const uint16_t *xs, int V, int K, int M,
+                 float *logits, float4 *part, hipStream_t s) {
     const int units = head_units(V);
-    hipLaunchKernelGGL(k_head, dim3((units + 3) / 4), dim3(256), 0, s, W, xs, V, K, M, logits,
-                       part, units);
+    hipLaunchKernelGGL(k_head, dim3((units + 3) / 4), dim3(256), 0, s, W, tiled, xs, V, K, M,
+                       logits, part, units);
+}
+
+// ---------------------------------------------------------------------------
+// Tiling of a row-major BF16 weight [batch][N][K] into the MFMA-operand order
+// described at the top of this file. One wave writes one 1 KiB (tile, k-step)
+// block; padding rows/columns are written as zeros.
+__global__ __launch_bounds__(256) void k_tile(const uint16_t *__restrict__ src,
+                                              uint16_t *__restrict__ dst, int N, int K,
+                                              long long blocks_per_mat, long long total) {
+    const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= total) return;
+    const int lane = threadIdx.x & 63;
+    const int S = (K + 31) >> 5;
+    const long long mat = blk / blocks_per_mat;
+    const long long b = blk - mat * blocks_per_mat;
+    const int t = (int)(b / S), st = (int)(b - (long long)t * S);
+    const int row = t * 16 + (lane & 15), col = st * 32 + 8 * (lane >> 4);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < N && col < K) v = *(const uint4 *)(src + (size_t)mat * N * K + (size_t)row * K + col);
+    *(uint4 *)(dst + ((size_t)mat * blocks_per_mat * 64 + (size_t)b * 64 + lane) * 8) = v;
+}
+
+size_t tiled_elems(long long N, long long K) {
+    return (size_t)((N + 15) / 16) * (size_t)((K + 31) / 32) * 512;
+}
+
+void launch_tile(const uint16_t *src, uint16_t *dst, long long batch, int N, int K, hipStream_t s) {
+    const long long per = (long long)((N + 15) / 16) * ((K + 31) / 32);
+    const long long total = per * batch;
+    hipLaunchKernelGGL(k_tile, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, src, dst, N, K,
+                       per, total);
 }
 
 // one block per activation row: fold every unit's top-2 record

@@ -20,7 +20,7 @@ struct GemmSeg {
     float *out;
     const uint16_t *xs0;  // split tile 0
     const uint16_t *xs1;  // split tile 1 (nb == 2)
-    int N, K, nb, ksplit, kslice_steps, tiles, unit_begin, pad_;
+    int N, K, nb, ksplit, kslice_steps, tiles, unit_begin, tiled;  // tiled: DBF_BF16_T16 layout
 };
 
 struct GemmArgs {
@@ -41,10 +41,17 @@ void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s);
 // lm_head: logits = h W^T over V rows, with per-unit top-2 records for the
 // argmax, then a per-row reduction.
 // ---------------------------------------------------------------------------
-constexpr int HEAD_NA = 4;  // 64 vocabulary rows per wave unit
+#ifndef DBF_HEAD_NA
+#define DBF_HEAD_NA 4
+#endif
+constexpr int HEAD_NA = DBF_HEAD_NA;  // 16*HEAD_NA vocabulary rows per wave unit
 int head_units(int V);
-void launch_head(const uint16_t *W, const uint16_t *xs, int V, int K, int M, float *logits,
-                 float4 *part, hipStream_t s);
+void launch_head(const uint16_t *W, int tiled, const uint16_t *xs, int V, int K, int M,
+                 float *logits, float4 *part, hipStream_t s);
+
+// weight tiling (MFMA operand order, see gemm.hip)
+size_t tiled_elems(long long N, long long K);
+void launch_tile(const uint16_t *src, uint16_t *dst, long long batch, int N, int K, hipStream_t s);
 void launch_head_reduce(const float4 *part, int units, int M, int32_t *argmax, float *margin,
                         hipStream_t s);
 

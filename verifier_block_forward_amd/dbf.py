@@ -25,7 +25,7 @@ import torch  # noqa: E402,F401
 _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ESHAPE, EDTYPE, ERANGE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
-F32, BF16, I32 = 0, 1, 2
+F32, BF16, I32, BF16_T16 = 0, 1, 2, 3
 KIND_DFLASH, KIND_MTP = 0, 1
 FFN_DENSE, FFN_MOE = 0, 1
 MAX_M = 16
@@ -95,6 +95,10 @@ _lib.accept_prefix.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.
 _lib.accept_prefix.restype = C.c_int
 _lib.kv_rollback.argtypes = [C.POINTER(KVCache), C.c_int32]
 _lib.kv_rollback.restype = C.c_int
+_lib.dbf_tiled_bytes.argtypes = [C.c_int64, C.c_int64]
+_lib.dbf_tiled_bytes.restype = C.c_size_t
+_lib.dbf_tile_weight.argtypes = [C.POINTER(Tensor), C.c_void_p, C.c_void_p]
+_lib.dbf_tile_weight.restype = C.c_int
 _lib.dbf_last_error.restype = C.c_char_p
 _lib.dbf_abi_version.restype = C.c_int
 
@@ -142,10 +146,25 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
+class Tiled:
+    """A BF16 weight in the tiled matrix-core layout: device storage + logical shape."""
+
+    def __init__(self, data, shape):
+        self.data = data
+        self.shape = tuple(int(x) for x in shape)
+
+
 def tensor(t) -> Tensor:
-    """dbf_tensor view of a contiguous torch tensor (or an empty view for None)."""
+    """dbf_tensor view of a contiguous torch tensor or a Tiled weight (empty for None)."""
     out = Tensor()
     if t is None:
+        return out
+    if isinstance(t, Tiled):
+        out.data = t.data.data_ptr()
+        out.dtype = BF16_T16
+        out.ndim = len(t.shape)
+        for i, s in enumerate(t.shape):
+            out.shape[i] = s
         return out
     torch = _torch()
     if not t.is_contiguous():
@@ -241,6 +260,22 @@ def accept_prefix(drafts, target, result, eos=None, committed=None, stream=None)
     n_eos = 0 if eos is None else eos.numel()
     _check(_lib.accept_prefix(_ptr(drafts), _ptr(target), K, _ptr(eos), n_eos, _ptr(result),
                               _ptr(committed), _stream(stream)))
+
+
+def tiled_bytes(N: int, K: int) -> int:
+    return int(_lib.dbf_tiled_bytes(N, K))
+
+
+def tile_weight(t, stream=None) -> Tiled:
+    """Repack a row-major BF16 weight [N, K] or [B, N, K] into the tiled layout."""
+    torch = _torch()
+    B = t.shape[0] if t.dim() == 3 else 1
+    N, K = t.shape[-2], t.shape[-1]
+    nbytes = B * tiled_bytes(N, K)
+    dst = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=t.device)
+    src = tensor(t)
+    _check(_lib.dbf_tile_weight(C.byref(src), C.c_void_p(dst.data_ptr()), _stream(stream)))
+    return Tiled(dst, t.shape)
 
 
 def kv_rollback(cache: KVCache, n: int) -> None:
