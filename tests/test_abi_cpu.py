@@ -179,3 +179,20 @@ def test_head_accept_rollback_errors():
     assert kv.seq_len == 6
     dbf.kv_rollback(kv, 6)
     assert kv.seq_len == 0
+
+
+def test_workspace_sizing_every_workload_and_moe_bounds():
+    """Sizing never divides by an empty FFN (MoE configs have no dense width) and
+    MoE limits are enforced."""
+    for name in configs.CONFIGS:
+        c = dbf.make_config(configs.get(name))
+        for M, R in ((1, 0), (16, 16), (4, 3)):
+            assert dbf.draft_block_workspace_bytes(c, M, R) > 0, (name, M, R, dbf.last_error())
+    c = dbf.make_config(configs.get("c4"))
+    c.top_k = 0
+    assert dbf.draft_block_workspace_bytes(c, 1, 0) == 0
+    c.top_k = 17
+    assert dbf.draft_block_workspace_bytes(c, 1, 0) == 0
+    c = dbf.make_config(configs.get("c4"))
+    c.n_experts = 2000
+    assert dbf.draft_block_workspace_bytes(c, 1, 0) == 0

@@ -103,7 +103,7 @@ def test_block_incremental_context(orc):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_block_full_size(orc, name):
     run_case(orc, configs.get(name))
 
@@ -160,3 +160,54 @@ def test_block_mixed_layouts_bitwise():
 @pytest.mark.slow
 def test_block_c1_tiled(orc):
     run_case(orc, configs.C1, prep=Prepared(configs.C1, tiled=True))
+
+
+# ---------------------------------------------------------------------------
+# MoE FFN (MTP block with routed experts + shared expert)
+# ---------------------------------------------------------------------------
+
+def small_moe(**kw):
+    base = dict(name="small_moe", seed=31, kind="mtp", n_layers=1, hidden=256, n_q_heads=4,
+                n_kv_heads=2, head_dim=64, vocab=500, M=3, R=0, C=20, kv_dtype="f32",
+                ffn_kind="moe", n_experts=16, top_k=4, expert_intermediate=64,
+                shared_intermediate=96, has_attn_gate=True, block_input="x0")
+    base.update(kw)
+    return configs.BlockConfig(**base)
+
+
+def run_moe_case(orc, cfg, tiled=False):
+    print(f"\n[moe] {cfg.name} M={cfg.M} E={cfg.n_experts} top_k={cfg.top_k} tiled={tiled}", flush=True)
+    prep = Prepared(cfg, tiled=tiled)
+    got = prep.run()
+    want = orc.block_forward(cfg, prep.w_host, prep.in_host)
+    # the expert sets are unique only where the router's rank-k / rank-k+1 logit gap is
+    # clear of rounding; the seeded inputs are checked to have no such near-tie
+    if cfg.top_k < cfg.n_experts:
+        assert want["moe_gap"].min() > 1e-4, f"near-tie in the router: gap {want['moe_gap'].min()}"
+    gk, gv = prep.cache_host(*got["cache"])
+    s0 = cfg.C
+    worst = compare_block(cfg, got, want, s0, s0 + cfg.R + cfg.M, (gk, gv),
+                          (want["cache_k"], want["cache_v"]))
+    print(f"  worst err/tol = {worst:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("cfg", [
+    small_moe(),
+    small_moe(name="moe_m1", M=1),
+    small_moe(name="moe_top1", top_k=1, M=4),
+    small_moe(name="moe_all", n_experts=8, top_k=8, M=2),
+    small_moe(name="moe_m16", M=16, C=40),
+    small_moe(name="moe_ragged", hidden=200, expert_intermediate=40, shared_intermediate=24, M=5),
+], ids=lambda c: c.name)
+def test_block_moe_small(orc, cfg):
+    run_moe_case(orc, cfg)
+
+
+def test_block_moe_tiled(orc):
+    run_moe_case(orc, small_moe(name="moe_tiled", M=4), tiled=True)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["c4", "c4m4"])
+def test_block_moe_full_size(orc, name):
+    run_moe_case(orc, configs.get(name), tiled=True)

@@ -70,12 +70,16 @@ struct Plan {
     size_t ssp_x, ssp_x1, ssp_ctx, ssp_e, ssp_h;
     int ncb;
     size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_o, p_gate, p_up, p_down;
+    // MoE
+    int max_slots;
+    GemmPlan router, sgi, shg, eg, ed, shd;
+    size_t p_router, p_sgi, p_shg, p_shu, p_eg, p_eu, p_ed, p_shd, xs_e, xs_sh;
+    size_t moe_n, moe_slot, moe_coef, moe_sscale, moe_sel;
     size_t total;
 };
 
 Plan make_plan(const dbf_config &c, int M, int R) {
     Plan p{};
-    (void)M;
     p.H = c.hidden;
     p.qt = c.n_q_heads * c.head_dim;
     p.kt = c.n_kv_heads * c.head_dim;
@@ -90,9 +94,11 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.v = p.k;
     p.g = p.q;
     p.o = gemm_plan(p.H, p.qt, na, TARGET_UNITS);
-    p.gate = gemm_plan(p.I, p.H, na, TARGET_UNITS / 2);
-    p.up = p.gate;
-    p.down = gemm_plan(p.H, p.I, na, TARGET_UNITS);
+    if (c.ffn_kind == DBF_FFN_DENSE) {
+        p.gate = gemm_plan(p.I, p.H, na, TARGET_UNITS / 2);
+        p.up = p.gate;
+        p.down = gemm_plan(p.H, p.I, na, TARGET_UNITS);
+    }
     const int rows_kv = R > 0 ? 32 : 16;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -125,9 +131,38 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.p_v = take((size_t)p.v.ksplit * rows_kv * p.kt * f);
     p.p_g = take((size_t)p.g.ksplit * 16 * p.qt * f);
     p.p_o = take((size_t)p.o.ksplit * 16 * p.H * f);
-    p.p_gate = take((size_t)p.gate.ksplit * 16 * (p.I > 0 ? p.I : 1) * f);
-    p.p_up = take((size_t)p.up.ksplit * 16 * (p.I > 0 ? p.I : 1) * f);
-    p.p_down = take((size_t)p.down.ksplit * 16 * p.H * f);
+    if (c.ffn_kind == DBF_FFN_DENSE) {
+        p.p_gate = take((size_t)p.gate.ksplit * 16 * p.I * f);
+        p.p_up = take((size_t)p.up.ksplit * 16 * p.I * f);
+        p.p_down = take((size_t)p.down.ksplit * 16 * p.H * f);
+    }
+    if (c.ffn_kind == DBF_FFN_MOE) {
+        const int E = c.n_experts, Ie = c.expert_intermediate, Is = c.shared_intermediate;
+        p.max_slots = E < M * c.top_k ? E : M * c.top_k;  // >= 1: M >= 1, top_k >= 1
+        p.router = gemm_plan(E, p.H, na, TARGET_UNITS / 4);
+        p.sgi = gemm_plan(1, p.H, na, 64);
+        p.shg = gemm_plan(Is, p.H, na, TARGET_UNITS / 8);
+        int per_slot = TARGET_UNITS / (2 * p.max_slots);
+        p.eg = gemm_plan(Ie, p.H, na, per_slot < 1 ? 1 : per_slot);
+        per_slot = TARGET_UNITS / p.max_slots;
+        p.ed = gemm_plan(p.H, Ie, na, per_slot < 1 ? 1 : per_slot);
+        p.shd = gemm_plan(p.H, Is, na, TARGET_UNITS / 8);
+        p.p_router = take((size_t)p.router.ksplit * 16 * E * f);
+        p.p_sgi = take((size_t)p.sgi.ksplit * 16 * 1 * f);
+        p.p_shg = take((size_t)p.shg.ksplit * 16 * Is * f);
+        p.p_shu = take((size_t)p.shg.ksplit * 16 * Is * f);
+        p.p_eg = take((size_t)p.max_slots * p.eg.ksplit * 16 * Ie * f);
+        p.p_eu = take((size_t)p.max_slots * p.eg.ksplit * 16 * Ie * f);
+        p.p_ed = take((size_t)p.max_slots * p.ed.ksplit * 16 * p.H * f);
+        p.p_shd = take((size_t)p.shd.ksplit * 16 * p.H * f);
+        p.xs_e = take((size_t)p.max_slots * split_tile_bytes(Ie));
+        p.xs_sh = take(split_tile_bytes(Is));
+        p.moe_n = take(sizeof(int32_t));
+        p.moe_slot = take((size_t)p.max_slots * sizeof(int32_t));
+        p.moe_coef = take((size_t)p.max_slots * 16 * f);
+        p.moe_sscale = take(16 * f);
+        p.moe_sel = take((size_t)16 * c.top_k * sizeof(int32_t));
+    }
     p.total = off;
     return p;
 }
@@ -153,6 +188,20 @@ struct SegList {
         a.total_units += pl.tiles * pl.ksplit;
         if (s.nb > nbmax) nbmax = s.nb;
     }
+    // grouped (MoE experts): `slots` matrices selected on the device
+    void add_grouped(const dbf_tensor &t, int N, int K, const GemmPlan &pl, float *out,
+                     const uint16_t *xs0, long long xs_stride, int slots, const int32_t *slot_expert,
+                     const int32_t *nslots) {
+        add(t, N, K, pl, out, xs0);
+        GemmSeg &s = a.seg[a.nseg - 1];
+        s.slots = slots;
+        s.slot_expert = slot_expert;
+        s.nslots = nslots;
+        s.w_stride = s.tiled ? (long long)tiled_elems(N, K) : (long long)N * K;
+        s.xs_stride = xs_stride;
+        s.out_stride = (long long)pl.ksplit * 16 * N;
+        a.total_units += (slots - 1) * pl.tiles * pl.ksplit;
+    }
     void launch(hipStream_t st) { launch_gemm(a, GEMM_NA, nbmax, st); }
 };
 
@@ -177,7 +226,13 @@ int validate_config(const dbf_config *c) {
         if (c->intermediate < 8 || c->intermediate % 8)
             return fail(DBF_ESHAPE, "intermediate %d must be a positive multiple of 8", c->intermediate);
     } else if (c->ffn_kind == DBF_FFN_MOE) {
-        return fail(DBF_EINVAL, "MoE FFN not available in this build");
+        if (c->n_experts < 1 || c->n_experts > 1024)
+            return fail(DBF_EINVAL, "n_experts %d outside [1, 1024]", c->n_experts);
+        if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > DBF_MAX_TOPK)
+            return fail(DBF_EINVAL, "top_k %d outside [1, min(E, %d)]", c->top_k, DBF_MAX_TOPK);
+        if (c->expert_intermediate < 8 || c->expert_intermediate % 8 || c->shared_intermediate < 8 ||
+            c->shared_intermediate % 8)
+            return fail(DBF_ESHAPE, "expert/shared intermediate sizes must be positive multiples of 8");
     } else {
         return fail(DBF_EINVAL, "ffn_kind %d unknown", c->ffn_kind);
     }
@@ -224,6 +279,16 @@ int validate_weights(const dbf_config &c, const dbf_weights *w, bool need_embed)
             T(ffn_gate, DBF_BF16, 2, c.intermediate, H);
             T(ffn_up, DBF_BF16, 2, c.intermediate, H);
             T(ffn_down, DBF_BF16, 2, H, c.intermediate);
+        } else {
+            const int E = c.n_experts, Ie = c.expert_intermediate, Is = c.shared_intermediate;
+            T(router, DBF_BF16, 2, E, H);
+            T(exp_gate, DBF_BF16, 3, E, Ie, H);
+            T(exp_up, DBF_BF16, 3, E, Ie, H);
+            T(exp_down, DBF_BF16, 3, E, H, Ie);
+            T(sh_gate, DBF_BF16, 2, Is, H);
+            T(sh_up, DBF_BF16, 2, Is, H);
+            T(sh_down, DBF_BF16, 2, H, Is);
+            T(sh_gate_inp, DBF_BF16, 2, 1, H);
         }
 #undef T
     }
@@ -252,6 +317,7 @@ const char *dbf_last_error(void) { return g_err.c_str(); }
 size_t draft_block_workspace_bytes(const dbf_config *cfg, int32_t M, int32_t R) {
     if (validate_config(cfg) != DBF_OK) return 0;
     if (M < 1 || M > DBF_MAX_M || R < 0 || R > DBF_MAX_R) return 0;
+    if (cfg->kind == DBF_KIND_MTP) R = 0;
     return make_plan(*cfg, M, R).total;
 }
 
@@ -501,44 +567,141 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             a.ssp_out = ssp_x1;
             launch_colsum(a, st);
         }
-        {
-            SegList sl;
-            sl.add(L.ffn_gate, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
-            sl.add(L.ffn_up, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
-            sl.launch(st);
-            SwigluArgs sa{};
-            sa.pg = at<float>(ws, p.p_gate);
-            sa.pu = at<float>(ws, p.p_up);
-            sa.ksg = p.gate.ksplit;
-            sa.ksu = p.up.ksplit;
-            sa.ssp = ssp_x1;
-            sa.ncb = ncb;
-            sa.H = H;
-            sa.eps = eps;
-            sa.M = M;
-            sa.I = p.I;
-            sa.xs = xs_ff;
-            launch_swiglu(sa, st);
-            SegList sd;
-            sd.add(L.ffn_down, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
-            sd.launch(st);
+        if (c.ffn_kind == DBF_FFN_DENSE) {
+            {
+                SegList sl;
+                sl.add(L.ffn_gate, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
+                sl.add(L.ffn_up, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
+                sl.launch(st);
+                SwigluArgs sa{};
+                sa.pg = at<float>(ws, p.p_gate);
+                sa.pu = at<float>(ws, p.p_up);
+                sa.ksg = p.gate.ksplit;
+                sa.ksu = p.up.ksplit;
+                sa.ssp = ssp_x1;
+                sa.ncb = ncb;
+                sa.H = H;
+                sa.eps = eps;
+                sa.M = M;
+                sa.I = p.I;
+                sa.xs = xs_ff;
+                launch_swiglu(sa, st);
+                SegList sd;
+                sd.add(L.ffn_down, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
+                sd.launch(st);
+            }
+        } else {
+            // MoE: router + shared-expert projections, routing, grouped experts, combine
+            const int E = c.n_experts, Ie = c.expert_intermediate, Is = c.shared_intermediate;
+            int32_t *nsl = at<int32_t>(ws, p.moe_n), *slot_e = at<int32_t>(ws, p.moe_slot);
+            float *coef = at<float>(ws, p.moe_coef), *sscale = at<float>(ws, p.moe_sscale);
+            {
+                SegList sl;
+                sl.add(L.router, E, H, p.router, at<float>(ws, p.p_router), xs_blk);
+                sl.add(L.sh_gate_inp, 1, H, p.sgi, at<float>(ws, p.p_sgi), xs_blk);
+                sl.add(L.sh_gate, Is, H, p.shg, at<float>(ws, p.p_shg), xs_blk);
+                sl.add(L.sh_up, Is, H, p.shg, at<float>(ws, p.p_shu), xs_blk);
+                sl.launch(st);
+            }
+            {
+                MoeRouteArgs ra{};
+                ra.p_router = at<float>(ws, p.p_router);
+                ra.ks_router = p.router.ksplit;
+                ra.p_sgi = at<float>(ws, p.p_sgi);
+                ra.ks_sgi = p.sgi.ksplit;
+                ra.ssp = ssp_x1;
+                ra.ncb = ncb;
+                ra.H = H;
+                ra.eps = eps;
+                ra.M = M;
+                ra.E = E;
+                ra.top_k = c.top_k;
+                ra.max_slots = p.max_slots;
+                ra.nslots = nsl;
+                ra.slot_expert = slot_e;
+                ra.coef = coef;
+                ra.shared_scale = sscale;
+                ra.sel = at<int32_t>(ws, p.moe_sel);
+                launch_moe_route(ra, st);
+            }
+            {
+                SegList sl;
+                sl.add_grouped(L.exp_gate, Ie, H, p.eg, at<float>(ws, p.p_eg), xs_blk, 0, p.max_slots,
+                               slot_e, nsl);
+                sl.add_grouped(L.exp_up, Ie, H, p.eg, at<float>(ws, p.p_eu), xs_blk, 0, p.max_slots,
+                               slot_e, nsl);
+                sl.launch(st);
+            }
+            {
+                MoeSwigluArgs sa{};
+                sa.pg = at<float>(ws, p.p_eg);
+                sa.pu = at<float>(ws, p.p_eu);
+                sa.ks = p.eg.ksplit;
+                sa.psg = at<float>(ws, p.p_shg);
+                sa.psu = at<float>(ws, p.p_shu);
+                sa.ks_sh = p.shg.ksplit;
+                sa.ssp = ssp_x1;
+                sa.ncb = ncb;
+                sa.H = H;
+                sa.eps = eps;
+                sa.M = M;
+                sa.Ie = Ie;
+                sa.Is = Is;
+                sa.max_slots = p.max_slots;
+                sa.nslots = nsl;
+                sa.xs_e = at<uint16_t>(ws, p.xs_e);
+                sa.xs_sh = at<uint16_t>(ws, p.xs_sh);
+                launch_moe_swiglu(sa, st);
+            }
+            {
+                SegList sl;
+                sl.add_grouped(L.exp_down, H, Ie, p.ed, at<float>(ws, p.p_ed), at<uint16_t>(ws, p.xs_e),
+                               (long long)(split_tile_bytes(Ie) / 2), p.max_slots, slot_e, nsl);
+                sl.add(L.sh_down, H, Is, p.shd, at<float>(ws, p.p_shd), at<uint16_t>(ws, p.xs_sh));
+                sl.launch(st);
+            }
         }
         {
             // x = x1 + FFN; split(x (.) next in_norm), or the final norm after the last layer
-            ColArgs a = col();
-            a.M = M;
-            a.base = x1;
-            a.ldb = H;
-            a.p0 = at<float>(ws, p.p_down);
-            a.ks0 = p.down.ksplit;
-            a.rows0 = 16;
-            a.out = xres;
-            a.copy0 = io->layer_hidden ? io->layer_hidden + (size_t)l * M * H : nullptr;
-            a.copy1 = last ? io->hidden_out : nullptr;
-            a.w = last ? nullptr : (const float *)Ls[l + 1].in_norm.data;
-            a.xs = last ? nullptr : xs_blk;
-            a.ssp_out = ssp_x;
-            launch_colsum(a, st);
+            float *lh = io->layer_hidden ? io->layer_hidden + (size_t)l * M * H : nullptr;
+            const float *wn = last ? nullptr : (const float *)Ls[l + 1].in_norm.data;
+            if (c.ffn_kind == DBF_FFN_DENSE) {
+                ColArgs a = col();
+                a.M = M;
+                a.base = x1;
+                a.ldb = H;
+                a.p0 = at<float>(ws, p.p_down);
+                a.ks0 = p.down.ksplit;
+                a.rows0 = 16;
+                a.out = xres;
+                a.copy0 = lh;
+                a.copy1 = last ? io->hidden_out : nullptr;
+                a.w = wn;
+                a.xs = last ? nullptr : xs_blk;
+                a.ssp_out = ssp_x;
+                launch_colsum(a, st);
+            } else {
+                MoeCombineArgs a{};
+                a.base = x1;
+                a.pd = at<float>(ws, p.p_ed);
+                a.ks = p.ed.ksplit;
+                a.psd = at<float>(ws, p.p_shd);
+                a.ks_sh = p.shd.ksplit;
+                a.nslots = at<int32_t>(ws, p.moe_n);
+                a.coef = at<float>(ws, p.moe_coef);
+                a.shared_scale = at<float>(ws, p.moe_sscale);
+                a.M = M;
+                a.H = H;
+                a.max_slots = p.max_slots;
+                a.out = xres;
+                a.copy0 = lh;
+                a.copy1 = last ? io->hidden_out : nullptr;
+                a.w = wn;
+                a.xs = last ? nullptr : xs_blk;
+                a.ssp_out = ssp_x;
+                a.ncb = ncb;
+                launch_moe_combine(a, st);
+            }
             if (last)
                 launch_final_norm(xres, ssp_x, M, H, (const float *)w->final_norm.data, eps,
                                   io->h_final, st);

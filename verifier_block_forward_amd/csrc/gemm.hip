@@ -98,7 +98,19 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     for (int i = 1; i < args.nseg; i++)
         if (unit >= args.seg[i].unit_begin) si = i;
     const GemmSeg &sg = args.seg[si];
-    const int local = unit - sg.unit_begin;
+    int local = unit - sg.unit_begin;
+    const uint16_t *Wbase = sg.W;
+    const uint16_t *xsb0 = sg.xs0;
+    float *outb = sg.out;
+    if (sg.slots > 0) {  // grouped: this unit's matrix is the slot's expert
+        const int per = sg.tiles * sg.ksplit;
+        const int slot = local / per;
+        if (slot >= *sg.nslots) return;
+        local -= slot * per;
+        Wbase += (size_t)sg.slot_expert[slot] * (size_t)sg.w_stride;
+        xsb0 += (size_t)slot * (size_t)sg.xs_stride;
+        outb += (size_t)slot * (size_t)sg.out_stride;
+    }
     const int tile = local % sg.tiles;
     const int ks = local / sg.tiles;
     const int N = sg.N, K = sg.K;
@@ -117,16 +129,16 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
             int t = tile * NA + a;
             const int T = (N + 15) >> 4;
             if (t > T - 1) t = T - 1;  // tile past the padded rows: re-read, result dropped
-            wrow[a] = sg.W + ((size_t)t * S * 64 + lane) * 8;
+            wrow[a] = Wbase + ((size_t)t * S * 64 + lane) * 8;
         } else {
             int row = row0 + 16 * a + r;
             if (row > N - 1) row = N - 1;  // ragged last tile: re-read a valid row, result dropped
-            wrow[a] = sg.W + (size_t)row * K + 8 * g;
+            wrow[a] = Wbase + (size_t)row * K + 8 * g;
         }
     }
     const uint16_t *xs[NB];
-    xs[0] = sg.xs0;
-    if (NB > 1) xs[NB - 1] = sg.nb > 1 ? sg.xs1 : sg.xs0;
+    xs[0] = xsb0;
+    if (NB > 1) xs[NB - 1] = sg.nb > 1 ? sg.xs1 : xsb0;
 
     f32x4 acc[NA][NB];
 #pragma unroll
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
         for (int b = 0; b < NB; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (NB == 2 && sg.nb == 1) {
-        const uint16_t *xs1[1] = {sg.xs0};
+        const uint16_t *xs1[1] = {xsb0};
         f32x4 acc1[NA][1];
 #pragma unroll
         for (int a = 0; a < NA; a++) acc1[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     }
 
     const int nb = NB == 1 ? 1 : sg.nb;
-    float *out = sg.out + (size_t)ks * 16 * nb * N;
+    float *out = outb + (size_t)ks * 16 * nb * N;
 #pragma unroll
     for (int a = 0; a < NA; a++)
 #pragma unroll
@@ -163,7 +175,8 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
 }
 
 GemmPlan gemm_plan(int N, int K, int na, int target_units) {
-    GemmPlan p;
+    GemmPlan p{0, 0, 0};
+    if (N < 1 || K < 1 || na < 1) return p;  // empty projection: no units
     p.tiles = (N + 16 * na - 1) / (16 * na);
     const int S = (K + 31) / 32;
     int ks = (target_units + p.tiles - 1) / p.tiles;

@@ -21,6 +21,13 @@ struct GemmSeg {
     const uint16_t *xs0;  // split tile 0
     const uint16_t *xs1;  // split tile 1 (nb == 2)
     int N, K, nb, ksplit, kslice_steps, tiles, unit_begin, tiled;  // tiled: DBF_BF16_T16 layout
+    // grouped (MoE) segments: `slots` independent matrices W + slot_expert[s] * w_stride,
+    // each with its own split tile xs0 + s * xs_stride and output out + s * out_stride;
+    // slots >= *nslots (known only on the device) exit at once. slots == 0: plain.
+    const int32_t *slot_expert;
+    const int32_t *nslots;
+    long long w_stride, xs_stride, out_stride;
+    int slots, pad_;
 };
 
 struct GemmArgs {
@@ -145,5 +152,58 @@ void launch_attn_combine(const CombineArgs &a, hipStream_t s);
 
 void launch_accept(const int32_t *drafts, const int32_t *target, int K, const int32_t *eos,
                    int n_eos, int32_t *result, int32_t *committed, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// MoE FFN (moe.hip)
+// ---------------------------------------------------------------------------
+struct MoeRouteArgs {
+    const float *p_router;  // [ks][16][E] router partials (unscaled by the row norm)
+    int ks_router;
+    const float *p_sgi;     // [ks][16][1] shared-expert gate-input partials
+    int ks_sgi;
+    const float *ssp;       // FFN input rows' norm partials [16][ncb]
+    int ncb, H;
+    float eps;
+    int M, E, top_k, max_slots;
+    int32_t *nslots;        // out: number of distinct experts touched
+    int32_t *slot_expert;   // out: [max_slots] expert ids, ascending
+    float *coef;            // out: [max_slots][16] routing weight of each row (0: not routed)
+    float *shared_scale;    // out: [16] sigmoid(x . w_sg) per row
+    int32_t *sel;           // out: [16][top_k] selected experts per row (descending weight)
+};
+void launch_moe_route(const MoeRouteArgs &a, hipStream_t s);
+
+struct MoeSwigluArgs {
+    const float *pg, *pu;   // expert partials [slot][ks][16][Ie]
+    int ks;
+    const float *psg, *psu; // shared-expert partials [ks_sh][16][Is]
+    int ks_sh;
+    const float *ssp;
+    int ncb, H;
+    float eps;
+    int M, Ie, Is, max_slots;
+    const int32_t *nslots;
+    uint16_t *xs_e;         // [max_slots] split tiles (K = Ie)
+    uint16_t *xs_sh;        // split tile (K = Is)
+};
+void launch_moe_swiglu(const MoeSwigluArgs &a, hipStream_t s);
+
+struct MoeCombineArgs {
+    const float *base;      // x1 [M][H]
+    const float *pd;        // expert down partials [slot][ks][16][H]
+    int ks;
+    const float *psd;       // shared down partials [ks_sh][16][H]
+    int ks_sh;
+    const int32_t *nslots;
+    const float *coef;      // [max_slots][16]
+    const float *shared_scale;
+    int M, H, max_slots;
+    float *out, *copy0, *copy1;
+    const float *w;         // next norm weight or null
+    uint16_t *xs;           // split tile or null
+    float *ssp_out;
+    int ncb;
+};
+void launch_moe_combine(const MoeCombineArgs &a, hipStream_t s);
 
 }  // namespace dbf
