@@ -465,6 +465,10 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         const int qt = attn_qtiles(hd, nq_group);
         attn_plan(P0 + R + M, nq_group < 16 * qt ? nq_group : 16 * qt, &chunk, &n_chunks);
     }
+    // RoPE inverse frequencies theta^(-2j/rotary_dim), in F64, shared by every layer
+    double inv_freq[ROPE_MAX_PAIRS];
+    for (int j = 0; j < p.rd / 2 && j < ROPE_MAX_PAIRS; j++)
+        inv_freq[j] = pow(c.rope_theta, -2.0 * (double)j / (double)p.rd);
     const size_t elt = cache->dtype == DBF_BF16 ? 2 : 4;
     const size_t layer_stride = (size_t)c.n_kv_heads * cache->capacity * hd * elt;
 
@@ -507,7 +511,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             qa.q_norm = (const float *)L.q_norm.data;
             qa.k_norm = (const float *)L.k_norm.data;
             qa.eps = eps;
-            qa.theta = c.rope_theta;
+            memcpy(qa.inv_freq, inv_freq, sizeof(double) * (size_t)(p.rd / 2));
             qa.rotary_dim = p.rd;
             qa.M = M;
             qa.R = R;
@@ -714,7 +718,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
 
 size_t lm_head_argmax_workspace_bytes(int32_t M, int32_t H, int32_t V) {
     if (M < 1 || M > DBF_MAX_M || H < 8 || V < 1) return 0;
-    return align256(split_tile_bytes(H)) + align256((size_t)head_units(V) * 16 * sizeof(float4));
+    return align256((size_t)head_blocks(V) * 16 * sizeof(float4));
 }
 
 int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, int32_t *argmax,
@@ -736,18 +740,10 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
     if (ws_bytes < need) return fail(DBF_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();
-    uint16_t *xs = (uint16_t *)ws;
-    float4 *part = at<float4>(ws, align256(split_tile_bytes(H)));
-    ColArgs a{};
-    a.M = M;
-    a.H = H;
-    a.base = h;
-    a.ldb = H;
-    a.xs = xs;
-    launch_colsum(a, st);
-    launch_head((const uint16_t *)lm_head->data, lm_head->dtype == DBF_BF16_T16, xs, V, H, M, logits,
+    float4 *part = (float4 *)ws;
+    launch_head((const uint16_t *)lm_head->data, lm_head->dtype == DBF_BF16_T16, h, V, H, M, logits,
                 part, st);
-    launch_head_reduce(part, head_units(V), M, argmax, top2_margin, st);
+    launch_head_reduce(part, head_blocks(V), M, argmax, top2_margin, st);
     return hip_check("lm_head_argmax launch");
 }
 

@@ -60,6 +60,86 @@ struct AttnLds {
     static constexpr int BYTES = LOOP > MERGE ? LOOP : MERGE;
 };
 
+// Raw K/V rows of one 16-key sub-tile as a lane loads them: lane (r16, g) holds key
+// row r16, dims 32*st + 8g .. +7 of every 32-dim step st.
+template <int HD, bool KVB>
+struct KvRaw;
+template <int HD>
+struct KvRaw<HD, false> {
+    float4 k[HD / 16], v[HD / 16];
+};
+template <int HD>
+struct KvRaw<HD, true> {
+    uint4 k[HD / 32], v[HD / 32];
+};
+
+// Sub-tiles held in registers ahead of use: every wave issues its first PF
+// sub-tiles' loads before anything else, then refills a slot as soon as it has
+// been converted. Two slots only where they fit the register budget of two
+// workgroups per CU (BF16 caches up to 128 dims).
+template <int HD, bool KVB>
+constexpr int attn_prefetch() {
+    return (KVB && HD <= 128) ? 2 : 1;
+}
+
+template <int HD, bool KVB>
+__device__ __forceinline__ void attn_load(KvRaw<HD, KVB> &r, const AttnArgs &a, size_t head_off,
+                                          long long krow, int g) {
+#pragma unroll
+    for (int st = 0; st < HD / 32; st++) {
+        const size_t off = head_off + (size_t)krow * HD + 32 * st + 8 * g;
+        if constexpr (KVB) {
+            r.k[st] = *(const uint4 *)((const uint16_t *)a.cache_k + off);
+            r.v[st] = *(const uint4 *)((const uint16_t *)a.cache_v + off);
+        } else {
+            const float4 *kp = (const float4 *)((const float *)a.cache_k + off);
+            const float4 *vp = (const float4 *)((const float *)a.cache_v + off);
+            r.k[2 * st] = kp[0];
+            r.k[2 * st + 1] = kp[1];
+            r.v[2 * st] = vp[0];
+            r.v[2 * st + 1] = vp[1];
+        }
+    }
+}
+
+// K rows -> MFMA A operands (split hi/lo for F32), V rows -> this wave's V^T planes.
+template <int HD, bool KVB, int VTW>
+__device__ __forceinline__ void attn_convert(const KvRaw<HD, KVB> &r, bf16x8 *kh, bf16x8 *kl,
+                                             uint16_t *vth, uint16_t *vtl, int g, int r16) {
+#pragma unroll
+    for (int st = 0; st < HD / 32; st++) {
+        const int d0 = 32 * st + 8 * g;
+        if constexpr (KVB) {
+            kh[st] = __builtin_bit_cast(bf16x8, r.k[st]);
+            const uint32_t w4[4] = {r.v[st].x, r.v[st].y, r.v[st].z, r.v[st].w};
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                vth[(d0 + j) * VTW + r16] = (uint16_t)((j & 1) ? (w4[j >> 1] >> 16) : (w4[j >> 1] & 0xffffu));
+        } else {
+            const float4 k0 = r.k[2 * st], k1 = r.k[2 * st + 1];
+            const float4 v0 = r.v[2 * st], v1 = r.v[2 * st + 1];
+            const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            split8(kf, kh[st], kl[st]);
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint16_t hb = f32_to_bf16(vf[j]);
+                vth[(d0 + j) * VTW + r16] = hb;
+                vtl[(d0 + j) * VTW + r16] = f32_to_bf16(vf[j] - bf16_to_f32(hb));
+            }
+        }
+    }
+}
+
+// Order this wave's LDS writes before its following reads (and reads before later
+// writes). A wavefront's LDS instructions execute in issue order, so only the
+// compiler has to be kept from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // One workgroup (4 waves) per (key chunk, kv head, group of up to 16*QT queries);
 // wave w takes the w-th quarter of the chunk and the four online-softmax states are
 // merged through LDS at the end, so the chunk writes a single (acc, m, l) partial.
@@ -67,13 +147,19 @@ struct AttnLds {
 // A = 16 keys x 32 dims straight from the cache rows, B = pre-scaled queries split
 // hi/lo in LDS). That accumulator layout (lane: keys 4g..4g+3 of query l%16) is the
 // B operand of v_mfma_f32_16x16x16_bf16 for O^T[d][q] += V^T[d][key] P^T[key][q],
-// so the probabilities never leave their lanes; V is transposed through LDS.
-// F32 caches are split hi/lo (three products: hh, hl, lh); BF16 caches are exact
-// (two products: h*K, l*K).
+// so the probabilities never leave their lanes; V is transposed through a V^T plane
+// private to the wave, so the key loop has no workgroup barrier. F32 caches are
+// split hi/lo (three products: hh, hl, lh); BF16 caches are exact (two products:
+// h*K, l*K). The K/V loads of the first sub-tiles are issued before the queries
+// are staged, so their latency overlaps the staging.
+#ifndef DBF_ATT_WPE
+#define DBF_ATT_WPE 2
+#endif
 template <int HD, int QT, bool KVB>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE))) void k_attn(AttnArgs a) {
     using L = AttnLds<HD, QT, KVB>;
     constexpr int S = L::S, DT = L::DT, VTW = L::VTW;
+    constexpr int PF = attn_prefetch<HD, KVB>();
     __shared__ __align__(16) unsigned char smem[L::BYTES];
     uint4 *qsm = (uint4 *)smem;
 
@@ -91,7 +177,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const long long c_hi = (long long)(c + 1) * a.chunk < n_all ? (long long)(c + 1) * a.chunk : n_all;
     const long long k_lo = (long long)c * a.chunk + (long long)w * pw;
     const long long k_hi = k_lo + pw < c_hi ? k_lo + pw : c_hi;  // may be <= k_lo: wave idle
+    const int n_sub = k_hi > k_lo ? (int)((k_hi - k_lo + ATT_KT - 1) / ATT_KT) : 0;
     const float scale = 1.0f / sqrtf((float)HD);
+    const size_t head_off = (size_t)kvh * a.capacity * HD;
+
+    KvRaw<HD, KVB> rb[PF];
+#pragma unroll
+    for (int u = 0; u < PF; u++) {
+        if (u < n_sub) {
+            long long krow = k_lo + (long long)u * ATT_KT + r16;  // clamped to a valid row
+            if (krow > n_all - 1) krow = n_all - 1;
+            attn_load<HD, KVB>(rb[u], a, head_off, krow, g);
+        }
+    }
 
     int qm[QT];
     bool qv[QT];
@@ -126,105 +224,87 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DT; d++) acc[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const size_t head_off = (size_t)kvh * a.capacity * HD;
-    const int n_sub = pw / ATT_KT;  // same trip count in every wave (block barriers)
+    __syncthreads();  // queries staged
 
-    for (int it = 0; it < n_sub; it++) {
-        const long long kb = k_lo + (long long)it * ATT_KT;
-        long long krow = kb + r16;  // this lane's key row, clamped to a valid row
-        if (krow > n_all - 1) krow = n_all - 1;
-        bf16x8 kh[S], kl[S];
-        __syncthreads();  // Q written / previous sub-tile's V^T reads done
+    for (int base = 0; base < n_sub; base += PF) {
 #pragma unroll
-        for (int st = 0; st < S; st++) {
-            const int d0 = 32 * st + 8 * g;
-            const size_t off = head_off + (size_t)krow * HD + d0;
-            if (KVB) {
-                kh[st] = __builtin_bit_cast(bf16x8, *(const uint4 *)((const uint16_t *)a.cache_k + off));
-                const uint4 vraw = *(const uint4 *)((const uint16_t *)a.cache_v + off);
-                const uint16_t *vv = (const uint16_t *)&vraw;
-#pragma unroll
-                for (int j = 0; j < 8; j++) vth[(d0 + j) * VTW + r16] = vv[j];
-            } else {
-                const float4 *kp = (const float4 *)((const float *)a.cache_k + off);
-                const float4 *vp = (const float4 *)((const float *)a.cache_v + off);
-                const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-                const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-                const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                split8(kf, kh[st], kl[st]);
-                // V^T planes, converted element by element through scalars
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const uint16_t hb = f32_to_bf16(vf[j]);
-                    vth[(d0 + j) * VTW + r16] = hb;
-                    vtl[(d0 + j) * VTW + r16] = f32_to_bf16(vf[j] - bf16_to_f32(hb));
-                }
+        for (int u = 0; u < PF; u++) {
+            const int it = base + u;
+            if (it >= n_sub) break;
+            const long long kb = k_lo + (long long)it * ATT_KT;
+            bf16x8 kh[S], kl[S];
+            attn_convert<HD, KVB, VTW>(rb[u], kh, kl, vth, vtl, g, r16);
+            if (it + PF < n_sub) {
+                long long krow = kb + (long long)PF * ATT_KT + r16;
+                if (krow > n_all - 1) krow = n_all - 1;
+                attn_load<HD, KVB>(rb[u], a, head_off, krow, g);
             }
-        }
-        f32x4 sc[QT];
-#pragma unroll
-        for (int t = 0; t < QT; t++) {
-            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < S; st++) {
-                const bf16x8 qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
-                const bf16x8 ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
-                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], qh, sc[t], 0, 0, 0);
-                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], ql, sc[t], 0, 0, 0);
-                if (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[st], qh, sc[t], 0, 0, 0);
-            }
-        }
-        s16x4 ph[QT], pl[QT];
-        float alpha[QT];
-#pragma unroll
-        for (int t = 0; t < QT; t++) {
-            const long long lim = a.n_ctx + qm[t];  // last key visible to this query
-            float v[4];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const long long kp = kb + 4 * g + i;
-                v[i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
-                mx = fmaxf(mx, v[i]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[t], mx);
-            float al = 1.f, ps = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float p = m_new == -INFINITY ? 0.f : expf(v[i] - m_new);
-                ps += p;
-                const __bf16 h = (__bf16)p;
-                ph[t][i] = __builtin_bit_cast(short, h);
-                pl[t][i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
-            }
-            if (m_new != -INFINITY) al = expf(m_run[t] - m_new);
-            ps += __shfl_xor(ps, 16, 64);
-            ps += __shfl_xor(ps, 32, 64);
-            l_run[t] = l_run[t] * al + ps;
-            m_run[t] = m_new;
-            alpha[t] = al;
-        }
-        __syncthreads();  // V^T of this sub-tile is in LDS
-#pragma unroll
-        for (int d = 0; d < DT; d++) {
-            const int row = (16 * d + r16) * VTW + 4 * g;
-            const uint32_t *vr = (const uint32_t *)(vth + row);
-            const s16x4 vh = __builtin_bit_cast(s16x4, make_uint2(vr[0], vr[1]));
-            s16x4 vl;
-            if (!KVB) {
-                const uint32_t *vq = (const uint32_t *)(vtl + row);
-                vl = __builtin_bit_cast(s16x4, make_uint2(vq[0], vq[1]));
-            }
+            f32x4 sc[QT];
 #pragma unroll
             for (int t = 0; t < QT; t++) {
-                f32x4 o = acc[t][d] * alpha[t];
-                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, ph[t], o, 0, 0, 0);
-                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, pl[t], o, 0, 0, 0);
-                if (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vl, ph[t], o, 0, 0, 0);
-                acc[t][d] = o;
+                sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < S; st++) {
+                    const bf16x8 qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
+                    const bf16x8 ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
+                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], qh, sc[t], 0, 0, 0);
+                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], ql, sc[t], 0, 0, 0);
+                    if (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[st], qh, sc[t], 0, 0, 0);
+                }
             }
+            s16x4 ph[QT], pl[QT];
+            float alpha[QT];
+#pragma unroll
+            for (int t = 0; t < QT; t++) {
+                const long long lim = a.n_ctx + qm[t];  // last key visible to this query
+                float v[4];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const long long kp = kb + 4 * g + i;
+                    v[i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
+                    mx = fmaxf(mx, v[i]);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float m_new = fmaxf(m_run[t], mx);
+                float al = 1.f, ps = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float p = m_new == -INFINITY ? 0.f : expf(v[i] - m_new);
+                    ps += p;
+                    const __bf16 h = (__bf16)p;
+                    ph[t][i] = __builtin_bit_cast(short, h);
+                    pl[t][i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
+                }
+                if (m_new != -INFINITY) al = expf(m_run[t] - m_new);
+                ps += __shfl_xor(ps, 16, 64);
+                ps += __shfl_xor(ps, 32, 64);
+                l_run[t] = l_run[t] * al + ps;
+                m_run[t] = m_new;
+                alpha[t] = al;
+            }
+            wave_lds_sync();  // V^T of this sub-tile written by every lane
+#pragma unroll
+            for (int d = 0; d < DT; d++) {
+                const int row = (16 * d + r16) * VTW + 4 * g;
+                const uint32_t *vr = (const uint32_t *)(vth + row);
+                const s16x4 vh = __builtin_bit_cast(s16x4, make_uint2(vr[0], vr[1]));
+                s16x4 vl;
+                if (!KVB) {
+                    const uint32_t *vq = (const uint32_t *)(vtl + row);
+                    vl = __builtin_bit_cast(s16x4, make_uint2(vq[0], vq[1]));
+                }
+#pragma unroll
+                for (int t = 0; t < QT; t++) {
+                    f32x4 o = acc[t][d] * alpha[t];
+                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, ph[t], o, 0, 0, 0);
+                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, pl[t], o, 0, 0, 0);
+                    if (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vl, ph[t], o, 0, 0, 0);
+                    acc[t][d] = o;
+                }
+            }
+            wave_lds_sync();  // V^T reads done before the next sub-tile overwrites it
         }
     }
 
@@ -308,62 +388,78 @@ void launch_attn(const AttnArgs &a, hipStream_t s) {
 }
 
 // Merge the chunk partials of query (m, h), apply the optional sigmoid gate and
-// write the attention output row into the split tile of the O projection. The
-// chunk weights exp(m_c - max) are formed once per query in LDS; the weighted sums
-// then read all chunks with independent loads. Rows m >= M and the padding columns
-// are written as zeros.
+// write the attention output row into the split tile of the O projection. Thread t
+// takes dim t % hd of the chunks congruent to t / hd modulo 256 / hd; it reads them
+// in batches of CMB_BATCH records with every load of a batch in flight at once and
+// folds each batch into a running (max, sum, acc) state; the chunk groups are then
+// merged through LDS in a fixed order. Rows m >= M and the padding columns are
+// written as zeros.
+constexpr int CMB_BATCH = 16;
+
 __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
-    __shared__ float wgt[ATT_CHUNKS_MAX];
-    __shared__ float red[8];
+    __shared__ float sm_m[256], sm_l[256], sm_o[256];
     const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int hd = a.hd, K = a.nq * hd, rec = hd + ATT_PART_EXTRA;
+    const int ngrp = 256 / hd;
+    const int d = tid % hd, grp = tid / hd;
     const bool valid = m < a.M;
-    float lsum = 0.f;
+    float mr = -INFINITY, lr = 0.f, orun = 0.f;
     if (valid) {
-        const size_t q = (size_t)m * a.nq + h;
         const size_t stride = (size_t)a.M * a.nq * rec;
-        float mc = -INFINITY, lc = 0.f;
-        if (tid < a.n_chunks) {
-            const float *p = a.part + tid * stride + q * rec;
-            mc = p[hd];
-            lc = p[hd + 1];
-            if (!(lc > 0.f)) mc = -INFINITY;
-        }
-        float mx = wave_max(mc);
-        if ((tid & 63) == 0) red[tid >> 6] = mx;
-        __syncthreads();
-        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        const float e = (tid < a.n_chunks && lc > 0.f) ? expf(mc - mx) : 0.f;
-        if (tid < ATT_CHUNKS_MAX) wgt[tid] = e;
-        float ls = wave_sum(lc * e);
-        __syncthreads();
-        if ((tid & 63) == 0) red[4 + (tid >> 6)] = ls;
-        __syncthreads();
-        lsum = (red[4] + red[5]) + (red[6] + red[7]);
-    }
-    for (int d = tid; d < hd; d += blockDim.x) {
-        float o = 0.f;
-        if (valid) {
-            const size_t q = (size_t)m * a.nq + h;
-            const size_t stride = (size_t)a.M * a.nq * rec;
-            const float *p = a.part + q * rec + d;
-            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-            int c = 0;
-            for (; c + 3 < a.n_chunks; c += 4) {
-                s0 += p[(c + 0) * stride] * wgt[c + 0];
-                s1 += p[(c + 1) * stride] * wgt[c + 1];
-                s2 += p[(c + 2) * stride] * wgt[c + 2];
-                s3 += p[(c + 3) * stride] * wgt[c + 3];
+        const float *p = a.part + ((size_t)m * a.nq + h) * rec;
+        for (int c0 = grp; c0 < a.n_chunks; c0 += CMB_BATCH * ngrp) {
+            float mv[CMB_BATCH], lv[CMB_BATCH], ov[CMB_BATCH];
+#pragma unroll
+            for (int j = 0; j < CMB_BATCH; j++) {
+                const int cc = c0 + j * ngrp;
+                const float *pc = p + (size_t)(cc < a.n_chunks ? cc : c0) * stride;
+                mv[j] = pc[hd];
+                lv[j] = cc < a.n_chunks ? pc[hd + 1] : 0.f;
+                ov[j] = pc[d];
             }
-            for (; c < a.n_chunks; c++) s0 += p[c * stride] * wgt[c];
-            o = ((s0 + s1) + (s2 + s3)) / lsum;
-            if (a.g) o *= sigmoidf_(a.g[(size_t)m * K + h * hd + d]);
+            float bm = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < CMB_BATCH; j++)
+                if (lv[j] > 0.f) bm = fmaxf(bm, mv[j]);
+            const float mn = fmaxf(mr, bm);
+            if (mn != -INFINITY) {
+                const float sc = lr > 0.f ? expf(mr - mn) : 0.f;
+                orun *= sc;
+                lr *= sc;
+#pragma unroll
+                for (int j = 0; j < CMB_BATCH; j++) {
+                    const float e = lv[j] > 0.f ? expf(mv[j] - mn) : 0.f;
+                    orun += ov[j] * e;
+                    lr += lv[j] * e;
+                }
+                mr = mn;
+            }
         }
-        split_store(a.xs, m, h * hd + d, o);
     }
+    sm_m[tid] = mr;
+    sm_l[tid] = lr;
+    sm_o[tid] = orun;
+    __syncthreads();
+    if (grp != 0) return;
+    float o = 0.f;
+    if (valid) {
+        float mx = -INFINITY;
+        for (int q = 0; q < ngrp; q++)
+            if (sm_l[q * hd + d] > 0.f) mx = fmaxf(mx, sm_m[q * hd + d]);
+        float osum = 0.f, lsum = 0.f;
+        for (int q = 0; q < ngrp; q++) {
+            const float lq = sm_l[q * hd + d];
+            const float e = lq > 0.f ? expf(sm_m[q * hd + d] - mx) : 0.f;
+            osum += sm_o[q * hd + d] * e;
+            lsum += lq * e;
+        }
+        o = osum / lsum;
+        if (a.g) o *= sigmoidf_(a.g[(size_t)m * K + h * hd + d]);
+    }
+    split_store(a.xs, m, h * hd + d, o);
     if (h == a.nq - 1) {
         const int Kp = (K + 31) & ~31;
-        for (int k = K + tid; k < Kp; k += blockDim.x) split_store(a.xs, m, k, 0.f);
+        for (int k = K + d; k < Kp; k += hd) split_store(a.xs, m, k, 0.f);
     }
 }
 

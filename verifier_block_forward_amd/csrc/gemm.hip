@@ -174,18 +174,155 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
         }
 }
 
-GemmPlan gemm_plan(int N, int K, int na, int target_units) {
+// ---------------------------------------------------------------------------
+// Variant with the activation slice staged in LDS: the four waves of a workgroup
+// share (segment, k-slice) and own consecutive row tiles, so the slice's split
+// activations are copied into LDS once (one barrier) and each wave's registers
+// hold only weights: a deep ring of LPIPE stages keeps (LPIPE-1)*NA KiB of weight
+// loads in flight per wave, which the short split-K slices of the per-layer
+// projections need to cover the ~4 us loaded memory latency.
+#ifndef DBF_LPIPE
+#define DBF_LPIPE 8
+#endif
+constexpr int LPIPE = DBF_LPIPE;
+constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
+
+template <int NA, int NB>
+__global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
+    __shared__ __align__(16) uint4 xl[LDS_X_BYTES / 16];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wg = blockIdx.x;
+    int si = 0;
+#pragma unroll 1
+    for (int i = 1; i < args.nseg; i++)
+        if (wg >= args.seg[i].unit_begin) si = i;
+    const GemmSeg &sg = args.seg[si];
+    int local = wg - sg.unit_begin;  // workgroup units: (tile group, ks) per slot
+    const int groups = (sg.tiles + 3) / 4;
+    const uint16_t *Wbase = sg.W;
+    const uint16_t *xsb0 = sg.xs0;
+    float *outb = sg.out;
+    if (sg.slots > 0) {
+        const int per = groups * sg.ksplit;
+        const int slot = local / per;
+        if (slot >= *sg.nslots) return;  // whole workgroup leaves together
+        local -= slot * per;
+        Wbase += (size_t)sg.slot_expert[slot] * (size_t)sg.w_stride;
+        xsb0 += (size_t)slot * (size_t)sg.xs_stride;
+        outb += (size_t)slot * (size_t)sg.out_stride;
+    }
+    const int grp = local % groups, ks = local / groups;
+    const int tile = grp * 4 + wv;
+    const int N = sg.N, K = sg.K;
+    const int S = (K + 31) >> 5;
+    const int s0 = ks * sg.kslice_steps;
+    int s1 = s0 + sg.kslice_steps;
+    if (s1 > S) s1 = S;
+    const int n = s1 - s0;
+    const int nb = NB == 1 ? 1 : sg.nb;
+    // stage the activation slice: per tile, steps [s0, s1) are contiguous (2 KiB each)
+    {
+        const uint4 *src0 = (const uint4 *)(xsb0 + (size_t)s0 * 2 * 64 * 8);
+        const int per = n * 128;  // uint4 per tile
+        for (int i = threadIdx.x; i < per; i += 256) xl[i] = src0[i];
+        if (NB > 1 && nb > 1) {
+            const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
+            for (int i = threadIdx.x; i < per; i += 256) xl[per + i] = src1[i];
+        }
+    }
+    __syncthreads();
+    if (tile >= sg.tiles) return;
+
+    const int r = lane & 15, g = lane >> 4;
+    const int row0 = tile * 16 * NA;
+    const uint16_t *wrow[NA];
+    const int wstep = sg.tiled ? 512 : 32;
+#pragma unroll
+    for (int a = 0; a < NA; a++) {
+        if (sg.tiled) {
+            int t = tile * NA + a;
+            const int T = (N + 15) >> 4;
+            if (t > T - 1) t = T - 1;
+            wrow[a] = Wbase + ((size_t)t * S * 64 + lane) * 8;
+        } else {
+            int row = row0 + 16 * a + r;
+            if (row > N - 1) row = N - 1;
+            wrow[a] = Wbase + (size_t)row * K + 8 * g;
+        }
+    }
+    f32x4 acc[NA][NB];
+#pragma unroll
+    for (int a = 0; a < NA; a++)
+#pragma unroll
+        for (int b = 0; b < NB; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    bf16x8 wb[LPIPE][NA];
+    const bool tiled = sg.tiled;
+#define DBF_LOAD_W(u, step)                                                     \
+    do {                                                                        \
+        const int sc_ = (step) < s1 ? (step) : s1 - 1;                          \
+        const bool in_ = tiled || 32 * sc_ + 8 * g < K;                         \
+        const int col_ = in_ ? wstep * sc_ : 0;                                 \
+        _Pragma("unroll") for (int a = 0; a < NA; a++) {                        \
+            const bf16x8 v_ = ld16(wrow[a] + col_);                             \
+            wb[u][a] = in_ ? v_ : zero8();                                      \
+        }                                                                       \
+    } while (0)
+#pragma unroll
+    for (int u = 0; u < LPIPE; u++) DBF_LOAD_W(u, s0 + u);
+    const int per = n * 128;
+    for (int base = 0; base < n; base += LPIPE) {
+#pragma unroll
+        for (int u = 0; u < LPIPE; u++) {
+            const int j = base + u;
+            if (j < n) {
+#pragma unroll
+                for (int b = 0; b < NB; b++) {
+                    if (b >= nb) continue;
+                    const bf16x8 xh = __builtin_bit_cast(bf16x8, xl[b * per + (j * 2 + 0) * 64 + lane]);
+                    const bf16x8 xlo = __builtin_bit_cast(bf16x8, xl[b * per + (j * 2 + 1) * 64 + lane]);
+#pragma unroll
+                    for (int a = 0; a < NA; a++) {
+                        acc[a][b] = MFMA(wb[u][a], xh, acc[a][b]);
+                        acc[a][b] = MFMA(wb[u][a], xlo, acc[a][b]);
+                    }
+                }
+            }
+            DBF_LOAD_W(u, s0 + base + u + LPIPE);
+        }
+    }
+#undef DBF_LOAD_W
+    float *out = outb + (size_t)ks * 16 * nb * N;
+#pragma unroll
+    for (int a = 0; a < NA; a++)
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            if (b >= nb) continue;
+            const int m = 16 * b + r;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int o = row0 + 16 * a + 4 * g + j;
+                if (o < N) out[(size_t)m * N + o] = acc[a][b][j];
+            }
+        }
+}
+
+GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {
     GemmPlan p{0, 0, 0};
     if (N < 1 || K < 1 || na < 1) return p;  // empty projection: no units
     p.tiles = (N + 16 * na - 1) / (16 * na);
     const int S = (K + 31) / 32;
     int ks = (target_units + p.tiles - 1) / p.tiles;
+    const int ks_min = max_steps > 0 ? (S + max_steps - 1) / max_steps : 1;
+    if (ks < ks_min) ks = ks_min;
     int max_ks = S / 4;  // keep at least 4 k-steps (128 columns) per slice
+    if (max_ks < ks_min) max_ks = ks_min;
     if (max_ks < 1) max_ks = 1;
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;
     int steps = (S + ks - 1) / ks;
     steps = (steps + 1) & ~1;  // even: slices start on 128-byte boundaries
+    if (max_steps > 0 && steps > max_steps) steps = max_steps & ~1;
     p.kslice_steps = steps;
     p.ksplit = (S + steps - 1) / steps;
     return p;
@@ -193,8 +330,12 @@ GemmPlan gemm_plan(int N, int K, int na, int target_units) {
 
 template <int NA, int NB>
 static void go(const GemmArgs &a, hipStream_t s) {
-    const int blocks = (a.total_units + 3) / 4;
-    hipLaunchKernelGGL((k_gemm_splitk<NA, NB>), dim3(blocks), dim3(256), 0, s, a);
+    if (a.lds_x) {  // total_units counts workgroups
+        hipLaunchKernelGGL((k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), 0, s, a);
+    } else {
+        const int blocks = (a.total_units + 3) / 4;
+        hipLaunchKernelGGL((k_gemm_splitk<NA, NB>), dim3(blocks), dim3(256), 0, s, a);
+    }
 }
 
 void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s) {
@@ -248,70 +389,188 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
     return o;
 }
 
-__global__ __launch_bounds__(256) void k_head(const uint16_t *__restrict__ W, int tiled,
-                                              const uint16_t *__restrict__ xs, int V, int K,
-                                              int M, float *__restrict__ logits,
-                                              float4 *__restrict__ part, int units) {
-    constexpr int NA = HEAD_NA;
-    const int lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (unit >= units) return;
+// The hidden rows come in as F32 [M][K]. The workgroup stages them through LDS in
+// chunks of HEAD_XCH k-steps: its 256 threads load a chunk once (16 rows x 64
+// contiguous bytes per load instruction), split every value into the BF16 hi/lo
+// pair and store the chunk in the split-tile order, double-buffered; the four
+// waves then read their B operands from LDS as contiguous 1 KiB lines. The next
+// chunk's loads are in flight while the current one feeds the matrix cores, and
+// the weight ring runs across chunk boundaries. Rows r >= M and columns past K
+// are zeros. The four waves merge their records in LDS, so the workgroup writes
+// one record per activation row, stored [16][workgroups].
+#ifndef DBF_HEAD_WPE
+#define DBF_HEAD_WPE 2
+#endif
+#ifndef DBF_HEAD_PIPE
+#define DBF_HEAD_PIPE 4
+#endif
+constexpr int HEAD_PIPE = DBF_HEAD_PIPE;
+constexpr int HEAD_XCH = 8;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
+static_assert(HEAD_XCH % HEAD_PIPE == 0, "chunk must hold whole pipeline rounds");
+
+// this thread's share of chunk c: 4 float4 (row tid % 16, float4 columns tid/16 + 16i)
+__device__ __forceinline__ void head_x_load(float4 (&xr)[4], const float *h, int M, int K, int c) {
+    const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
+    const bool rok = r < M;
+    const float *row = h + (size_t)(rok ? r : 0) * K;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int col = c * HEAD_XCH * 32 + 4 * (q + 16 * i);
+        const bool ok = rok && col < K;  // K % 8 == 0: a float4 is all in or all out
+        const float4 v = *(const float4 *)(row + (ok ? col : 0));
+        xr[i].x = ok ? v.x : 0.f;
+        xr[i].y = ok ? v.y : 0.f;
+        xr[i].z = ok ? v.z : 0.f;
+        xr[i].w = ok ? v.w : 0.f;
+    }
+}
+
+// split the thread's share and store it in split-tile order (element offset
+// ((s*2 + half)*64 + g*16 + r)*8 + j for local step s, column 8g + j)
+__device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[4]) {
+    const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int k = 4 * (q + 16 * i);  // local column
+        const int s = k >> 5, g = (k & 31) >> 3, j = k & 7;
+        const float f[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const __bf16 h0 = (__bf16)f[2 * e], h1 = (__bf16)f[2 * e + 1];
+            const __bf16 l0 = (__bf16)(f[2 * e] - (float)h0), l1 = (__bf16)(f[2 * e + 1] - (float)h1);
+            hw[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            lw[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        *(uint2 *)(buf + ((s * 2 + 0) * 64 + g * 16 + r) * 8 + j) = make_uint2(hw[0], hw[1]);
+        *(uint2 *)(buf + ((s * 2 + 1) * 64 + g * 16 + r) * 8 + j) = make_uint2(lw[0], lw[1]);
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WPE))) void k_head(
+    const uint16_t *__restrict__ W, int tiled, const float *__restrict__ h, int V, int K, int M,
+    float *__restrict__ logits, float4 *__restrict__ part, int units) {
+    constexpr int NA = HEAD_NA, PIPE = HEAD_PIPE;
+    constexpr int CHE = HEAD_XCH * 2 * 64 * 8;  // elements of one staged chunk
+    __shared__ __align__(16) uint16_t xbuf[2][CHE];
+    __shared__ Top2 wrec[4][16];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int unit = blockIdx.x * 4 + wv;
+    const bool active = unit < units;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = unit * 16 * NA;
-    const uint16_t *wrow[NA];
     const int S = (K + 31) >> 5;
+    const int nch = (S + HEAD_XCH - 1) / HEAD_XCH;
+
+    const uint16_t *wrow[NA];
 #pragma unroll
     for (int a = 0; a < NA; a++) {
         if (tiled) {
-            int t = unit * NA + a;
+            int tt = unit * NA + a;
             const int T = (V + 15) >> 4;
-            if (t > T - 1) t = T - 1;
-            wrow[a] = W + ((size_t)t * S * 64 + lane) * 8;
+            if (tt > T - 1) tt = T - 1;
+            wrow[a] = W + ((size_t)tt * S * 64 + lane) * 8;
         } else {
             int row = row0 + 16 * a + r;
             if (row > V - 1) row = V - 1;
             wrow[a] = W + (size_t)row * K + 8 * g;
         }
     }
-    const uint16_t *xsp[1] = {xs};
-    f32x4 acc[NA][1];
+    const int wstep = tiled ? 512 : 32;
+    f32x4 acc[NA];
 #pragma unroll
-    for (int a = 0; a < NA; a++) acc[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    skinny_mainloop<NA, 1, GEMM_PIPE>(wrow, tiled ? 512 : 32, tiled != 0, xsp, K, 0, S, lane, acc);
-
-    // lane holds rows o = row0 + 16a + 4g + j for activation row m = r
-    Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+    for (int a = 0; a < NA; a++) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 wb[PIPE][NA];
+#define DBF_HEAD_STAGE(u, step)                                                 \
+    do {                                                                        \
+        const int sc_ = (step) < S ? (step) : S - 1;                            \
+        const bool in_ = tiled || 32 * sc_ + 8 * g < K;                         \
+        const int col_ = in_ ? wstep * sc_ : 0;                                 \
+        _Pragma("unroll") for (int a = 0; a < NA; a++) {                        \
+            const bf16x8 v_ = ld16(wrow[a] + col_);                             \
+            wb[u][a] = in_ ? v_ : zero8();                                      \
+        }                                                                       \
+    } while (0)
+    if (active) {
 #pragma unroll
-    for (int a = 0; a < NA; a++)
+        for (int u = 0; u < PIPE; u++) DBF_HEAD_STAGE(u, u);
+    }
+    float4 xr[4];
+    head_x_load(xr, h, M, K, 0);
+    head_x_store(xbuf[0], xr);
+    if (nch > 1) head_x_load(xr, h, M, K, 1);
+    __syncthreads();
+    for (int c = 0; c < nch; c++) {
+        if (active) {
+            const uint4 *xb = (const uint4 *)xbuf[c & 1];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int o = row0 + 16 * a + 4 * g + j;
-            if (o < V) {
-                Top2 c{acc[a][0][j], o, -INFINITY};
-                t = merge(t, c);
+            for (int base = 0; base < HEAD_XCH; base += PIPE) {
+#pragma unroll
+                for (int u = 0; u < PIPE; u++) {
+                    const int sl = base + u, step = c * HEAD_XCH + sl;
+                    if (step < S) {
+                        const bf16x8 xh = __builtin_bit_cast(bf16x8, xb[(sl * 2 + 0) * 64 + lane]);
+                        const bf16x8 xl = __builtin_bit_cast(bf16x8, xb[(sl * 2 + 1) * 64 + lane]);
+#pragma unroll
+                        for (int a = 0; a < NA; a++) {
+                            acc[a] = MFMA(wb[u][a], xh, acc[a]);
+                            acc[a] = MFMA(wb[u][a], xl, acc[a]);
+                        }
+                    }
+                    DBF_HEAD_STAGE(u, step + PIPE);
+                }
             }
         }
-    if (logits && r < M) {
+        if (c + 1 < nch) {
+            head_x_store(xbuf[(c + 1) & 1], xr);
+            if (c + 2 < nch) head_x_load(xr, h, M, K, c + 2);
+        }
+        __syncthreads();
+    }
+#undef DBF_HEAD_STAGE
+
+    Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+    if (active) {
+        // lane holds rows o = row0 + 16a + 4g + j for activation row m = r
 #pragma unroll
         for (int a = 0; a < NA; a++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int o = row0 + 16 * a + 4 * g + j;
-                if (o < V) logits[(size_t)r * V + o] = acc[a][0][j];
+                if (o < V) {
+                    Top2 cnd{acc[a][j], o, -INFINITY};
+                    t = merge(t, cnd);
+                }
             }
+        if (logits && r < M) {
+#pragma unroll
+            for (int a = 0; a < NA; a++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int o = row0 + 16 * a + 4 * g + j;
+                    if (o < V) logits[(size_t)r * V + o] = acc[a][j];
+                }
+        }
+        t = merge(t, shfl_top2(t, 16));
+        t = merge(t, shfl_top2(t, 32));
     }
-    t = merge(t, shfl_top2(t, 16));
-    t = merge(t, shfl_top2(t, 32));
-    if (g == 0) part[(size_t)unit * 16 + r] = make_float4(t.v1, __int_as_float(t.i1), t.v2, 0.f);
+    if (g == 0) wrec[wv][r] = t;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int m = threadIdx.x;
+        const Top2 q = merge(merge(wrec[0][m], wrec[1][m]), merge(wrec[2][m], wrec[3][m]));
+        part[(size_t)m * gridDim.x + blockIdx.x] = make_float4(q.v1, __int_as_float(q.i1), q.v2, 0.f);
+    }
 }
 
 int head_units(int V) { return (V + 16 * HEAD_NA - 1) / (16 * HEAD_NA); }
+int head_blocks(int V) { return (head_units(V) + 3) / 4; }
 
-void launch_head(const uint16_t *W, int tiled, const uint16_t *xs, int V, int K, int M,
-                 float *logits, float4 *part, hipStream_t s) {
+void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M, float *logits,
+                 float4 *part, hipStream_t s) {
     const int units = head_units(V);
-    hipLaunchKernelGGL(k_head, dim3((units + 3) / 4), dim3(256), 0, s, W, tiled, xs, V, K, M,
-                       logits, part, units);
+    hipLaunchKernelGGL(k_head, dim3(head_blocks(V)), dim3(256), 0, s, W, tiled, h, V, K, M, logits,
+                       part, units);
 }
 
 // ---------------------------------------------------------------------------
@@ -345,14 +604,16 @@ void launch_tile(const uint16_t *src, uint16_t *dst, long long batch, int N, int
                        per, total);
 }
 
-// one block per activation row: fold every unit's top-2 record
-__global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ part, int units,
+// one block per activation row: fold the workgroups' top-2 records of that row
+// (contiguous), in a fixed order
+__global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ part, int blocks,
                                                      int32_t *__restrict__ argmax,
                                                      float *__restrict__ margin) {
     const int m = blockIdx.x;
     Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
-    for (int u = threadIdx.x; u < units; u += 256) {
-        float4 p = part[(size_t)u * 16 + m];
+    const float4 *pm = part + (size_t)m * blocks;
+    for (int u = threadIdx.x; u < blocks; u += 256) {
+        const float4 p = pm[u];
         Top2 c{p.x, __float_as_int(p.y), p.z};
         t = merge(t, c);
     }
@@ -368,9 +629,9 @@ __global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ 
     }
 }
 
-void launch_head_reduce(const float4 *part, int units, int M, int32_t *argmax, float *margin,
+void launch_head_reduce(const float4 *part, int blocks, int M, int32_t *argmax, float *margin,
                         hipStream_t s) {
-    hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, s, part, units, argmax, margin);
+    hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, s, part, blocks, argmax, margin);
 }
 
 }  // namespace dbf

@@ -80,4 +80,41 @@ __device__ __forceinline__ float block_sum_256(float v, float *sh4) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Split-K partial sums. A projection writes its ks partial products as
+// [ks][rows][N] F32; consumers add them in increasing ks order. The loads go out
+// in batches of PARTIAL_BATCH (indexes past ks re-read the last partial and are
+// not added), so a sum over ks partials costs ceil(ks / PARTIAL_BATCH) memory
+// round trips instead of one per few partials.
+constexpr int PARTIAL_BATCH = 16;
+
+// NV sums sharing ks and the partial stride: out[v] = sum_t base[v][t * stride]
+template <int NV>
+__device__ __forceinline__ void sum_partials_n(const float *const base[NV], int ks, size_t stride,
+                                               float out[NV]) {
+#pragma unroll
+    for (int v = 0; v < NV; v++) out[v] = 0.f;
+    for (int t0 = 0; t0 < ks; t0 += PARTIAL_BATCH) {
+        float x[NV][PARTIAL_BATCH];
+#pragma unroll
+        for (int u = 0; u < PARTIAL_BATCH; u++) {
+            const int t = t0 + u < ks ? t0 + u : ks - 1;
+#pragma unroll
+            for (int v = 0; v < NV; v++) x[v][u] = base[v][(size_t)t * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < PARTIAL_BATCH; u++)
+#pragma unroll
+            for (int v = 0; v < NV; v++) out[v] += t0 + u < ks ? x[v][u] : 0.f;
+    }
+}
+
+// element (row, col) summed over the ks partials of a [ks][rows][N] buffer
+__device__ __forceinline__ float sum_partials(const float *p, int ks, int rows, int N, int row,
+                                              int col) {
+    const float *b[1] = {p + (size_t)row * N + col};
+    float o[1];
+    sum_partials_n<1>(b, ks, (size_t)rows * N, o);
+    return o[0];
+}
+
 }  // namespace dbf

@@ -33,33 +33,39 @@ struct GemmSeg {
 struct GemmArgs {
     GemmSeg seg[GEMM_MAXSEG];
     int nseg;
-    int total_units;
+    int total_units;  // wave units (lds_x = 0) or workgroup units (lds_x = 1)
+    int lds_x;        // 1: k_gemm_lds (activation slice staged in LDS)
 };
 
 // Work decomposition of one segment: rows per wave unit = 16 * na.
 struct GemmPlan {
     int tiles, ksplit, kslice_steps;
 };
-GemmPlan gemm_plan(int N, int K, int na, int target_units);
+// max_steps > 0 caps the k-slice length (steps of 32 columns)
+GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps = 0);
+constexpr int LDS_X_STEPS_NB1 = 20;  // 40 KiB of split activations per workgroup
+constexpr int LDS_X_STEPS_NB2 = 10;
 
 void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// lm_head: logits = h W^T over V rows, with per-unit top-2 records for the
+// lm_head: logits = h W^T over V rows, with per-workgroup top-2 records for the
 // argmax, then a per-row reduction.
 // ---------------------------------------------------------------------------
 #ifndef DBF_HEAD_NA
-#define DBF_HEAD_NA 4
+#define DBF_HEAD_NA 8
 #endif
 constexpr int HEAD_NA = DBF_HEAD_NA;  // 16*HEAD_NA vocabulary rows per wave unit
 int head_units(int V);
-void launch_head(const uint16_t *W, int tiled, const uint16_t *xs, int V, int K, int M,
+int head_blocks(int V);  // workgroups of the head launch (4 wave units each)
+// h: F32 [M][K] hidden rows; part: [16][head_blocks(V)] top-2 records
+void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M,
                  float *logits, float4 *part, hipStream_t s);
 
 // weight tiling (MFMA operand order, see gemm.hip)
 size_t tiled_elems(long long N, long long K);
 void launch_tile(const uint16_t *src, uint16_t *dst, long long batch, int N, int K, hipStream_t s);
-void launch_head_reduce(const float4 *part, int units, int M, int32_t *argmax, float *margin,
+void launch_head_reduce(const float4 *part, int blocks, int M, int32_t *argmax, float *margin,
                         hipStream_t s);
 
 // ---------------------------------------------------------------------------
@@ -91,6 +97,8 @@ void launch_colsum(const ColArgs &a, hipStream_t s);
 void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
                        float *out, hipStream_t s);
 
+constexpr int ROPE_MAX_PAIRS = 128;  // rotary_dim <= 256
+
 struct QkvPostArgs {
     const float *pq;   // [ksq][16][qt]
     const float *pk;   // [ksk][rows_kv][kt]
@@ -102,7 +110,7 @@ struct QkvPostArgs {
     int ncb, H;
     const float *q_norm, *k_norm;
     float eps;
-    double theta;
+    double inv_freq[ROPE_MAX_PAIRS];  // theta^(-2j/rotary_dim), j < rotary_dim/2, in F64
     int rotary_dim;
     int M, R, nq, nkv, hd;
     long long P0;

@@ -29,20 +29,6 @@ __device__ __forceinline__ float moe_row_scale(const float *ssp_row, int ncb, in
     return 1.0f / sqrtf(s / (float)H + eps);
 }
 
-__device__ __forceinline__ float moe_sum_partials(const float *p, int ks, int rows, int N, int row,
-                                                  int col) {
-    const size_t stride = (size_t)rows * N;
-    const float *q = p + (size_t)row * N + col;
-    float a0 = 0.f, a1 = 0.f;
-    int t = 0;
-    for (; t + 1 < ks; t += 2) {
-        a0 += q[t * stride];
-        a1 += q[(t + 1) * stride];
-    }
-    if (t < ks) a0 += q[t * stride];
-    return a0 + a1;
-}
-
 // (value, index) with ties to the lower index
 __device__ __forceinline__ void better_pair(float &v, int &i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) {
@@ -69,7 +55,7 @@ __global__ __launch_bounds__(256) void k_moe_route(MoeRouteArgs a) {
     for (int m = 0; m < a.M; m++) {
         const float s = moe_row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
         for (int e = tid; e < E; e += 256) {
-            z[e] = s * moe_sum_partials(a.p_router, a.ks_router, 16, E, m, e);
+            z[e] = s * sum_partials(a.p_router, a.ks_router, 16, E, m, e);
             taken[e] = 0;
         }
         __syncthreads();
@@ -115,7 +101,7 @@ __global__ __launch_bounds__(256) void k_moe_route(MoeRouteArgs a) {
             }
         }
         if (wv == 0) {
-            const float g = s * moe_sum_partials(a.p_sgi, a.ks_sgi, 16, 1, m, 0);
+            const float g = s * sum_partials(a.p_sgi, a.ks_sgi, 16, 1, m, 0);
             if (lane == 0) a.shared_scale[m] = sigmoidf_(g);
         }
         __syncthreads();
@@ -165,12 +151,12 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
         if (k < I) {
             float g, u;
             if (shared) {
-                g = s * moe_sum_partials(a.psg, a.ks_sh, 16, I, m, k);
-                u = s * moe_sum_partials(a.psu, a.ks_sh, 16, I, m, k);
+                g = s * sum_partials(a.psg, a.ks_sh, 16, I, m, k);
+                u = s * sum_partials(a.psu, a.ks_sh, 16, I, m, k);
             } else {
                 const size_t so = (size_t)slot * a.ks * 16 * I;
-                g = s * moe_sum_partials(a.pg + so, a.ks, 16, I, m, k);
-                u = s * moe_sum_partials(a.pu + so, a.ks, 16, I, m, k);
+                g = s * sum_partials(a.pg + so, a.ks, 16, I, m, k);
+                u = s * sum_partials(a.pu + so, a.ks, 16, I, m, k);
             }
             h = g / (1.0f + expf(-g)) * u;
         }
@@ -200,9 +186,9 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
         for (int sl = 0; sl < ns; sl++) {
             const float c = a.coef[(size_t)sl * 16 + m];
             if (c != 0.f)
-                y += c * moe_sum_partials(a.pd + (size_t)sl * a.ks * 16 * a.H, a.ks, 16, a.H, m, k);
+                y += c * sum_partials(a.pd + (size_t)sl * a.ks * 16 * a.H, a.ks, 16, a.H, m, k);
         }
-        y += a.shared_scale[m] * moe_sum_partials(a.psd, a.ks_sh, 16, a.H, m, k);
+        y += a.shared_scale[m] * sum_partials(a.psd, a.ks_sh, 16, a.H, m, k);
         v += y;
         if (a.out) a.out[(size_t)m * a.H + k] = v;
         if (a.copy0) a.copy0[(size_t)m * a.H + k] = v;

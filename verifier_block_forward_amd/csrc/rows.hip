@@ -24,23 +24,6 @@ __device__ __forceinline__ float row_scale(const float *ssp_row, int ncb, int H,
     return 1.0f / sqrtf(s / (float)H + eps);
 }
 
-// sum over ks split-K partials of element (row, col) in a [ks][rows][N] buffer
-__device__ __forceinline__ float sum_partials(const float *p, int ks, int rows, int N, int row,
-                                              int col) {
-    const size_t stride = (size_t)rows * N;
-    const float *q = p + (size_t)row * N + col;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int t = 0;
-    for (; t + 3 < ks; t += 4) {
-        a0 += q[(t + 0) * stride];
-        a1 += q[(t + 1) * stride];
-        a2 += q[(t + 2) * stride];
-        a3 += q[(t + 3) * stride];
-    }
-    for (; t < ks; t++) a0 += q[t * stride];
-    return (a0 + a1) + (a2 + a3);
-}
-
 // ---------------------------------------------------------------------------
 // Generic column kernel. Grid (ncb = ceil(H/64), 4), 256 threads: wave w handles
 // row m = 4*blockIdx.y + w, lane the column blockIdx.x*64 + lane.
@@ -108,22 +91,27 @@ void launch_final_norm(const float *x, const float *ssp, int M, int H, const flo
 // Q/K/V post-processing, one wavefront per head vector (qwen35/mtp.rs
 // `forward_full_attention`): sum split-K partials and apply the row's RMSNorm
 // scale; per-head RMSNorm (q_norm / k_norm); rotate-half RoPE over the first
-// rotary_dim lanes with angle pos * theta^(-2j/rotary_dim) formed in F64 (an F32
-// product is off by ~1e-3 rad at 32k positions); store q (block rows) and the raw
-// gate, or the key and value rows of the cache (F32, or BF16 with RNE).
+// rotary_dim lanes; store q (block rows) and the raw gate, or the key and value
+// rows of the cache (F32, or BF16 with RNE). The RoPE angle pos * inv_freq[j] is
+// formed in F64 from the host's F64 table theta^(-2j/rotary_dim) and reduced
+// modulo 2 pi in F64 (an F32 product is off by ~1e-3 rad at 32k positions), then
+// sin/cos are taken in F32 on the reduced angle. The partial sums of the head and
+// of its companion (gate or value) are loaded together. Each lane owns CPL =
+// hd/64 columns d = lane + 64 i.
 // Blocks [0, M*nq) are q heads of block rows; then (R+M)*nkv k/v heads, context
 // rows first. DFlash context rows sit at positions P0+r, block rows at P0+R+m.
+template <int CPL>
 __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
-    __shared__ float vec[256];
+    __shared__ float vec[64 * CPL];
     const int lane = threadIdx.x;
-    const int hd = a.hd, qt = a.nq * hd, kt = a.nkv * hd;
+    const int hd = 64 * CPL, qt = a.nq * hd, kt = a.nkv * hd;
     const int b = blockIdx.x;
     const bool isq = b < a.M * a.nq;
     int row, head;         // row within its group (block rows or all kv rows), head index
     long long pos;
     float s;               // RMSNorm scale of the source row
-    const float *src, *wn; // partial buffer, head-norm weight
-    int ks, prow, N;
+    const float *src, *src2, *wn;  // partials of the head and of its gate / value, head-norm weight
+    int ks, ks2, prow, N, rows;
     if (isq) {
         row = b / a.nq;
         head = b % a.nq;
@@ -131,8 +119,11 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
         s = row_scale(a.ssp_x + (size_t)row * a.ncb, a.ncb, a.H, a.eps);
         src = a.pq;
         ks = a.ksq;
+        src2 = a.pg;
+        ks2 = a.ksg;
         prow = row;
         N = qt;
+        rows = 16;
         wn = a.q_norm;
     } else {
         const int idx = b - a.M * a.nq;
@@ -145,76 +136,91 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
                 : row_scale(a.ssp_x + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
         src = a.pk;
         ks = a.ksk;
+        src2 = a.pv;
+        ks2 = a.ksv;
         prow = ctx ? m : a.kv_block_row0 + m;
         N = kt;
+        rows = a.rows_kv;
         wn = a.k_norm;
     }
-    const int rows = isq ? 16 : a.rows_kv;
-    float raw[4];
+    const size_t stride = (size_t)rows * N;
+    const size_t rowoff = (size_t)prow * N + (size_t)head * hd + lane;
+    float raw[CPL], side[CPL] = {};
+    if (src2 && ks2 == ks) {
+        const float *bb[2 * CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            bb[i] = src + rowoff + 64 * i;
+            bb[CPL + i] = src2 + rowoff + 64 * i;
+        }
+        float o[2 * CPL];
+        sum_partials_n<2 * CPL>(bb, ks, stride, o);
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            raw[i] = o[i];
+            side[i] = o[CPL + i];
+        }
+    } else {
+        const float *bb[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; i++) bb[i] = src + rowoff + 64 * i;
+        sum_partials_n<CPL>(bb, ks, stride, raw);
+        if (src2) {
+#pragma unroll
+            for (int i = 0; i < CPL; i++) bb[i] = src2 + rowoff + 64 * i;
+            sum_partials_n<CPL>(bb, ks2, stride, side);
+        }
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int d = lane + 64 * i;
-        raw[i] = 0.f;
-        if (d < hd) {
-            raw[i] = s * sum_partials(src, ks, rows, N, prow, head * hd + d);
-            ss += raw[i] * raw[i];
-        }
+    for (int i = 0; i < CPL; i++) {
+        raw[i] *= s;
+        side[i] *= s;
+        ss += raw[i] * raw[i];
     }
     const float hs = 1.0f / sqrtf(wave_sum(ss) / (float)hd + a.eps);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < CPL; i++) {
         const int d = lane + 64 * i;
-        if (d < hd) vec[d] = raw[i] * hs * wn[d];
+        vec[d] = raw[i] * hs * wn[d];
     }
     __syncthreads();
     const int half = a.rotary_dim / 2;
     const size_t cache_off = ((size_t)head * a.capacity + pos) * hd;
+    const double two_pi = 6.283185307179586;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < CPL; i++) {
         const int d = lane + 64 * i;
-        if (d >= hd) continue;
         float val = vec[d];
         if (d < 2 * half) {
             const int j = d < half ? d : d - half;
             const float pv = vec[d < half ? d + half : d - half];
-            const double ang = (double)pos * pow(a.theta, -2.0 * (double)j / (double)a.rotary_dim);
-            double sn, cs;
-            sincos(ang, &sn, &cs);
-            const float c = (float)cs, sv = (float)sn;
+            const double ang = (double)pos * a.inv_freq[j];
+            const double red = fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);  // |red| <= pi
+            float sv, c;
+            sincosf((float)red, &sv, &c);
             val = d < half ? val * c - pv * sv : pv * sv + val * c;
         }
         if (isq) {
             a.q_out[(size_t)row * qt + head * hd + d] = val;
+            if (src2) a.g_out[(size_t)row * qt + head * hd + d] = side[i];
         } else {
-            if (a.kv_bf16) ((uint16_t *)a.cache_k)[cache_off + d] = f32_to_bf16(val);
-            else ((float *)a.cache_k)[cache_off + d] = val;
-        }
-    }
-    // the gate (q blocks) and the value row (k blocks): same source row, no head norm
-    if (isq && a.pg) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int d = lane + 64 * i;
-            if (d < hd)
-                a.g_out[(size_t)row * qt + head * hd + d] =
-                    s * sum_partials(a.pg, a.ksg, 16, qt, row, head * hd + d);
-        }
-    }
-    if (!isq) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int d = lane + 64 * i;
-            if (d >= hd) continue;
-            const float v = s * sum_partials(a.pv, a.ksv, a.rows_kv, kt, prow, head * hd + d);
-            if (a.kv_bf16) ((uint16_t *)a.cache_v)[cache_off + d] = f32_to_bf16(v);
-            else ((float *)a.cache_v)[cache_off + d] = v;
+            if (a.kv_bf16) {
+                ((uint16_t *)a.cache_k)[cache_off + d] = f32_to_bf16(val);
+                ((uint16_t *)a.cache_v)[cache_off + d] = f32_to_bf16(side[i]);
+            } else {
+                ((float *)a.cache_k)[cache_off + d] = val;
+                ((float *)a.cache_v)[cache_off + d] = side[i];
+            }
         }
     }
 }
 
 void launch_qkv_post(const QkvPostArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_qkv_post, dim3(a.M * a.nq + (a.R + a.M) * a.nkv), dim3(64), 0, s, a);
+    const dim3 grid(a.M * a.nq + (a.R + a.M) * a.nkv);
+    if (a.hd == 64) hipLaunchKernelGGL(k_qkv_post<1>, grid, dim3(64), 0, s, a);
+    else if (a.hd == 128) hipLaunchKernelGGL(k_qkv_post<2>, grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(k_qkv_post<4>, grid, dim3(64), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
