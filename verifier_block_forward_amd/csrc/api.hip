@@ -56,7 +56,7 @@ int check_t(const dbf_tensor &t, const char *name, int dtype, int ndim, int64_t 
     } while (0)
 
 constexpr int TARGET_UNITS = 2048;  // wave units per projection launch (256 CUs x 8)
-constexpr int GEMM_NA = 2;
+constexpr int GEMM_NA = 2;          // row tiles per wave of the plain split-K kernel
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -88,14 +88,18 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.rd = c.rotary_dim > 0 ? c.rotary_dim : c.head_dim;
     const int na = GEMM_NA;
     p.in = gemm_plan(p.H, p.Kin, na, c.kind == DBF_KIND_MTP ? TARGET_UNITS / 2 : TARGET_UNITS);
-    // Q, K, V (and gate) share one launch: split the unit budget by row counts
-    p.q = gemm_plan(p.qt, p.H, na, TARGET_UNITS / 2);
-    p.k = gemm_plan(p.kt, p.H, na, TARGET_UNITS / 4);
+    // Launch shapes measured on MI355X at the benchmark sizes: the wide projections
+    // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one)
+    // stream faster with the activation slice in LDS and a deep weight ring; the
+    // O, down and input projections with the plain split-K kernel.
+    const int nbq = R > 0 ? 2 : 1;  // K/V also project the context rows
+    p.q = gemm_plan_lds(p.qt, p.H, 1, TARGET_UNITS / 4, nbq);
+    p.k = gemm_plan_lds(p.kt, p.H, 1, TARGET_UNITS / 4, nbq);
     p.v = p.k;
     p.g = p.q;
-    p.o = gemm_plan(p.H, p.qt, na, TARGET_UNITS);
+    p.o = gemm_plan(p.H, p.qt, na, TARGET_UNITS / 2);
     if (c.ffn_kind == DBF_FFN_DENSE) {
-        p.gate = gemm_plan(p.I, p.H, na, TARGET_UNITS / 2);
+        p.gate = gemm_plan_lds(p.I, p.H, 2, TARGET_UNITS / 4, 1);
         p.up = p.gate;
         p.down = gemm_plan(p.H, p.I, na, TARGET_UNITS);
     }
@@ -167,11 +171,17 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     return p;
 }
 
+// One projection launch: segments planned with the same na and lds (the first
+// segment's plan fixes the kernel).
 struct SegList {
     GemmArgs a{};
-    int nbmax = 1;
+    int nbmax = 1, na = GEMM_NA;
     void add(const dbf_tensor &t, int N, int K, const GemmPlan &pl, float *out, const uint16_t *xs0,
              const uint16_t *xs1 = nullptr) {
+        if (a.nseg == 0) {
+            na = pl.na;
+            a.lds_x = pl.lds;
+        }
         GemmSeg &s = a.seg[a.nseg++];
         s.W = (const uint16_t *)t.data;
         s.tiled = t.dtype == DBF_BF16_T16;
@@ -185,7 +195,7 @@ struct SegList {
         s.kslice_steps = pl.kslice_steps;
         s.tiles = pl.tiles;
         s.unit_begin = a.total_units;
-        a.total_units += pl.tiles * pl.ksplit;
+        a.total_units += plan_units(pl);
         if (s.nb > nbmax) nbmax = s.nb;
     }
     // grouped (MoE experts): `slots` matrices selected on the device
@@ -200,9 +210,9 @@ struct SegList {
         s.w_stride = s.tiled ? (long long)tiled_elems(N, K) : (long long)N * K;
         s.xs_stride = xs_stride;
         s.out_stride = (long long)pl.ksplit * 16 * N;
-        a.total_units += (slots - 1) * pl.tiles * pl.ksplit;
+        a.total_units += (slots - 1) * plan_units(pl);
     }
-    void launch(hipStream_t st) { launch_gemm(a, GEMM_NA, nbmax, st); }
+    void launch(hipStream_t st) { launch_gemm(a, na, nbmax, st); }
 };
 
 int validate_config(const dbf_config *c) {

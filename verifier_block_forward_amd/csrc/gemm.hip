@@ -182,14 +182,14 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
 // loads in flight per wave, which the short split-K slices of the per-layer
 // projections need to cover the ~4 us loaded memory latency.
 #ifndef DBF_LPIPE
-#define DBF_LPIPE 8
+#define DBF_LPIPE 6
 #endif
 constexpr int LPIPE = DBF_LPIPE;
 constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
 
 template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
-    __shared__ __align__(16) uint4 xl[LDS_X_BYTES / 16];
+    extern __shared__ __align__(16) uint4 xl[];  // NB * kslice_steps * 2 KiB (<= LDS_X_BYTES)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wg = blockIdx.x;
     int si = 0;
@@ -220,19 +220,6 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     if (s1 > S) s1 = S;
     const int n = s1 - s0;
     const int nb = NB == 1 ? 1 : sg.nb;
-    // stage the activation slice: per tile, steps [s0, s1) are contiguous (2 KiB each)
-    {
-        const uint4 *src0 = (const uint4 *)(xsb0 + (size_t)s0 * 2 * 64 * 8);
-        const int per = n * 128;  // uint4 per tile
-        for (int i = threadIdx.x; i < per; i += 256) xl[i] = src0[i];
-        if (NB > 1 && nb > 1) {
-            const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
-            for (int i = threadIdx.x; i < per; i += 256) xl[per + i] = src1[i];
-        }
-    }
-    __syncthreads();
-    if (tile >= sg.tiles) return;
-
     const int r = lane & 15, g = lane >> 4;
     const int row0 = tile * 16 * NA;
     const uint16_t *wrow[NA];
@@ -242,7 +229,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
         if (sg.tiled) {
             int t = tile * NA + a;
             const int T = (N + 15) >> 4;
-            if (t > T - 1) t = T - 1;
+            if (t > T - 1) t = T - 1;  // also for waves past the last tile: valid, unused
             wrow[a] = Wbase + ((size_t)t * S * 64 + lane) * 8;
         } else {
             int row = row0 + 16 * a + r;
@@ -268,8 +255,22 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
             wb[u][a] = in_ ? v_ : zero8();                                      \
         }                                                                       \
     } while (0)
+    // the weight stream starts before the activation slice is staged
 #pragma unroll
     for (int u = 0; u < LPIPE; u++) DBF_LOAD_W(u, s0 + u);
+    // stage the activation slice: per tile, steps [s0, s1) are contiguous (2 KiB each)
+    {
+        const uint4 *src0 = (const uint4 *)(xsb0 + (size_t)s0 * 2 * 64 * 8);
+        const int per = n * 128;  // uint4 per tile
+        for (int i = threadIdx.x; i < per; i += 256) xl[i] = src0[i];
+        if (NB > 1 && nb > 1) {
+            const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
+            for (int i = threadIdx.x; i < per; i += 256) xl[per + i] = src1[i];
+        }
+    }
+    __syncthreads();
+    if (tile >= sg.tiles) return;
+
     const int per = n * 128;
     for (int base = 0; base < n; base += LPIPE) {
 #pragma unroll
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
 }
 
 GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {
-    GemmPlan p{0, 0, 0};
+    GemmPlan p{0, 0, 0, na, 0};
     if (N < 1 || K < 1 || na < 1) return p;  // empty projection: no units
     p.tiles = (N + 16 * na - 1) / (16 * na);
     const int S = (K + 31) / 32;
@@ -328,10 +329,21 @@ GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {
     return p;
 }
 
+GemmPlan gemm_plan_lds(int N, int K, int na, int target_units, int nbmax) {
+    GemmPlan p = gemm_plan(N, K, na, target_units, nbmax > 1 ? LDS_X_STEPS_NB2 : LDS_X_STEPS_NB1);
+    p.lds = 1;
+    return p;
+}
+
 template <int NA, int NB>
 static void go(const GemmArgs &a, hipStream_t s) {
     if (a.lds_x) {  // total_units counts workgroups
-        hipLaunchKernelGGL((k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), 0, s, a);
+        size_t lds = 0;
+        for (int i = 0; i < a.nseg; i++) {
+            const size_t b = (size_t)(NB > 1 ? a.seg[i].nb : 1) * a.seg[i].kslice_steps * 2048;
+            if (b > lds) lds = b;
+        }
+        hipLaunchKernelGGL((k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), lds, s, a);
     } else {
         const int blocks = (a.total_units + 3) / 4;
         hipLaunchKernelGGL((k_gemm_splitk<NA, NB>), dim3(blocks), dim3(256), 0, s, a);

@@ -37,14 +37,23 @@ struct GemmArgs {
     int lds_x;        // 1: k_gemm_lds (activation slice staged in LDS)
 };
 
-// Work decomposition of one segment: rows per wave unit = 16 * na.
+// Work decomposition of one segment: rows per wave unit = 16 * na; lds selects
+// the kernel with the activation slice staged in LDS (units are then workgroups of
+// four row tiles). Segments of one launch share na and lds.
 struct GemmPlan {
-    int tiles, ksplit, kslice_steps;
+    int tiles, ksplit, kslice_steps, na, lds;
 };
-// max_steps > 0 caps the k-slice length (steps of 32 columns)
+// target_units: wave units (tiles x ksplit) to aim for; max_steps > 0 caps the
+// k-slice length (steps of 32 columns)
 GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps = 0);
 constexpr int LDS_X_STEPS_NB1 = 20;  // 40 KiB of split activations per workgroup
 constexpr int LDS_X_STEPS_NB2 = 10;
+// LDS-staged plan for a launch whose segments have up to nbmax split tiles
+GemmPlan gemm_plan_lds(int N, int K, int na, int target_units, int nbmax);
+// units (waves, or workgroups for lds plans) of one matrix of the segment
+inline int plan_units(const GemmPlan &p) {
+    return p.lds ? ((p.tiles + 3) / 4) * p.ksplit : p.tiles * p.ksplit;
+}
 
 void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s);
 
