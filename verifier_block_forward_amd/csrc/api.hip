@@ -473,7 +473,8 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     {
         const int nq_group = (c.n_q_heads / c.n_kv_heads) * M;
         const int qt = attn_qtiles(hd, nq_group);
-        attn_plan(P0 + R + M, nq_group < 16 * qt ? nq_group : 16 * qt, &chunk, &n_chunks);
+        const int qgroups = (nq_group + 16 * qt - 1) / (16 * qt);
+        attn_plan(P0 + R + M, c.n_kv_heads * qgroups, &chunk, &n_chunks);
     }
     // RoPE inverse frequencies theta^(-2j/rotary_dim), in F64, shared by every layer
     double inv_freq[ROPE_MAX_PAIRS];

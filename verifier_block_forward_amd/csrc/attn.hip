@@ -5,8 +5,10 @@
 // prefix, this call's context rows and the block rows up to itself (causal within
 // the block). q head h reads kv head h*nkv/nq (contiguous GQA groups). Scores are
 // scaled by 1/sqrt(hd) and normalised with an online softmax (running max m, sum
-// l, accumulator acc); each (chunk, kv head) block writes (acc, m, l) for its
-// queries and the combine pass merges chunks. (qwen35/mtp.rs
+// l, accumulator acc) kept in base 2: the scores carry an extra factor log2(e), so
+// exp(s - m) is formed as 2^(s' - m') and m is stored in log2 units. Each (chunk,
+// kv head) block writes (acc, m, l) for its queries and the combine pass merges
+// chunks. (qwen35/mtp.rs
 // `forward_full_attention`: `apply_sdpa_with_kv_cache`, then
 // `apply_sigmoid_gate_multiply`.)
 #include "internal.hpp"
@@ -17,17 +19,29 @@ namespace dbf {
 constexpr int ATT_KT = 16;     // keys per sub-tile
 constexpr int ATT_WAVES = 4;   // waves per workgroup, each on a quarter of the chunk
 
-// Keys per wave: at least 16 and as many as the queries a wave serves (so the
-// (acc, m, l) partial of a 4-wave chunk stays ~1/8 of its K/V bytes), grown until
-// there are at most ATT_CHUNKS_MAX chunks.
-void attn_plan(long long n_keys, int nq_per_wave, int *chunk, int *n_chunks) {
-    long long pw = (nq_per_wave + ATT_KT - 1) / ATT_KT * ATT_KT;
+// Chunking of the keys. Keys per wave are sized so that the launch has about one
+// 4-wave workgroup per CU: on MI355X fewer, longer chunks were measured faster than
+// more parallelism, since every workgroup pays for staging the queries and merging
+// its waves, and every chunk adds a partial record to the combine. At least one
+// 16-key sub-tile per wave, and at most ATT_CHUNKS_MAX chunks.
+void attn_plan_keys(long long n_keys, int keys_per_wave, int *chunk, int *n_chunks) {
+    long long pw = (keys_per_wave + ATT_KT - 1) / ATT_KT * ATT_KT;
     if (pw < ATT_KT) pw = ATT_KT;
-    long long per = (n_keys + ATT_CHUNKS_MAX - 1) / ATT_CHUNKS_MAX;           // keys per chunk
-    long long pw_min = (per + ATT_WAVES * ATT_KT - 1) / (ATT_WAVES * ATT_KT) * ATT_KT;
+    const long long per = (n_keys + ATT_CHUNKS_MAX - 1) / ATT_CHUNKS_MAX;  // keys per chunk
+    const long long pw_min = (per + ATT_WAVES * ATT_KT - 1) / (ATT_WAVES * ATT_KT) * ATT_KT;
     if (pw < pw_min) pw = pw_min;
     *chunk = (int)(ATT_WAVES * pw);
     *n_chunks = (int)((n_keys + *chunk - 1) / *chunk);
+}
+
+void attn_plan(long long n_keys, int groups, int *chunk, int *n_chunks) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const long long chunks = cus / groups > 1 ? cus / groups : 1;
+    const long long per = (n_keys + chunks - 1) / chunks;
+    attn_plan_keys(n_keys, (int)((per + ATT_WAVES - 1) / ATT_WAVES), chunk, n_chunks);
 }
 
 int attn_qtiles(int hd, int nq_group) {
@@ -51,8 +65,8 @@ template <int HD, int QT, bool KVB>
 struct AttnLds {
     static constexpr int S = HD / 32, DT = HD / 16, VTW = 22;
     static constexpr int Q_BYTES = QT * S * 2 * 64 * 16;
-    static constexpr int VPLANE = HD * VTW * 2;  // bytes of one V^T plane
-    static constexpr int V_BYTES = ATT_WAVES * VPLANE * (KVB ? 1 : 2);
+    static constexpr int VPLANE = HD * VTW * 2;  // bytes of one V^T plane (BF16 caches)
+    static constexpr int V_BYTES = KVB ? ATT_WAVES * VPLANE : 0;
     static constexpr int LOOP = Q_BYTES + V_BYTES;
     static constexpr int ACC_BYTES = (ATT_WAVES - 1) * QT * DT * 64 * 16;
     static constexpr int ML_BYTES = ATT_WAVES * QT * 64 * 8;
@@ -60,13 +74,17 @@ struct AttnLds {
     static constexpr int BYTES = LOOP > MERGE ? LOOP : MERGE;
 };
 
-// Raw K/V rows of one 16-key sub-tile as a lane loads them: lane (r16, g) holds key
-// row r16, dims 32*st + 8g .. +7 of every 32-dim step st.
+// Raw K/V of one 16-key sub-tile as a lane (r16, g) loads it. K: key row r16, dims
+// 32*st + 8g .. +7 of every 32-dim step st (the A operand of the score product).
+// F32 V: already in the A-operand order of the P*V product, v[4*dt + j] = V[key
+// 4g + j][dim 16*dt + r16] (each load instruction reads 4 key rows x 64 contiguous
+// bytes). BF16 V: like K, transposed through LDS later.
 template <int HD, bool KVB>
 struct KvRaw;
 template <int HD>
 struct KvRaw<HD, false> {
-    float4 k[HD / 16], v[HD / 16];
+    float4 k[HD / 16];
+    float v[HD / 4];
 };
 template <int HD>
 struct KvRaw<HD, true> {
@@ -83,8 +101,10 @@ constexpr int attn_prefetch() {
 }
 
 template <int HD, bool KVB>
-__device__ __forceinline__ void attn_load(KvRaw<HD, KVB> &r, const AttnArgs &a, size_t head_off,
-                                          long long krow, int g) {
+__device__ __forceinline__ void attn_load_k(KvRaw<HD, KVB> &r, const AttnArgs &a, size_t head_off,
+                                            long long kb, long long n_all, int g, int r16) {
+    long long krow = kb + r16;  // rows past the last key re-read a valid row (masked later)
+    if (krow > n_all - 1) krow = n_all - 1;
 #pragma unroll
     for (int st = 0; st < HD / 32; st++) {
         const size_t off = head_off + (size_t)krow * HD + 32 * st + 8 * g;
@@ -93,41 +113,50 @@ __device__ __forceinline__ void attn_load(KvRaw<HD, KVB> &r, const AttnArgs &a, 
             r.v[st] = *(const uint4 *)((const uint16_t *)a.cache_v + off);
         } else {
             const float4 *kp = (const float4 *)((const float *)a.cache_k + off);
-            const float4 *vp = (const float4 *)((const float *)a.cache_v + off);
             r.k[2 * st] = kp[0];
             r.k[2 * st + 1] = kp[1];
-            r.v[2 * st] = vp[0];
-            r.v[2 * st + 1] = vp[1];
         }
     }
 }
 
-// K rows -> MFMA A operands (split hi/lo for F32), V rows -> this wave's V^T planes.
-template <int HD, bool KVB, int VTW>
-__device__ __forceinline__ void attn_convert(const KvRaw<HD, KVB> &r, bf16x8 *kh, bf16x8 *kl,
-                                             uint16_t *vth, uint16_t *vtl, int g, int r16) {
+// F32 V in the A-operand order of the P*V product (BF16 V comes with attn_load_k)
+template <int HD, bool KVB>
+__device__ __forceinline__ void attn_load_v(KvRaw<HD, KVB> &r, const AttnArgs &a, size_t head_off,
+                                            long long kb, long long n_all, int g, int r16) {
+    if constexpr (!KVB) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            long long vrow = kb + 4 * g + j;
+            if (vrow > n_all - 1) vrow = n_all - 1;
+            const float *vp = (const float *)a.cache_v + head_off + (size_t)vrow * HD + r16;
+#pragma unroll
+            for (int dt = 0; dt < HD / 16; dt++) r.v[4 * dt + j] = vp[16 * dt];
+        }
+    }
+}
+
+// BF16 V rows -> this wave's V^T plane (the A operand order of the P*V product)
+template <int HD, int VTW>
+__device__ __forceinline__ void attn_vt_store(const KvRaw<HD, true> &r, uint16_t *vth, int g, int r16) {
 #pragma unroll
     for (int st = 0; st < HD / 32; st++) {
         const int d0 = 32 * st + 8 * g;
-        if constexpr (KVB) {
-            kh[st] = __builtin_bit_cast(bf16x8, r.k[st]);
-            const uint32_t w4[4] = {r.v[st].x, r.v[st].y, r.v[st].z, r.v[st].w};
+        const uint32_t w4[4] = {r.v[st].x, r.v[st].y, r.v[st].z, r.v[st].w};
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                vth[(d0 + j) * VTW + r16] = (uint16_t)((j & 1) ? (w4[j >> 1] >> 16) : (w4[j >> 1] & 0xffffu));
-        } else {
-            const float4 k0 = r.k[2 * st], k1 = r.k[2 * st + 1];
-            const float4 v0 = r.v[2 * st], v1 = r.v[2 * st + 1];
-            const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            split8(kf, kh[st], kl[st]);
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const uint16_t hb = f32_to_bf16(vf[j]);
-                vth[(d0 + j) * VTW + r16] = hb;
-                vtl[(d0 + j) * VTW + r16] = f32_to_bf16(vf[j] - bf16_to_f32(hb));
-            }
-        }
+        for (int j = 0; j < 8; j++)
+            vth[(d0 + j) * VTW + r16] = (uint16_t)((j & 1) ? (w4[j >> 1] >> 16) : (w4[j >> 1] & 0xffffu));
+    }
+}
+
+// A operand(s) of the score product for 32-dim step st: BF16 K as is, F32 K split hi/lo
+template <int HD, bool KVB>
+__device__ __forceinline__ void attn_k_step(const KvRaw<HD, KVB> &r, int st, bf16x8 &kh, bf16x8 &kl) {
+    if constexpr (KVB) {
+        kh = __builtin_bit_cast(bf16x8, r.k[st]);
+    } else {
+        const float4 k0 = r.k[2 * st], k1 = r.k[2 * st + 1];
+        const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        split8(kf, kh, kl);
     }
 }
 
@@ -147,11 +176,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // A = 16 keys x 32 dims straight from the cache rows, B = pre-scaled queries split
 // hi/lo in LDS). That accumulator layout (lane: keys 4g..4g+3 of query l%16) is the
 // B operand of v_mfma_f32_16x16x16_bf16 for O^T[d][q] += V^T[d][key] P^T[key][q],
-// so the probabilities never leave their lanes; V is transposed through a V^T plane
-// private to the wave, so the key loop has no workgroup barrier. F32 caches are
-// split hi/lo (three products: hh, hl, lh); BF16 caches are exact (two products:
-// h*K, l*K). The K/V loads of the first sub-tiles are issued before the queries
-// are staged, so their latency overlaps the staging.
+// so the probabilities never leave their lanes. The V^T operand (4 keys x 1 dim per
+// lane) is loaded straight in that order for F32 caches and split in registers;
+// BF16 caches go through a V^T plane private to the wave. The key loop has no
+// workgroup barrier. F32 caches are split hi/lo (three products: hh, hl, lh); BF16
+// caches are exact (two products: h*K, l*K). The K/V loads of the first sub-tiles
+// are issued before the queries are staged, so their latency overlaps the staging.
 #ifndef DBF_ATT_WPE
 #define DBF_ATT_WPE 2
 #endif
@@ -165,8 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
 
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    uint16_t *vth = (uint16_t *)(smem + L::Q_BYTES + w * L::VPLANE * (KVB ? 1 : 2));
-    uint16_t *vtl = vth + HD * VTW;
+    uint16_t *vth = (uint16_t *)(smem + L::Q_BYTES + (KVB ? w * L::VPLANE : 0));  // BF16 caches
     const int r16 = lane & 15, g = lane >> 4;
     const int c = blockIdx.x, kvh = blockIdx.y;
     const int G = a.nq / a.nkv;
@@ -178,16 +207,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
     const long long k_lo = (long long)c * a.chunk + (long long)w * pw;
     const long long k_hi = k_lo + pw < c_hi ? k_lo + pw : c_hi;  // may be <= k_lo: wave idle
     const int n_sub = k_hi > k_lo ? (int)((k_hi - k_lo + ATT_KT - 1) / ATT_KT) : 0;
-    const float scale = 1.0f / sqrtf((float)HD);
+    // scores in log2 units: the queries carry log2(e)/sqrt(hd), so p = 2^(s - max)
+    const float scale = 1.4426950408889634f / sqrtf((float)HD);
     const size_t head_off = (size_t)kvh * a.capacity * HD;
 
     KvRaw<HD, KVB> rb[PF];
 #pragma unroll
     for (int u = 0; u < PF; u++) {
         if (u < n_sub) {
-            long long krow = k_lo + (long long)u * ATT_KT + r16;  // clamped to a valid row
-            if (krow > n_all - 1) krow = n_all - 1;
-            attn_load<HD, KVB>(rb[u], a, head_off, krow, g);
+            attn_load_k<HD, KVB>(rb[u], a, head_off, k_lo + (long long)u * ATT_KT, n_all, g, r16);
+            attn_load_v<HD, KVB>(rb[u], a, head_off, k_lo + (long long)u * ATT_KT, n_all, g, r16);
         }
     }
 
@@ -232,26 +261,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
             const int it = base + u;
             if (it >= n_sub) break;
             const long long kb = k_lo + (long long)it * ATT_KT;
-            bf16x8 kh[S], kl[S];
-            attn_convert<HD, KVB, VTW>(rb[u], kh, kl, vth, vtl, g, r16);
-            if (it + PF < n_sub) {
-                long long krow = kb + (long long)PF * ATT_KT + r16;
-                if (krow > n_all - 1) krow = n_all - 1;
-                attn_load<HD, KVB>(rb[u], a, head_off, krow, g);
-            }
+            if constexpr (KVB) attn_vt_store<HD, VTW>(rb[u], vth, g, r16);
+            const bool more = it + PF < n_sub;
+            const long long kb_next = kb + (long long)PF * ATT_KT;
             f32x4 sc[QT];
 #pragma unroll
-            for (int t = 0; t < QT; t++) {
-                sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < QT; t++) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int st = 0; st < S; st++) {
+            for (int st = 0; st < S; st++) {
+                bf16x8 kh, kl;
+                attn_k_step<HD, KVB>(rb[u], st, kh, kl);
+#pragma unroll
+                for (int t = 0; t < QT; t++) {
                     const bf16x8 qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
                     const bf16x8 ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
-                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], qh, sc[t], 0, 0, 0);
-                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[st], ql, sc[t], 0, 0, 0);
-                    if (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[st], qh, sc[t], 0, 0, 0);
+                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, sc[t], 0, 0, 0);
+                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql, sc[t], 0, 0, 0);
+                    if constexpr (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh, sc[t], 0, 0, 0);
                 }
             }
+            if (more) attn_load_k<HD, KVB>(rb[u], a, head_off, kb_next, n_all, g, r16);
             s16x4 ph[QT], pl[QT];
             float alpha[QT];
 #pragma unroll
@@ -271,40 +300,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
                 float al = 1.f, ps = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float p = m_new == -INFINITY ? 0.f : expf(v[i] - m_new);
+                    const float p = m_new == -INFINITY ? 0.f : exp2f(v[i] - m_new);
                     ps += p;
                     const __bf16 h = (__bf16)p;
                     ph[t][i] = __builtin_bit_cast(short, h);
                     pl[t][i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
                 }
-                if (m_new != -INFINITY) al = expf(m_run[t] - m_new);
+                if (m_new != -INFINITY) al = exp2f(m_run[t] - m_new);
                 ps += __shfl_xor(ps, 16, 64);
                 ps += __shfl_xor(ps, 32, 64);
                 l_run[t] = l_run[t] * al + ps;
                 m_run[t] = m_new;
                 alpha[t] = al;
             }
-            wave_lds_sync();  // V^T of this sub-tile written by every lane
+            if constexpr (KVB) wave_lds_sync();  // V^T of this sub-tile written by every lane
 #pragma unroll
             for (int d = 0; d < DT; d++) {
-                const int row = (16 * d + r16) * VTW + 4 * g;
-                const uint32_t *vr = (const uint32_t *)(vth + row);
-                const s16x4 vh = __builtin_bit_cast(s16x4, make_uint2(vr[0], vr[1]));
-                s16x4 vl;
-                if (!KVB) {
-                    const uint32_t *vq = (const uint32_t *)(vtl + row);
-                    vl = __builtin_bit_cast(s16x4, make_uint2(vq[0], vq[1]));
+                s16x4 va, vb;
+                if constexpr (KVB) {
+                    const uint32_t *vr = (const uint32_t *)(vth + (16 * d + r16) * VTW + 4 * g);
+                    va = __builtin_bit_cast(s16x4, make_uint2(vr[0], vr[1]));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float x = rb[u].v[4 * d + j];
+                        const __bf16 hx = (__bf16)x;
+                        va[j] = __builtin_bit_cast(short, hx);
+                        vb[j] = __builtin_bit_cast(short, (__bf16)(x - (float)hx));
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < QT; t++) {
                     f32x4 o = acc[t][d] * alpha[t];
-                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, ph[t], o, 0, 0, 0);
-                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, pl[t], o, 0, 0, 0);
-                    if (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vl, ph[t], o, 0, 0, 0);
+                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[t], o, 0, 0, 0);
+                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[t], o, 0, 0, 0);
+                    if constexpr (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, ph[t], o, 0, 0, 0);
                     acc[t][d] = o;
                 }
             }
-            wave_lds_sync();  // V^T reads done before the next sub-tile overwrites it
+            if constexpr (KVB) wave_lds_sync();  // V^T reads done before the next sub-tile overwrites it
+            if (more) attn_load_v<HD, KVB>(rb[u], a, head_off, kb_next, n_all, g, r16);
         }
     }
 
@@ -337,7 +372,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
         float e[ATT_WAVES], lsum = 0.f;
 #pragma unroll
         for (int v = 0; v < ATT_WAVES; v++) {
-            e[v] = lw[v] > 0.f ? expf(mw[v] - mx) : 0.f;
+            e[v] = lw[v] > 0.f ? exp2f(mw[v] - mx) : 0.f;
             lsum += lw[v] * e[v];
         }
         if (!qv[t]) continue;
@@ -423,12 +458,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
                 if (lv[j] > 0.f) bm = fmaxf(bm, mv[j]);
             const float mn = fmaxf(mr, bm);
             if (mn != -INFINITY) {
-                const float sc = lr > 0.f ? expf(mr - mn) : 0.f;
+                const float sc = lr > 0.f ? exp2f(mr - mn) : 0.f;
                 orun *= sc;
                 lr *= sc;
 #pragma unroll
                 for (int j = 0; j < CMB_BATCH; j++) {
-                    const float e = lv[j] > 0.f ? expf(mv[j] - mn) : 0.f;
+                    const float e = lv[j] > 0.f ? exp2f(mv[j] - mn) : 0.f;
                     orun += ov[j] * e;
                     lr += lv[j] * e;
                 }
@@ -449,7 +484,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
         float osum = 0.f, lsum = 0.f;
         for (int q = 0; q < ngrp; q++) {
             const float lq = sm_l[q * hd + d];
-            const float e = lq > 0.f ? expf(sm_m[q * hd + d] - mx) : 0.f;
+            const float e = lq > 0.f ? exp2f(sm_m[q * hd + d] - mx) : 0.f;
             osum += sm_o[q * hd + d] * e;
             lsum += lq * e;
         }

@@ -154,7 +154,9 @@ struct AttnArgs {
 };
 constexpr int ATT_PART_EXTRA = 4;  // partial record: acc[hd], m, l, 2 pad floats
 constexpr int ATT_CHUNKS_MAX = 256;
-void attn_plan(long long n_keys, int nq_per_wave, int *chunk, int *n_chunks);
+// groups: workgroups per chunk (kv heads x query tiles)
+void attn_plan(long long n_keys, int groups, int *chunk, int *n_chunks);
+void attn_plan_keys(long long n_keys, int keys_per_wave, int *chunk, int *n_chunks);
 int attn_qtiles(int hd, int nq_group);
 bool attn_supported(int hd);
 void launch_attn(const AttnArgs &a, hipStream_t s);
