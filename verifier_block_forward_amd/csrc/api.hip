@@ -93,8 +93,8 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     // stream faster with the activation slice in LDS and a deep weight ring; the
     // O, down and input projections with the plain split-K kernel.
     const int nbq = R > 0 ? 2 : 1;  // K/V also project the context rows
-    p.q = gemm_plan_lds(p.qt, p.H, 1, TARGET_UNITS / 4, nbq);
-    p.k = gemm_plan_lds(p.kt, p.H, 1, TARGET_UNITS / 4, nbq);
+    p.q = gemm_plan_lds(p.qt, p.H, 2, TARGET_UNITS / 4, nbq);
+    p.k = gemm_plan_lds(p.kt, p.H, 2, TARGET_UNITS / 4, nbq);
     p.v = p.k;
     p.g = p.q;
     p.o = gemm_plan(p.H, p.qt, na, TARGET_UNITS / 2);

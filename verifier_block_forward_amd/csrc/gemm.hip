@@ -177,12 +177,13 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
 // ---------------------------------------------------------------------------
 // Variant with the activation slice staged in LDS: the four waves of a workgroup
 // share (segment, k-slice) and own consecutive row tiles, so the slice's split
-// activations are copied into LDS once (one barrier) and each wave's registers
-// hold only weights: a deep ring of LPIPE stages keeps (LPIPE-1)*NA KiB of weight
-// loads in flight per wave, which the short split-K slices of the per-layer
-// projections need to cover the ~4 us loaded memory latency.
+// activations are read once per workgroup (not once per wave) and each wave's
+// registers hold only weights, in a ring of LPIPE stages. A launch of these
+// kernels asks for tens of MB at once; the ring is kept short (3 stages measured
+// best on MI355X) because more requests in flight only lengthen the queue that
+// the activation loads, which gate the first product, wait in.
 #ifndef DBF_LPIPE
-#define DBF_LPIPE 6
+#define DBF_LPIPE 3
 #endif
 constexpr int LPIPE = DBF_LPIPE;
 constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
@@ -255,23 +256,36 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
             wb[u][a] = in_ ? v_ : zero8();                                      \
         }                                                                       \
     } while (0)
-    // the weight stream starts before the activation slice is staged
-#pragma unroll
-    for (int u = 0; u < LPIPE; u++) DBF_LOAD_W(u, s0 + u);
-    // stage the activation slice: per tile, steps [s0, s1) are contiguous (2 KiB each)
+    // Stage the activation slice (per tile, steps [s0, s1) are contiguous, 2 KiB each):
+    // this thread's share is loaded first, the weight ring is issued behind it, and
+    // only then is the share stored, so the store waits for the activation loads
+    // alone (loads complete in issue order) while the weight loads are in flight.
+    constexpr int XPT = LDS_X_BYTES / 16 / 256;  // uint4 per thread at most
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // register-friendly
+    u32x4 xr[XPT];
+    const int per = n * 128;  // uint4 per tile
+    const int xtot = (NB > 1 && nb > 1) ? 2 * per : per;
     {
         const uint4 *src0 = (const uint4 *)(xsb0 + (size_t)s0 * 2 * 64 * 8);
-        const int per = n * 128;  // uint4 per tile
-        for (int i = threadIdx.x; i < per; i += 256) xl[i] = src0[i];
-        if (NB > 1 && nb > 1) {
-            const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
-            for (int i = threadIdx.x; i < per; i += 256) xl[per + i] = src1[i];
+        const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
+#pragma unroll
+        for (int q = 0; q < XPT; q++) {
+            const int i = threadIdx.x + 256 * q;
+            const int ic = i < xtot ? i : xtot - 1;  // always a valid address
+            const uint4 *sp = ic < per ? src0 + ic : src1 + (ic - per);  // pointer select
+            xr[q] = *(const u32x4 *)sp;
         }
+    }
+#pragma unroll
+    for (int u = 0; u < LPIPE; u++) DBF_LOAD_W(u, s0 + u);
+#pragma unroll
+    for (int q = 0; q < XPT; q++) {
+        const int i = threadIdx.x + 256 * q;
+        if (i < xtot) *(u32x4 *)&xl[i] = xr[q];
     }
     __syncthreads();
     if (tile >= sg.tiles) return;
 
-    const int per = n * 128;
     for (int base = 0; base < n; base += LPIPE) {
 #pragma unroll
         for (int u = 0; u < LPIPE; u++) {
