@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--row-major", action="store_true",
                     help="keep projection weights row-major instead of the tiled layout")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step captured in a HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after the timed region (counter scale)")
     args = ap.parse_args()
@@ -187,6 +189,30 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value = M * args.steps / wall
 
+    # The same step captured in a HIP graph and replayed (kv_rollback is host-side
+    # metadata: every replay rewrites the same cache rows, as the eager step does
+    # after its rollback).
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            dbf.draft_block_forward(ccfg, bw, kv, io, ws, cs)
+            dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, cs)
+            dbf.accept_prefix(drafts, target, result, stream=cs)
+        dbf.kv_rollback(kv, R + M)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del g
+
     # plain copy of known size after the timed region: the reference dispatch that
     # scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes
     if args.copy_probe_mib > 0:
@@ -235,6 +261,8 @@ def main():
                   "ms_draft_block_forward": round(float(np.mean(block_ms)), 4),
                   "ms_lm_head_argmax": round(head_avg, 4),
                   "ms_accept_prefix": round(float(np.mean(acc_ms)), 4),
+                  "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
+                  "graph_rows_per_s": round(M / (graph_ms * 1e-3), 1) if graph_ms else None,
                   "accept_result": result.cpu().tolist()},
         "cpu_baseline": cpu,
     }

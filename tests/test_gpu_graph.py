@@ -1,0 +1,71 @@
+"""HIP graph capture of one whole hot-path step: draft_block_forward, lm_head_argmax
+and accept_prefix enqueue on one stream, with no host synchronisation and no
+memsets, so the step can be captured and replayed. Every replay, with eager
+device work and synchronisations between replays, must reproduce the eager step
+bit for bit (the kernels are deterministic: fixed reduction orders, no float
+atomics). A replay rewrites the same cache rows, which is what the eager step does
+after kv_rollback(R + M).
+"""
+import numpy as np
+import pytest
+
+from verifier_block_forward_amd import configs, synth
+from tests.gpu_harness import Prepared, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c0", "c4m4"])
+def test_graph_replay_matches_eager(name):
+    from verifier_block_forward_amd import dbf
+    t = torch()
+    cfg = configs.get(name)
+    print(f"\n[graph] {name}", flush=True)
+    P = Prepared(cfg, tiled=True)
+    M, R, H, V = cfg.M, cfg.R, cfg.hidden, cfg.vocab
+    ck, cv = P.fresh_cache()
+    kv = dbf.make_cache(ck, cv, P.in_host["seq_len"])
+    h_final = t.empty((M, H), dtype=t.float32, device="cuda")
+    hidden_out = t.empty((M, H), dtype=t.float32, device="cuda")
+    argmax = t.empty(M, dtype=t.int32, device="cuda")
+    margin = t.empty(M, dtype=t.float32, device="cuda")
+    result = t.zeros(5, dtype=t.int32, device="cuda")
+    ws_head = t.empty(dbf.lm_head_argmax_workspace_bytes(M, H, V), dtype=t.uint8, device="cuda")
+    io = dbf.make_io(M, R, h_final, tokens=P.inp.get("tokens"), x0=P.inp.get("x0"),
+                     ctx=P.inp.get("ctx"), hidden_out=hidden_out)
+    K = cfg.K
+    drafts = argmax[1:] if cfg.kind == "dflash" else argmax[:1]
+    target_np, _ = synth.accept_targets(np.arange(K, dtype=np.int32), V, cfg.seed)
+    target = t.from_numpy(target_np).cuda()
+    lm_head = P.w_dev["lm_head"]
+
+    def step(stream):
+        dbf.draft_block_forward(P.ccfg, P.bw, kv, io, P.ws, stream)
+        dbf.lm_head_argmax(h_final, lm_head, argmax, None, margin, ws_head, stream)
+        dbf.accept_prefix(drafts, target, result, stream=stream)
+
+    outs = (h_final, hidden_out, argmax, margin, result, ck, cv)
+    step(t.cuda.current_stream())
+    dbf.kv_rollback(kv, R + M)
+    t.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step(t.cuda.current_stream())
+    dbf.kv_rollback(kv, R + M)  # capture advanced the host-side seq_len
+    assert kv.seq_len == P.in_host["seq_len"]
+
+    for rep in range(3):
+        junk = t.randn(4096, device="cuda")
+        float((junk * 2).sum().item())  # eager work and a sync between replays
+        h_final.fill_(float("nan"))
+        hidden_out.fill_(float("nan"))
+        argmax.fill_(-1)
+        margin.fill_(float("nan"))
+        result.fill_(-7)
+        g.replay()
+        t.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(outs, ref)):
+            assert t.equal(got, want), f"{name}: replay {rep}, output {i} differs from the eager step"
+        print(f"  replay {rep}: bitwise equal", flush=True)
