@@ -63,9 +63,9 @@ __device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo) {
 
 template <int HD, int QT, bool KVB>
 struct AttnLds {
-    static constexpr int S = HD / 32, DT = HD / 16, VTW = 22;
+    static constexpr int S = HD / 32, DT = HD / 16, VTW = HD + 8;  // V row pitch (elements)
     static constexpr int Q_BYTES = QT * S * 2 * 64 * 16;
-    static constexpr int VPLANE = HD * VTW * 2;  // bytes of one V^T plane (BF16 caches)
+    static constexpr int VPLANE = ATT_KT * VTW * 2;  // bytes of one wave's V rows (BF16 caches)
     static constexpr int V_BYTES = KVB ? ATT_WAVES * VPLANE : 0;
     static constexpr int LOOP = Q_BYTES + V_BYTES;
     static constexpr int ACC_BYTES = (ATT_WAVES - 1) * QT * DT * 64 * 16;
@@ -135,17 +135,26 @@ __device__ __forceinline__ void attn_load_v(KvRaw<HD, KVB> &r, const AttnArgs &a
     }
 }
 
-// BF16 V rows -> this wave's V^T plane (the A operand order of the P*V product)
+// BF16 V rows -> this wave's LDS rows, as loaded: row r16 holds key r16, pitch VTW
+// elements (HD + 8: the 16 rows of a transposed read then fall on different banks).
 template <int HD, int VTW>
-__device__ __forceinline__ void attn_vt_store(const KvRaw<HD, true> &r, uint16_t *vth, int g, int r16) {
+__device__ __forceinline__ void attn_v_store(const KvRaw<HD, true> &r, uint16_t *vrows, int g, int r16) {
 #pragma unroll
-    for (int st = 0; st < HD / 32; st++) {
-        const int d0 = 32 * st + 8 * g;
-        const uint32_t w4[4] = {r.v[st].x, r.v[st].y, r.v[st].z, r.v[st].w};
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-            vth[(d0 + j) * VTW + r16] = (uint16_t)((j & 1) ? (w4[j >> 1] >> 16) : (w4[j >> 1] & 0xffffu));
-    }
+    for (int st = 0; st < HD / 32; st++)
+        *(uint4 *)(vrows + r16 * VTW + 32 * st + 8 * g) = r.v[st];
+}
+
+// The A operand of the P*V product for dims 16*dt..+15, read transposed out of the
+// V rows with ds_read_b64_tr_b16 (gfx950). Within each 16-lane group that read
+// hands lane i, element j, element i%4 of the 8-byte chunk addressed by lane
+// 4j + i/4; so lane (i, g) addresses key 4g + i/4, dims 16*dt + 4*(i%4) .. +3, and
+// receives V[4g + j][16*dt + i] for j = 0..3: keys 4g..4g+3 of dim i (layout checked
+// with a probe on MI355X).
+typedef short s16x4_lds __attribute__((ext_vector_type(4)));
+template <int VTW>
+__device__ __forceinline__ s16x4_lds attn_v_operand(const uint16_t *vrows, int dt, int g, int r16) {
+    const uint16_t *p = vrows + (4 * g + (r16 >> 2)) * VTW + 16 * dt + 4 * (r16 & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_lds *)p);
 }
 
 // A operand(s) of the score product for 32-dim step st: BF16 K as is, F32 K split hi/lo
@@ -178,7 +187,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // B operand of v_mfma_f32_16x16x16_bf16 for O^T[d][q] += V^T[d][key] P^T[key][q],
 // so the probabilities never leave their lanes. The V^T operand (4 keys x 1 dim per
 // lane) is loaded straight in that order for F32 caches and split in registers;
-// BF16 caches go through a V^T plane private to the wave. The key loop has no
+// BF16 caches store the V rows in LDS (a region private to the wave) and read the
+// operand back transposed with ds_read_b64_tr_b16. The key loop has no
 // workgroup barrier. F32 caches are split hi/lo (three products: hh, hl, lh); BF16
 // caches are exact (two products: h*K, l*K). The K/V loads of the first sub-tiles
 // are issued before the queries are staged, so their latency overlaps the staging.
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
             const int it = base + u;
             if (it >= n_sub) break;
             const long long kb = k_lo + (long long)it * ATT_KT;
-            if constexpr (KVB) attn_vt_store<HD, VTW>(rb[u], vth, g, r16);
+            if constexpr (KVB) attn_v_store<HD, VTW>(rb[u], vth, g, r16);
             const bool more = it + PF < n_sub;
             const long long kb_next = kb + (long long)PF * ATT_KT;
             f32x4 sc[QT];
@@ -313,13 +323,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
                 m_run[t] = m_new;
                 alpha[t] = al;
             }
-            if constexpr (KVB) wave_lds_sync();  // V^T of this sub-tile written by every lane
+            if constexpr (KVB) wave_lds_sync();  // V rows of this sub-tile written by every lane
 #pragma unroll
             for (int d = 0; d < DT; d++) {
                 s16x4 va, vb;
                 if constexpr (KVB) {
-                    const uint32_t *vr = (const uint32_t *)(vth + (16 * d + r16) * VTW + 4 * g);
-                    va = __builtin_bit_cast(s16x4, make_uint2(vr[0], vr[1]));
+                    va = attn_v_operand<VTW>(vth, d, g, r16);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
                     acc[t][d] = o;
                 }
             }
-            if constexpr (KVB) wave_lds_sync();  // V^T reads done before the next sub-tile overwrites it
+            if constexpr (KVB) wave_lds_sync();  // V reads done before the next sub-tile overwrites them
             if (more) attn_load_v<HD, KVB>(rb[u], a, head_off, kb_next, n_all, g, r16);
         }
     }
