@@ -145,8 +145,10 @@ typedef struct {
 } dbf_kv_cache;
 
 /* Block inputs/outputs (device pointers).
- *   tokens      [M] int32 or NULL. DFlash only: rows are embed[tokens[i]]
- *               ([ORCH] per-round steps 1-2: [last_token, mask x K]). Ids are
+ *   tokens      [M] int32 or NULL. Rows are embed[tokens[i]]: DFlash block
+ *               rows ([ORCH] per-round steps 1-2: [last_token, mask x K]); MTP
+ *               embed_t, the embedding of the token a chained step drafts from
+ *               (the previous step's argmax, read on the device). Ids are
  *               clamped into [0, V).
  *   x0          [M, H] F32 block rows when tokens == NULL (MTP: embed_t).
  *   ctx         DFlash: [R, n_t*H] F32 concatenated target hidden states of the R

@@ -342,7 +342,8 @@ static void moe_ffn(const orc_cfg *c, const orc_layer *lw, const double *x, int 
  *          hidden_norm) over the R new context rows ([TENS] `DFlashModelTensors`:
  *          fc and hidden_norm; [ORCH] per-round loop, steps 1-4, new rows only).
  *          MTP: x = RMSNorm(e, enorm, 1e-6) ehE^T + RMSNorm(h, hnorm, 1e-6) ehH^T
- *          ([MTP] `project_embedding_and_hidden`; eps fixed at 1e-6 there).
+ *          ([MTP] `project_embedding_and_hidden`; eps fixed at 1e-6 there), e the
+ *          given embed_t or, for a chained step, embed[token].
  *  layer   ([MTP] `forward_full_attention`, `forward_ffn_residual`)
  *          xh = RMSNorm(x, in_norm); q = xh Wq^T, k = xh Wk^T, v = xh Wv^T,
  *          g = xh Wg^T (if gated); per-head RMSNorm of q and k; RoPE at each
@@ -394,10 +395,14 @@ int orc_block_forward(const orc_cfg *c, const orc_weights *w, orc_cache *kv, con
         double *hn = (double *)malloc(sizeof(double) * (size_t)M * H);
         double *pe = (double *)malloc(sizeof(double) * (size_t)M * H);
         double *ph = (double *)malloc(sizeof(double) * (size_t)M * H);
-        for (size_t i = 0; i < (size_t)M * H; i++) {
-            e[i] = (double)io->x0[i];
-            hp[i] = (double)io->ctx[i];
-        }
+        /* embed_t: given, or the embedding row of the token a chained step drafts
+         * from (the target's shared embedding, as for DFlash block rows) */
+        for (int m = 0; m < M; m++)
+            for (int h = 0; h < H; h++) {
+                const size_t i = (size_t)m * H + h;
+                e[i] = io->tokens ? bf(w->embed[(size_t)io->tokens[m] * H + h]) : (double)io->x0[i];
+                hp[i] = (double)io->ctx[i];
+            }
         for (int m = 0; m < M; m++) {
             orc_rmsnorm(e + (size_t)m * H, w->enorm, H, 1e-6, en + (size_t)m * H);
             orc_rmsnorm(hp + (size_t)m * H, w->hnorm, H, 1e-6, hn + (size_t)m * H);

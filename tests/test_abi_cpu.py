@@ -71,6 +71,25 @@ def test_block_argument_errors():
     assert _call_block(_cfg(hidden=260), dbf.BlockIO(M=4, R=0, h_final=h, x0=h))[0] == dbf.ESHAPE
     mtp = _cfg("c2")
     assert _call_block(mtp, dbf.BlockIO(M=1, R=1, h_final=h, x0=h, ctx=h))[0] == dbf.EINVAL
+    # MTP needs embed_t as rows (x0) or as token ids to gather
+    assert _call_block(mtp, dbf.BlockIO(M=1, R=0, h_final=h, ctx=h))[0] == dbf.EINVAL
+    assert "neither tokens nor x0" in dbf.last_error()
+
+
+def test_token_input_needs_the_embedding_table():
+    """Token ids (DFlash block rows, or a chained MTP step's embed_t) are gathered
+    from embed; without a valid embed tensor the call is refused before any launch."""
+    bc = configs.C0
+    cfg = dbf.make_config(bc)
+    w, _ = _weights_for(bc)
+    w.embed = dbf.Tensor()  # absent
+    rc, cache = _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=0x4000, tokens=0x4000), w=w)
+    assert rc in (dbf.EINVAL, dbf.ESHAPE) and "embed" in dbf.last_error()
+    assert cache.seq_len == 10
+    w, _ = _weights_for(bc)
+    w.embed.dtype = dbf.BF16_T16  # the gather reads rows: row-major only
+    rc, _ = _call_block(cfg, dbf.BlockIO(M=4, R=0, h_final=0x4000, tokens=0x4000), w=w)
+    assert rc == dbf.EDTYPE and "embed" in dbf.last_error()
 
 
 def _weights_for(bc, dtype_override=None):

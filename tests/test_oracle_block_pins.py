@@ -269,3 +269,22 @@ def test_capacity_overflow_rejected(orc):
     w, inp = data(cfg)
     with pytest.raises(RuntimeError):
         run(orc, cfg, w, inp, seq_len=cfg.C + 1)
+
+
+def test_mtp_token_input_is_the_embedding_row(orc):
+    """A chained MTP step takes embed_t as the embedding row of its token: the same
+    block with tokens equals the block with x0 = decode(embed[tokens]) exactly, and
+    differs from it once any token changes."""
+    cfg = tiny(name="tiny_mtp_tok", kind="mtp", R=0, M=2, n_layers=1, n_target_hidden=0,
+               has_attn_gate=True, block_input="tokens")
+    w, inp = data(cfg)
+    toks = np.array([5, 63], np.int32)
+    by_tok = dict(inp, tokens=toks)
+    by_x0 = {k: v for k, v in inp.items() if k != "tokens"}
+    by_x0["x0"] = _dec(w["embed"][toks]).astype(np.float32)
+    a = run(orc, cfg, w, by_tok)
+    b = run(orc, cfg, w, by_x0)
+    assert np.array_equal(a["h_final"], b["h_final"])
+    assert np.array_equal(a["hidden_out"], b["hidden_out"])
+    c = run(orc, cfg, w, dict(inp, tokens=np.array([6, 63], np.int32)))
+    assert not np.allclose(c["h_final"][0], a["h_final"][0])

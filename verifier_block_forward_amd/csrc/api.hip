@@ -255,13 +255,13 @@ int validate_weights(const dbf_config &c, const dbf_weights *w, bool need_embed)
     if (!w) return fail(DBF_EINVAL, "weights are null");
     const int H = c.hidden, qt = c.n_q_heads * c.head_dim, kt = c.n_kv_heads * c.head_dim;
     const int hd = c.head_dim;
+    if (need_embed) {
+        CHECK(check_t(w->embed, "embed", DBF_BF16, 2, c.vocab, H));
+        if (w->embed.dtype != DBF_BF16) return fail(DBF_EDTYPE, "embed must be row-major BF16");
+    }
     if (c.kind == DBF_KIND_DFLASH) {
         CHECK(check_t(w->fc, "fc", DBF_BF16, 2, H, (int64_t)c.n_target_hidden * H));
         CHECK(check_t(w->hidden_norm, "hidden_norm", DBF_F32, 1, H));
-        if (need_embed) {
-            CHECK(check_t(w->embed, "embed", DBF_BF16, 2, c.vocab, H));
-            if (w->embed.dtype != DBF_BF16) return fail(DBF_EDTYPE, "embed must be row-major BF16");
-        }
     } else {
         CHECK(check_t(w->enorm, "enorm", DBF_F32, 1, H));
         CHECK(check_t(w->hnorm, "hnorm", DBF_F32, 1, H));
@@ -346,10 +346,10 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         if (!io->tokens && !io->x0) return fail(DBF_EINVAL, "io: neither tokens nor x0 given");
         if (R > 0 && !io->ctx) return fail(DBF_EINVAL, "io.ctx is null with R = %d", R);
     } else {
-        if (!io->x0) return fail(DBF_EINVAL, "io.x0 (embed_t) is null");
+        if (!io->tokens && !io->x0) return fail(DBF_EINVAL, "io: neither tokens nor x0 (embed_t) given");
         if (!io->ctx) return fail(DBF_EINVAL, "io.ctx (prev_hidden) is null");
     }
-    CHECK(validate_weights(c, w, c.kind == DBF_KIND_DFLASH && io->tokens));
+    CHECK(validate_weights(c, w, io->tokens != nullptr));
     if (!cache || !cache->k || !cache->v) return fail(DBF_EINVAL, "cache or its buffers are null");
     if (cache->dtype != DBF_F32 && cache->dtype != DBF_BF16)
         return fail(DBF_EDTYPE, "cache dtype %s (F32 or BF16)", dtname(cache->dtype));
@@ -434,6 +434,9 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         float *ssp_e = at<float>(ws, p.ssp_e), *ssp_h = at<float>(ws, p.ssp_h);
         ColArgs e = col();
         e.M = M;
+        e.tokens = io->tokens;  // chained steps: embed_t = embed[token]
+        e.embed = (const uint16_t *)w->embed.data;
+        e.V = c.vocab;
         e.base = io->x0;
         e.ldb = H;
         e.w = (const float *)w->enorm.data;
@@ -441,6 +444,8 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         e.ssp_out = ssp_e;
         launch_colsum(e, st);
         ColArgs h = e;
+        h.tokens = nullptr;  // prev_hidden rows are given, never gathered
+        h.embed = nullptr;
         h.base = io->ctx;
         h.w = (const float *)w->hnorm.data;
         h.xs = xs_h;
