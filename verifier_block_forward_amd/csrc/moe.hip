@@ -146,18 +146,22 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
     const int Ip = (I + 31) & ~31;
     float h = 0.f;
     if (m < a.M) {
-        // whole wave (wave-uniform m) forms the row scale before any lane drops out
+        float g = 0.f, u = 0.f;
+        if (k < I) {  // partial loads first; the row scale forms while they arrive
+            const float *pg = shared ? a.psg : a.pg + (size_t)slot * a.ks * 16 * I;
+            const float *pu = shared ? a.psu : a.pu + (size_t)slot * a.ks * 16 * I;
+            const size_t off = (size_t)m * I + k;
+            const float *b[2] = {pg + off, pu + off};
+            float o[2];
+            sum_partials_n<2>(b, shared ? a.ks_sh : a.ks, (size_t)16 * I, o);
+            g = o[0];
+            u = o[1];
+        }
+        // whole wave (wave-uniform m) forms the row scale: no lane has left yet
         const float s = moe_row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
         if (k < I) {
-            float g, u;
-            if (shared) {
-                g = s * sum_partials(a.psg, a.ks_sh, 16, I, m, k);
-                u = s * sum_partials(a.psu, a.ks_sh, 16, I, m, k);
-            } else {
-                const size_t so = (size_t)slot * a.ks * 16 * I;
-                g = s * sum_partials(a.pg + so, a.ks, 16, I, m, k);
-                u = s * sum_partials(a.pu + so, a.ks, 16, I, m, k);
-            }
+            g *= s;
+            u *= s;
             h = g / (1.0f + expf(-g)) * u;
         }
     }

@@ -38,6 +38,11 @@ __global__ __launch_bounds__(256) void k_colsum(ColArgs a) {
     const bool ok = row_ok && k < a.H;
     float v = 0.f;
     if (row_ok) {
+        // the partial sums' loads go out first; the row scales (a wave reduction of
+        // the norm partials) are formed while they are in flight
+        float s0 = 0.f, s1 = 0.f;
+        if (ok && a.p0) s0 = sum_partials(a.p0, a.ks0, a.rows0, a.H, m, k);
+        if (ok && a.p1) s1 = sum_partials(a.p1, a.ks1, a.rows1, a.H, m, k);
         float sc0 = 1.f, sc1 = 1.f;
         if (a.p0 && a.ssp0) sc0 = row_scale(a.ssp0 + (size_t)m * a.ncb_in, a.ncb_in, a.H, a.eps0);
         if (a.p1 && a.ssp1) sc1 = row_scale(a.ssp1 + (size_t)m * a.ncb_in, a.ncb_in, a.H, a.eps1);
@@ -49,8 +54,8 @@ __global__ __launch_bounds__(256) void k_colsum(ColArgs a) {
             } else if (a.base) {
                 v = a.base[(size_t)m * a.ldb + k];
             }
-            if (a.p0) v += sc0 * sum_partials(a.p0, a.ks0, a.rows0, a.H, m, k);
-            if (a.p1) v += sc1 * sum_partials(a.p1, a.ks1, a.rows1, a.H, m, k);
+            if (a.p0) v += sc0 * s0;
+            if (a.p1) v += sc1 * s1;
             if (a.out) a.out[(size_t)m * a.H + k] = v;
             if (a.copy0) a.copy0[(size_t)m * a.H + k] = v;
             if (a.copy1) a.copy1[(size_t)m * a.H + k] = v;
@@ -109,14 +114,14 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
     const bool isq = b < a.M * a.nq;
     int row, head;         // row within its group (block rows or all kv rows), head index
     long long pos;
-    float s;               // RMSNorm scale of the source row
+    const float *sspr;     // norm partials of the source row (its RMSNorm scale)
     const float *src, *src2, *wn;  // partials of the head and of its gate / value, head-norm weight
     int ks, ks2, prow, N, rows;
     if (isq) {
         row = b / a.nq;
         head = b % a.nq;
         pos = a.P0 + a.R + row;
-        s = row_scale(a.ssp_x + (size_t)row * a.ncb, a.ncb, a.H, a.eps);
+        sspr = a.ssp_x + (size_t)row * a.ncb;
         src = a.pq;
         ks = a.ksq;
         src2 = a.pg;
@@ -132,8 +137,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
         const bool ctx = row < a.R;
         const int m = ctx ? row : row - a.R;
         pos = ctx ? a.P0 + row : a.P0 + a.R + m;
-        s = ctx ? row_scale(a.ssp_ctx + (size_t)m * a.ncb, a.ncb, a.H, a.eps)
-                : row_scale(a.ssp_x + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
+        sspr = (ctx ? a.ssp_ctx : a.ssp_x) + (size_t)m * a.ncb;
         src = a.pk;
         ks = a.ksk;
         src2 = a.pv;
@@ -171,6 +175,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
             sum_partials_n<CPL>(bb, ks2, stride, side);
         }
     }
+    const float s = row_scale(sspr, a.ncb, a.H, a.eps);  // while the partials arrive
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; i++) {
@@ -232,10 +237,24 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
     const int Ip = (a.I + 31) & ~31;
     float h = 0.f;
     if (m < a.M) {
+        float g = 0.f, u = 0.f;
+        if (k < a.I) {  // partial loads first, row scale while they are in flight
+            if (a.ksg == a.ksu) {
+                const size_t off = (size_t)m * a.I + k;
+                const float *b[2] = {a.pg + off, a.pu + off};
+                float o[2];
+                sum_partials_n<2>(b, a.ksg, (size_t)16 * a.I, o);
+                g = o[0];
+                u = o[1];
+            } else {
+                g = sum_partials(a.pg, a.ksg, 16, a.I, m, k);
+                u = sum_partials(a.pu, a.ksu, 16, a.I, m, k);
+            }
+        }
         const float s = row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
         if (k < a.I) {
-            const float g = s * sum_partials(a.pg, a.ksg, 16, a.I, m, k);
-            const float u = s * sum_partials(a.pu, a.ksu, 16, a.I, m, k);
+            g *= s;
+            u *= s;
             h = g / (1.0f + expf(-g)) * u;
         }
     }
