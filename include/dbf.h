@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DBF_ABI_VERSION 1
+#define DBF_ABI_VERSION 2
 
 /* status codes */
 #define DBF_OK 0
@@ -68,7 +68,12 @@ extern "C" {
 #define DBF_FFN_DENSE 0
 #define DBF_FFN_MOE 1
 
+/* block attention masks */
+#define DBF_MASK_CAUSAL 0 /* block row i sees block rows <= i (the spec reading) */
+#define DBF_MASK_BIDIR 1  /* every block row sees all M block rows (block-diffusion reading) */
+
 #define DBF_MAX_M 16   /* block rows per call (K+1 <= 16) */
+#define DBF_MAX_CTX_LAYERS 8 /* captured target layers gathered on the device */
 #define DBF_MAX_R 16   /* new context rows per call */
 #define DBF_MAX_TOPK 16
 
@@ -99,6 +104,8 @@ typedef struct {
     int32_t expert_intermediate; /* MoE: per-expert SwiGLU width */
     int32_t shared_intermediate; /* MoE: shared-expert SwiGLU width */
     int32_t has_attn_gate;   /* 1: o *= sigmoid(x Wg^T) before O ([MTP] `w_gate`) */
+    int32_t block_mask;      /* DBF_MASK_CAUSAL (default) | DBF_MASK_BIDIR */
+    int32_t reserved_;       /* zero */
     double rms_eps;          /* RMSNorm eps of every norm except MTP enorm/hnorm (fixed 1e-6) */
     double rope_theta;       /* RoPE base */
 } dbf_config;
@@ -152,8 +159,18 @@ typedef struct {
  *               clamped into [0, V).
  *   x0          [M, H] F32 block rows when tokens == NULL (MTP: embed_t).
  *   ctx         DFlash: [R, n_t*H] F32 concatenated target hidden states of the R
- *               new context rows (may be NULL when R == 0).
- *               MTP: prev_hidden [M, H] F32 (required).
+ *               new context rows (may be NULL when R == 0, or when ctx_layers is
+ *               given). MTP: prev_hidden [M, H] F32 (required).
+ *   ctx_layers  DFlash, optional: HOST array of n_t device pointers, the target's
+ *               captured hidden rows of each drafter target layer, [*, ctx_ld] F32
+ *               indexed by position. The R context rows are gathered on the
+ *               device: row r = concat_t ctx_layers[t][(ctx_row0 + r) * ctx_ld ..
+ *               + H) ([ORCH] per-round step 3, `extract_drafter_concat`, new rows
+ *               only, without its host copy). With buffers indexed by position,
+ *               accepted verify positions need no append: the next round gathers
+ *               them where the target wrote them. n_t <= DBF_MAX_CTX_LAYERS.
+ *   ctx_ld      row stride of every ctx_layers buffer, elements (>= H).
+ *   ctx_row0    position of the first new context row in ctx_layers.
  *   M           block rows, 1..DBF_MAX_M.  R: new context rows, 0..DBF_MAX_R
  *               (MTP: must be 0).
  *   hidden_out  [M, H] F32 pre-norm hidden of the last layer, or NULL.
@@ -167,6 +184,9 @@ typedef struct {
     float *hidden_out;
     float *h_final;
     float *layer_hidden;
+    const float *const *ctx_layers;
+    int64_t ctx_ld;
+    int64_t ctx_row0;
 } dbf_block_io;
 
 /* Drafter block forward ([MTP] `forward_draft_with_hidden` and its helpers
@@ -180,7 +200,8 @@ typedef struct {
  * Each layer: RMSNorm, Q/K/V (+gate) projections, per-head RMSNorm of q and k,
  * RoPE, K/V stored in the cache, GQA attention (q head h uses kv head
  * h*nkv/nq) over cache rows [0, P0+R+i] for block row i (causal within the
- * block), optional sigmoid gate, O projection + residual, RMSNorm, SwiGLU or
+ * block; with cfg.block_mask == DBF_MASK_BIDIR over [0, P0+R+M), every block
+ * row), optional sigmoid gate, O projection + residual, RMSNorm, SwiGLU or
  * MoE FFN + residual. Then h_final = RMSNorm(x, final_norm).
  * DFlash context rows go through each layer's wk/wv, k_norm and RoPE (no input
  * norm) and are stored at positions P0..P0+R-1; block rows at P0+R+i, where P0 =

@@ -167,7 +167,7 @@ typedef struct {
     int32_t ffn_moe, n_experts, top_k, expert_intermediate, shared_intermediate;
     int32_t has_gate;
     int32_t kv_bf16;
-    int32_t pad_;
+    int32_t block_bidir; /* 1: every block row attends to all M block rows */
     double eps, theta;
 } orc_cfg;
 
@@ -354,6 +354,8 @@ static void moe_ffn(const orc_cfg *c, const orc_layer *lw, const double *x, int 
  *          pages): the context rows h_ctx go through each layer's Wk/Wv, k_norm and
  *          RoPE with no input norm and sit at positions P0..P0+R-1; block row i
  *          sits at P0+R+i and attends causally to cache rows [0, P0+R+i].
+ *          With block_bidir (the block-diffusion reading of the in-block mask)
+ *          every block row attends to cache rows [0, P0+R+M): all M block rows.
  *  output  hidden_out = x; h_final = RMSNorm(x, final_norm) ([MTP]
  *          `forward_shared_head`; [TENS] final `norm`).
  *
@@ -473,7 +475,7 @@ int orc_block_forward(const orc_cfg *c, const orc_weights *w, orc_cache *kv, con
             for (int t = 0; t < M * nq; t++) {
                 int m = t / nq, h = t % nq;
                 int kvh = (int)(((int64_t)h * nkv) / nq);
-                int64_t n = P0 + R + m + 1;
+                int64_t n = c->block_bidir ? P0 + R + M : P0 + R + m + 1;
                 for (int64_t j = 0; j < n; j++)
                     for (int d = 0; d < hd; d++) {
                         keys[(size_t)j * hd + d] = cache_load(c, kv, 0, l, kvh, j, d);

@@ -42,7 +42,7 @@ class OrcCfg(C.Structure):
                 ("n_target_hidden", C.c_int32), ("vocab", C.c_int32), ("ffn_moe", C.c_int32),
                 ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("expert_intermediate", C.c_int32), ("shared_intermediate", C.c_int32),
-                ("has_gate", C.c_int32), ("kv_bf16", C.c_int32), ("pad_", C.c_int32),
+                ("has_gate", C.c_int32), ("kv_bf16", C.c_int32), ("block_bidir", C.c_int32),
                 ("eps", C.c_double), ("theta", C.c_double)]
 
 
@@ -177,7 +177,8 @@ def make_cfg(cfg) -> OrcCfg:
                   top_k=cfg.top_k, expert_intermediate=cfg.expert_intermediate,
                   shared_intermediate=cfg.shared_intermediate,
                   has_gate=1 if cfg.has_attn_gate else 0,
-                  kv_bf16=1 if cfg.kv_dtype == "bf16" else 0, pad_=0,
+                  kv_bf16=1 if cfg.kv_dtype == "bf16" else 0,
+                  block_bidir=1 if getattr(cfg, "block_mask", "causal") == "bidirectional" else 0,
                   eps=cfg.rms_eps, theta=cfg.rope_theta)
 
 

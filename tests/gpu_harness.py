@@ -83,7 +83,7 @@ class Prepared:
         return self.inp["cache_k"].clone(), self.inp["cache_v"].clone()
 
     def run(self, M=None, R=None, seq_len=None, cache=None, x0=None, ctx=None, tokens=None,
-            want_layers=True):
+            want_layers=True, ctx_layers=None, ctx_row0=0):
         from verifier_block_forward_amd import dbf
         t = torch()
         cfg = self.cfg
@@ -98,10 +98,10 @@ class Prepared:
         if tokens is None and x0 is None:
             tokens = self.inp.get("tokens")
             x0 = self.inp.get("x0")
-        if ctx is None:
+        if ctx is None and ctx_layers is None:
             ctx = self.inp.get("ctx")
         io = dbf.make_io(M, R, h_final, tokens=tokens, x0=x0, ctx=ctx, hidden_out=hidden_out,
-                         layer_hidden=layers)
+                         layer_hidden=layers, ctx_layers=ctx_layers, ctx_row0=ctx_row0)
         kv = dbf.make_cache(ck, cv, seq_len)
         dbf.draft_block_forward(self.ccfg, self.bw, kv, io, self.ws)
         t.cuda.synchronize()

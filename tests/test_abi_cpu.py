@@ -15,7 +15,7 @@ def test_exports_every_declared_symbol():
                           "dbf_last_error", "dbf_abi_version"}
     for n in names:
         assert hasattr(dbf.lib(), n), n
-    assert dbf.abi_version() == 1
+    assert dbf.abi_version() == 2
 
 
 def _cfg(name="c0", **kw):
@@ -71,6 +71,18 @@ def test_block_argument_errors():
     assert _call_block(_cfg(hidden=260), dbf.BlockIO(M=4, R=0, h_final=h, x0=h))[0] == dbf.ESHAPE
     mtp = _cfg("c2")
     assert _call_block(mtp, dbf.BlockIO(M=1, R=1, h_final=h, x0=h, ctx=h))[0] == dbf.EINVAL
+    assert _call_block(_cfg(block_mask=2), dbf.BlockIO(M=4, R=0, h_final=h, x0=h))[0] == dbf.EINVAL
+    assert "block_mask" in dbf.last_error()
+    # DFlash context rows: given (ctx) or gathered from captured target layers
+    assert _call_block(cfg, dbf.BlockIO(M=4, R=2, h_final=h, x0=h))[0] == dbf.EINVAL
+    import ctypes as C
+    arr = (C.c_void_p * 2)(h, None)
+    io = dbf.BlockIO(M=4, R=2, h_final=h, x0=h, ctx_ld=256)
+    io.ctx_layers = C.cast(arr, C.POINTER(C.c_void_p))
+    assert _call_block(cfg, io)[0] == dbf.EINVAL and "ctx_layers[1]" in dbf.last_error()
+    arr[1] = h
+    io.ctx_ld = 8  # shorter than a row
+    assert _call_block(cfg, io)[0] == dbf.EINVAL and "ctx_ld" in dbf.last_error()
     # MTP needs embed_t as rows (x0) or as token ids to gather
     assert _call_block(mtp, dbf.BlockIO(M=1, R=0, h_final=h, ctx=h))[0] == dbf.EINVAL
     assert "neither tokens nor x0" in dbf.last_error()

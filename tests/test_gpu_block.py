@@ -211,3 +211,42 @@ def test_block_moe_tiled(orc):
 @pytest.mark.parametrize("name", ["c4", "c4m4"])
 def test_block_moe_full_size(orc, name):
     run_moe_case(orc, configs.get(name), tiled=True)
+
+
+@pytest.mark.parametrize("cfg", [
+    small(name="bidir", block_mask="bidirectional"),
+    small(name="bidir_bf16kv", block_mask="bidirectional", kv_dtype="bf16", M=9, R=5),
+    small(name="bidir_mtp_m4", kind="mtp", R=0, M=4, has_attn_gate=True, n_layers=1,
+          n_target_hidden=0, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, C=300,
+          block_mask="bidirectional"),
+], ids=lambda c: c.name)
+def test_block_bidirectional_mask(orc, cfg):
+    run_case(orc, cfg)
+
+
+def test_block_context_gathered_on_device(orc):
+    """The R context rows gathered on the device from the captured target layers
+    (row r = concat_t layer_t[row0 + r], the pages' extract_drafter_concat for the
+    new rows) give bit for bit the block of the host-built context, and match the
+    oracle fed the host-built rows."""
+    from tests.gpu_harness import to_dev, torch
+    cfg = small(name="gather", R=6, n_target_hidden=3)
+    H, R, nt = cfg.hidden, cfg.R, cfg.n_target_hidden
+    prep = Prepared(cfg)
+    rng = np.random.default_rng(44)
+    row0, P_cap, pitch = 17, 50, H + 8  # padded rows: the gather honours the stride
+    layers = [rng.standard_normal((P_cap, pitch)).astype(np.float32) for _ in range(nt)]
+    T = np.concatenate([L[row0:row0 + R, :H] for L in layers], axis=1)
+    print(f"\n[gather] R={R} n_t={nt} row0={row0}", flush=True)
+    by_ctx = prep.run(ctx=to_dev(T))
+    got = prep.run(ctx_layers=[to_dev(L) for L in layers], ctx_row0=row0)
+    for k in ("h_final", "hidden_out", "layer_hidden"):
+        assert np.array_equal(got[k], by_ctx[k]), f"gathered context differs in {k}"
+    gk, gv = prep.cache_host(*got["cache"])
+    ck, cv = prep.cache_host(*by_ctx["cache"])
+    assert np.array_equal(gk, ck) and np.array_equal(gv, cv)
+    inp = dict(prep.in_host, ctx=T)
+    s0 = prep.in_host["seq_len"]
+    want = orc.block_forward(cfg, prep.w_host, inp, seq_len=s0)
+    worst = compare_block(cfg, got, want, s0, s0 + R + cfg.M, (gk, gv), (want["cache_k"], want["cache_v"]))
+    print(f"  worst err/tol = {worst:.3f}", flush=True)

@@ -288,3 +288,28 @@ def test_mtp_token_input_is_the_embedding_row(orc):
     assert np.array_equal(a["hidden_out"], b["hidden_out"])
     c = run(orc, cfg, w, dict(inp, tokens=np.array([6, 63], np.int32)))
     assert not np.allclose(c["h_final"][0], a["h_final"][0])
+
+
+def test_bidirectional_block_mask(orc):
+    """Block-diffusion reading of the in-block mask: every block row attends to all M
+    block rows. With one row it equals the causal block exactly; in a one-layer block
+    the last row sees the same keys under both masks (exactly equal) while earlier
+    rows differ; and row 0 now depends on the later rows."""
+    cfg = tiny(n_layers=1)
+    bid = tiny(n_layers=1, block_mask="bidirectional")
+    w, inp = data(cfg)
+    c = run(orc, cfg, w, inp)
+    b = run(orc, bid, w, inp)
+    assert np.array_equal(b["h_final"][-1], c["h_final"][-1])
+    for m in range(cfg.M - 1):
+        assert not np.allclose(b["h_final"][m], c["h_final"][m])
+    w2, inp2_ = data(tiny(n_layers=2, M=1))
+    one_c = run(orc, tiny(n_layers=2, M=1), w2, inp2_)
+    one_b = run(orc, tiny(n_layers=2, M=1, block_mask="bidirectional"), w2, inp2_)
+    assert np.array_equal(one_c["h_final"], one_b["h_final"])
+    inp2 = dict(inp, x0=inp["x0"].copy())
+    inp2["x0"][-1] += 1.0
+    b2 = run(orc, bid, w, inp2)
+    c2 = run(orc, cfg, w, inp2)
+    assert not np.allclose(b2["h_final"][0], b["h_final"][0])
+    assert np.array_equal(c2["h_final"][0], c["h_final"][0])

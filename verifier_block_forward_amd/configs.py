@@ -48,6 +48,7 @@ class BlockConfig:
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     block_input: str = "x0"  # "x0" (F32 rows given) | "tokens" (gather from embed)
+    block_mask: str = "causal"  # "causal" | "bidirectional" (every block row sees the block)
     description: str = ""
 
     @property

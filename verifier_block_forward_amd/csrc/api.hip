@@ -232,6 +232,8 @@ int validate_config(const dbf_config *c) {
     if (rd % 2 || rd > c->head_dim) return fail(DBF_ESHAPE, "rotary_dim %d invalid", rd);
     if (c->kind == DBF_KIND_DFLASH && c->n_target_hidden < 1)
         return fail(DBF_EINVAL, "DFlash config needs n_target_hidden >= 1");
+    if (c->block_mask != DBF_MASK_CAUSAL && c->block_mask != DBF_MASK_BIDIR)
+        return fail(DBF_EINVAL, "block_mask %d unknown", c->block_mask);
     if (c->ffn_kind == DBF_FFN_DENSE) {
         if (c->intermediate < 8 || c->intermediate % 8)
             return fail(DBF_ESHAPE, "intermediate %d must be a positive multiple of 8", c->intermediate);
@@ -344,7 +346,18 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     if (!io->h_final) return fail(DBF_EINVAL, "io.h_final is null");
     if (c.kind == DBF_KIND_DFLASH) {
         if (!io->tokens && !io->x0) return fail(DBF_EINVAL, "io: neither tokens nor x0 given");
-        if (R > 0 && !io->ctx) return fail(DBF_EINVAL, "io.ctx is null with R = %d", R);
+        if (R > 0 && !io->ctx && !io->ctx_layers)
+            return fail(DBF_EINVAL, "io: neither ctx nor ctx_layers given with R = %d", R);
+        if (R > 0 && !io->ctx && io->ctx_layers) {
+            if (c.n_target_hidden > DBF_MAX_CTX_LAYERS)
+                return fail(DBF_EINVAL, "ctx_layers: n_target_hidden %d > %d", c.n_target_hidden,
+                            DBF_MAX_CTX_LAYERS);
+            for (int t = 0; t < c.n_target_hidden; t++)
+                if (!io->ctx_layers[t]) return fail(DBF_EINVAL, "ctx_layers[%d] is null", t);
+            if (io->ctx_ld < c.hidden || io->ctx_row0 < 0)
+                return fail(DBF_EINVAL, "ctx_ld %lld (>= H) or ctx_row0 %lld (>= 0) invalid",
+                            (long long)io->ctx_ld, (long long)io->ctx_row0);
+        }
     } else {
         if (!io->tokens && !io->x0) return fail(DBF_EINVAL, "io: neither tokens nor x0 (embed_t) given");
         if (!io->ctx) return fail(DBF_EINVAL, "io.ctx (prev_hidden) is null");
@@ -414,6 +427,12 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             t.H = p.Kin;
             t.base = io->ctx;
             t.ldb = p.Kin;
+            if (!io->ctx) {  // gather the captured target layers on the device
+                for (int i = 0; i < c.n_target_hidden; i++) t.gsrc[i] = io->ctx_layers[i];
+                t.gH = H;
+                t.gld = io->ctx_ld;
+                t.grow0 = io->ctx_row0;
+            }
             t.xs = xs_T;
             launch_colsum(t, st);
             SegList sl;
@@ -557,6 +576,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             aa.hd = hd;
             aa.chunk = chunk;
             aa.n_chunks = n_chunks;
+            aa.bidir = c.block_mask == DBF_MASK_BIDIR;
             aa.part = attn_part;
             launch_attn(aa, st);
             CombineArgs ca{};

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
             float alpha[QT];
 #pragma unroll
             for (int t = 0; t < QT; t++) {
-                const long long lim = a.n_ctx + qm[t];  // last key visible to this query
+                const long long lim = a.n_ctx + (a.bidir ? a.M - 1 : qm[t]);  // last visible key
                 float v[4];
                 float mx = -INFINITY;
 #pragma unroll

@@ -87,6 +87,11 @@ struct ColArgs {
     int V;
     const float *base;        // [M][ldb] base rows, or null
     int ldb;
+    // gather mode (base == null, gsrc[0] set): column k of row m is
+    // gsrc[k / gH][(grow0 + m) * gld + k % gH] (captured target layers)
+    const float *gsrc[8];
+    int gH;
+    long long gld, grow0;
     const float *p0;          // split-K partials [ks0][rows0][H], or null
     int ks0, rows0;
     const float *ssp0;        // row-scale source for set 0 ([16][ncb_in]) or null (scale 1)
@@ -150,6 +155,7 @@ struct AttnArgs {
     long long n_ctx;       // keys visible to block row 0 minus one: P0 + R
     int M, nq, nkv, hd;
     int chunk, n_chunks;
+    int bidir;             // 1: every block row sees all M block rows
     float *part;           // [n_chunks][M*nq][hd + 4]
 };
 constexpr int ATT_PART_EXTRA = 4;  // partial record: acc[hd], m, l, 2 pad floats

@@ -53,6 +53,9 @@ __global__ __launch_bounds__(256) void k_colsum(ColArgs a) {
                 v = bf16_to_f32(a.embed[(size_t)t * a.H + k]);
             } else if (a.base) {
                 v = a.base[(size_t)m * a.ldb + k];
+            } else if (a.gsrc[0]) {
+                const int t = k / a.gH;
+                v = a.gsrc[t][(size_t)(a.grow0 + m) * a.gld + (k - t * a.gH)];
             }
             if (a.p0) v += sc0 * s0;
             if (a.p1) v += sc1 * s1;

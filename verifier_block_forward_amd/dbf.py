@@ -26,6 +26,7 @@ _lib = C.CDLL(LIB_PATH)
 
 OK, EINVAL, ESHAPE, EDTYPE, ERANGE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16, I32, BF16_T16 = 0, 1, 2, 3
+MASK_CAUSAL, MASK_BIDIR = 0, 1
 KIND_DFLASH, KIND_MTP = 0, 1
 FFN_DENSE, FFN_MOE = 0, 1
 MAX_M = 16
@@ -50,7 +51,8 @@ class Config(C.Structure):
                 ("n_target_hidden", C.c_int32), ("vocab", C.c_int32), ("ffn_kind", C.c_int32),
                 ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("expert_intermediate", C.c_int32), ("shared_intermediate", C.c_int32),
-                ("has_attn_gate", C.c_int32), ("rms_eps", C.c_double), ("rope_theta", C.c_double)]
+                ("has_attn_gate", C.c_int32), ("block_mask", C.c_int32), ("reserved_", C.c_int32),
+                ("rms_eps", C.c_double), ("rope_theta", C.c_double)]
 
 
 LAYER_FIELDS = ["in_norm", "post_norm", "wq", "wk", "wv", "attn_gate", "wo", "q_norm", "k_norm",
@@ -77,7 +79,8 @@ class KVCache(C.Structure):
 class BlockIO(C.Structure):
     _fields_ = [("tokens", C.c_void_p), ("x0", C.c_void_p), ("ctx", C.c_void_p),
                 ("M", C.c_int32), ("R", C.c_int32), ("hidden_out", C.c_void_p),
-                ("h_final", C.c_void_p), ("layer_hidden", C.c_void_p)]
+                ("h_final", C.c_void_p), ("layer_hidden", C.c_void_p),
+                ("ctx_layers", C.POINTER(C.c_void_p)), ("ctx_ld", C.c_int64), ("ctx_row0", C.c_int64)]
 
 
 _lib.draft_block_forward.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(KVCache),
@@ -192,8 +195,9 @@ def make_config(bc) -> Config:
                   n_experts=bc.n_experts, top_k=bc.top_k,
                   expert_intermediate=bc.expert_intermediate,
                   shared_intermediate=bc.shared_intermediate,
-                  has_attn_gate=1 if bc.has_attn_gate else 0, rms_eps=bc.rms_eps,
-                  rope_theta=bc.rope_theta)
+                  has_attn_gate=1 if bc.has_attn_gate else 0,
+                  block_mask=MASK_BIDIR if bc.block_mask == "bidirectional" else MASK_CAUSAL,
+                  rms_eps=bc.rms_eps, rope_theta=bc.rope_theta)
 
 
 class BlockWeights:
@@ -222,10 +226,19 @@ def make_cache(k, v, seq_len: int) -> KVCache:
 
 
 def make_io(M, R, h_final, tokens=None, x0=None, ctx=None, hidden_out=None,
-            layer_hidden=None) -> BlockIO:
-    return BlockIO(tokens=_ptr(tokens), x0=_ptr(x0), ctx=_ptr(ctx), M=M, R=R,
-                   hidden_out=_ptr(hidden_out), h_final=_ptr(h_final),
-                   layer_hidden=_ptr(layer_hidden))
+            layer_hidden=None, ctx_layers=None, ctx_row0=0) -> BlockIO:
+    """ctx_layers: list of n_t device tensors [positions, >= H] F32 (captured target
+    layers); the R context rows are gathered from positions ctx_row0.."""
+    io = BlockIO(tokens=_ptr(tokens), x0=_ptr(x0), ctx=_ptr(ctx), M=M, R=R,
+                 hidden_out=_ptr(hidden_out), h_final=_ptr(h_final),
+                 layer_hidden=_ptr(layer_hidden))
+    if ctx_layers is not None:
+        arr = (C.c_void_p * len(ctx_layers))(*[t.data_ptr() for t in ctx_layers])
+        io._ctx_arr = arr  # the host pointer array must outlive the call
+        io.ctx_layers = C.cast(arr, C.POINTER(C.c_void_p))
+        io.ctx_ld = ctx_layers[0].stride(0)
+        io.ctx_row0 = ctx_row0
+    return io
 
 
 # ---------------------------------------------------------------------------
