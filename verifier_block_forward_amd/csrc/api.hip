@@ -419,9 +419,10 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         a.w = (const float *)Ls[0].in_norm.data;
         a.xs = xs_blk;
         a.ssp_out = ssp_x;
-        launch_colsum(a, st);
+        if (R == 0) launch_colsum(a, st);
         if (R > 0) {
-            // h_ctx = RMSNorm(T fc^T, hidden_norm): split T, project, split(proj (.) hidden_norm)
+            // h_ctx = RMSNorm(T fc^T, hidden_norm): split T (in the same launch as the
+            // block rows), project, split(proj (.) hidden_norm)
             ColArgs t = col();
             t.M = R;
             t.H = p.Kin;
@@ -434,7 +435,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 t.grow0 = io->ctx_row0;
             }
             t.xs = xs_T;
-            launch_colsum(t, st);
+            launch_colsum2(a, t, st);
             SegList sl;
             sl.add(w->fc, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
             sl.launch(st);
@@ -461,7 +462,6 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         e.w = (const float *)w->enorm.data;
         e.xs = xs_blk;
         e.ssp_out = ssp_e;
-        launch_colsum(e, st);
         ColArgs h = e;
         h.tokens = nullptr;  // prev_hidden rows are given, never gathered
         h.embed = nullptr;
@@ -469,7 +469,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         h.w = (const float *)w->hnorm.data;
         h.xs = xs_h;
         h.ssp_out = ssp_h;
-        launch_colsum(h, st);
+        launch_colsum2(e, h, st);  // embed_t and prev_hidden rows in one launch
         SegList sl;
         sl.add(w->eh_embed, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
         sl.add(w->eh_hidden, H, H, p.in, at<float>(ws, p.p_in1), xs_h);

@@ -439,16 +439,22 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
 #define DBF_HEAD_PIPE 4
 #endif
 constexpr int HEAD_PIPE = DBF_HEAD_PIPE;
-constexpr int HEAD_XCH = 8;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
+#ifndef DBF_HEAD_XCH
+#define DBF_HEAD_XCH 8
+#endif
+constexpr int HEAD_XCH = DBF_HEAD_XCH;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
 static_assert(HEAD_XCH % HEAD_PIPE == 0, "chunk must hold whole pipeline rounds");
 
-// this thread's share of chunk c: 4 float4 (row tid % 16, float4 columns tid/16 + 16i)
-__device__ __forceinline__ void head_x_load(float4 (&xr)[4], const float *h, int M, int K, int c) {
+// this thread's share of chunk c: HEAD_XPT float4 (row tid % 16, float4 columns
+// tid/16 + 16i); a chunk is 16 rows x HEAD_XCH*32 columns = HEAD_XCH*128 float4
+constexpr int HEAD_XPT = HEAD_XCH / 2;
+static_assert(HEAD_XCH % 2 == 0, "a chunk holds whole float4 pairs per thread");
+__device__ __forceinline__ void head_x_load(float4 (&xr)[HEAD_XPT], const float *h, int M, int K, int c) {
     const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
     const bool rok = r < M;
     const float *row = h + (size_t)(rok ? r : 0) * K;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < HEAD_XPT; i++) {
         const int col = c * HEAD_XCH * 32 + 4 * (q + 16 * i);
         const bool ok = rok && col < K;  // K % 8 == 0: a float4 is all in or all out
         const float4 v = *(const float4 *)(row + (ok ? col : 0));
@@ -461,10 +467,10 @@ __device__ __forceinline__ void head_x_load(float4 (&xr)[4], const float *h, int
 
 // split the thread's share and store it in split-tile order (element offset
 // ((s*2 + half)*64 + g*16 + r)*8 + j for local step s, column 8g + j)
-__device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[4]) {
+__device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[HEAD_XPT]) {
     const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < HEAD_XPT; i++) {
         const int k = 4 * (q + 16 * i);  // local column
         const int s = k >> 5, g = (k & 31) >> 3, j = k & 7;
         const float f[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
@@ -529,7 +535,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WP
 #pragma unroll
         for (int u = 0; u < PIPE; u++) DBF_HEAD_STAGE(u, u);
     }
-    float4 xr[4];
+    float4 xr[HEAD_XPT];
     head_x_load(xr, h, M, K, 0);
     head_x_store(xbuf[0], xr);
     if (nch > 1) head_x_load(xr, h, M, K, 1);

@@ -108,6 +108,7 @@ struct ColArgs {
     int ncb_out;
 };
 void launch_colsum(const ColArgs &a, hipStream_t s);
+void launch_colsum2(const ColArgs &a0, const ColArgs &a1, hipStream_t s);  // independent jobs
 void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
                        float *out, hipStream_t s);
 

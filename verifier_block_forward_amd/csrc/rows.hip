@@ -30,7 +30,12 @@ __device__ __forceinline__ float row_scale(const float *ssp_row, int ncb, int H,
 //   v = [gather embed row | base] + scale0 * sum P0 + scale1 * sum P1
 //   out/copies <- v;  xs <- split(v (.) w);  ssp_out[m][cb] <- sum over the 64 columns of v^2
 // Rows m >= M and padding columns write zeros into the split tile.
-__global__ __launch_bounds__(256) void k_colsum(ColArgs a) {
+__device__ __forceinline__ int colsum_row_groups(const ColArgs &a) {
+    return a.xs ? 4 : (a.M + 3) / 4;  // split tiles need all 16 rows written
+}
+
+__device__ __forceinline__ void colsum_body(const ColArgs &a) {
+    if ((int)blockIdx.x >= (a.H + 63) / 64 || (int)blockIdx.y >= colsum_row_groups(a)) return;
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 64 + lane;
@@ -71,10 +76,26 @@ __global__ __launch_bounds__(256) void k_colsum(ColArgs a) {
     if (a.xs && k < ((a.H + 31) & ~31)) split_store(a.xs, m, k, ok ? v * (a.w ? a.w[k] : 1.f) : 0.f);
 }
 
+__global__ __launch_bounds__(256) void k_colsum(ColArgs a) { colsum_body(a); }
+
+// two independent column jobs in one launch (blockIdx.z selects the job)
+__global__ __launch_bounds__(256) void k_colsum2(ColArgs a0, ColArgs a1) {
+    if (blockIdx.z == 0) colsum_body(a0);
+    else colsum_body(a1);
+}
+
+static dim3 colsum_grid(const ColArgs &a) {
+    return dim3((a.H + 63) / 64, a.xs ? 4 : (a.M + 3) / 4);
+}
+
 void launch_colsum(const ColArgs &a, hipStream_t s) {
-    const int ncb = (a.H + 63) / 64;
-    const int rg = a.xs ? 4 : (a.M + 3) / 4;  // split tiles need all 16 rows written
-    hipLaunchKernelGGL(k_colsum, dim3(ncb, rg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_colsum, colsum_grid(a), dim3(256), 0, s, a);
+}
+
+void launch_colsum2(const ColArgs &a0, const ColArgs &a1, hipStream_t s) {
+    const dim3 g0 = colsum_grid(a0), g1 = colsum_grid(a1);
+    const dim3 g(g0.x > g1.x ? g0.x : g1.x, g0.y > g1.y ? g0.y : g1.y, 2);
+    hipLaunchKernelGGL(k_colsum2, g, dim3(256), 0, s, a0, a1);
 }
 
 // ---------------------------------------------------------------------------
