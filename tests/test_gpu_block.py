@@ -198,6 +198,9 @@ def run_moe_case(orc, cfg, tiled=False):
     small_moe(name="moe_all", n_experts=8, top_k=8, M=2),
     small_moe(name="moe_m16", M=16, C=40),
     small_moe(name="moe_ragged", hidden=200, expert_intermediate=40, shared_intermediate=24, M=5),
+    # E not a multiple of the wavefront; the largest E with M = 16 routes in two row passes
+    small_moe(name="moe_e100", n_experts=100, top_k=5, M=7, seed=32),
+    small_moe(name="moe_e1024_m16", n_experts=1024, top_k=16, M=16, C=40, seed=32),
 ], ids=lambda c: c.name)
 def test_block_moe_small(orc, cfg):
     run_moe_case(orc, cfg)

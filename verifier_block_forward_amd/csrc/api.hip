@@ -496,7 +496,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     int chunk = 0, n_chunks = 0;
     {
         const int nq_group = (c.n_q_heads / c.n_kv_heads) * M;
-        const int qt = attn_qtiles(hd, nq_group);
+        const int qt = attn_qtiles(hd, nq_group, cache->dtype == DBF_BF16);
         const int qgroups = (nq_group + 16 * qt - 1) / (16 * qt);
         attn_plan(P0 + R + M, c.n_kv_heads * qgroups, &chunk, &n_chunks);
     }

@@ -11,6 +11,8 @@
 // chunks. (qwen35/mtp.rs
 // `forward_full_attention`: `apply_sdpa_with_kv_cache`, then
 // `apply_sigmoid_gate_multiply`.)
+#include <atomic>
+
 #include "internal.hpp"
 #include "kernels.hpp"
 
@@ -34,19 +36,40 @@ void attn_plan_keys(long long n_keys, int keys_per_wave, int *chunk, int *n_chun
     *n_chunks = (int)((n_keys + *chunk - 1) / *chunk);
 }
 
-void attn_plan(long long n_keys, int groups, int *chunk, int *n_chunks) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+// compute units of the current device, queried once per device
+static int device_cus() {
+    constexpr int MAXDEV = 64;
+    static std::atomic<int> cached[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < MAXDEV) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
+    if (dev < MAXDEV) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+void attn_plan(long long n_keys, int groups, int *chunk, int *n_chunks) {
+    const int cus = device_cus();
     const long long chunks = cus / groups > 1 ? cus / groups : 1;
     const long long per = (n_keys + chunks - 1) / chunks;
     attn_plan_keys(n_keys, (int)((per + ATT_WAVES - 1) / ATT_WAVES), chunk, n_chunks);
 }
 
-int attn_qtiles(int hd, int nq_group) {
+// Query tiles (16 queries each) one workgroup may take: the accumulators
+// (QT * hd / 16 float4 per lane) and one sub-tile of raw K/V must fit a wave's
+// registers without spilling. F32 caches hold twice the raw bytes of BF16 ones.
+constexpr int attn_qt_cap(int hd, bool kv_bf16) {
+    return kv_bf16 ? (hd == 256 ? 2 : 4) : (hd == 256 ? 1 : (hd == 128 ? 2 : 4));
+}
+
+int attn_qtiles(int hd, int nq_group, bool kv_bf16) {
     const int need = (nq_group + 15) / 16;
-    const int cap = hd == 256 ? 2 : 4;
+    const int cap = attn_qt_cap(hd, kv_bf16);
     return need < cap ? (need <= 1 ? 1 : (need <= 2 ? 2 : 4)) : cap;
 }
 
@@ -90,6 +113,19 @@ template <int HD>
 struct KvRaw<HD, true> {
     uint4 k[HD / 32], v[HD / 32];
 };
+
+#ifndef DBF_ATT_WPE
+#define DBF_ATT_WPE 2
+#endif
+// Waves per SIMD the register allocation is sized for. The planner launches about
+// one workgroup per CU, so the F32-cache variants that would spill inside the key
+// loop at two waves per SIMD take the whole register file (one wave) instead. The
+// 128-dim two-tile F32 variant keeps two: at that budget it parks two addresses
+// in scratch outside the loop only, and measured faster than at one wave.
+template <int HD, int QT, bool KVB>
+constexpr int attn_wpe() {
+    return (!KVB && (HD == 256 || (HD == 64 && QT == 4))) ? 1 : DBF_ATT_WPE;
+}
 
 // Sub-tiles held in registers ahead of use: every wave issues its first PF
 // sub-tiles' loads before anything else, then refills a slot as soon as it has
@@ -192,11 +228,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // workgroup barrier. F32 caches are split hi/lo (three products: hh, hl, lh); BF16
 // caches are exact (two products: h*K, l*K). The K/V loads of the first sub-tiles
 // are issued before the queries are staged, so their latency overlaps the staging.
-#ifndef DBF_ATT_WPE
-#define DBF_ATT_WPE 2
-#endif
 template <int HD, int QT, bool KVB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE))) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD, QT, KVB>()))) void k_attn(AttnArgs a) {
     using L = AttnLds<HD, QT, KVB>;
     constexpr int S = L::S, DT = L::DT, VTW = L::VTW;
     constexpr int PF = attn_prefetch<HD, KVB>();
@@ -408,17 +441,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_ATT_WPE
 
 bool attn_supported(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 
+// qt comes from attn_qtiles with the same cap, so every value reaching here has a variant
 template <int HD, bool KVB>
 static void go_attn(const AttnArgs &a, int qt, dim3 grid, hipStream_t s) {
-    if (qt == 1) hipLaunchKernelGGL((k_attn<HD, 1, KVB>), grid, dim3(256), 0, s, a);
-    else if (qt == 2) hipLaunchKernelGGL((k_attn<HD, 2, KVB>), grid, dim3(256), 0, s, a);
-    else if (HD != 256) hipLaunchKernelGGL((k_attn<HD, (HD == 256 ? 2 : 4), KVB>), grid, dim3(256), 0, s, a);
+    constexpr int CAP = attn_qt_cap(HD, KVB);
+    if (qt == 1) {
+        hipLaunchKernelGGL((k_attn<HD, 1, KVB>), grid, dim3(256), 0, s, a);
+    } else if constexpr (CAP >= 2) {
+        if (qt == 2) hipLaunchKernelGGL((k_attn<HD, 2, KVB>), grid, dim3(256), 0, s, a);
+        else if constexpr (CAP >= 4) hipLaunchKernelGGL((k_attn<HD, 4, KVB>), grid, dim3(256), 0, s, a);
+    }
 }
 
 void launch_attn(const AttnArgs &a, hipStream_t s) {
     const int G = a.nq / a.nkv;
     const int NQ = G * a.M;
-    const int qt = attn_qtiles(a.hd, NQ);
+    const int qt = attn_qtiles(a.hd, NQ, a.kv_bf16 != 0);
     dim3 grid(a.n_chunks, a.nkv, (NQ + 16 * qt - 1) / (16 * qt));
     if (a.kv_bf16) {
         if (a.hd == 64) go_attn<64, true>(a, qt, grid, s);

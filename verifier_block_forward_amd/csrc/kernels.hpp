@@ -164,7 +164,7 @@ constexpr int ATT_CHUNKS_MAX = 256;
 // groups: workgroups per chunk (kv heads x query tiles)
 void attn_plan(long long n_keys, int groups, int *chunk, int *n_chunks);
 void attn_plan_keys(long long n_keys, int keys_per_wave, int *chunk, int *n_chunks);
-int attn_qtiles(int hd, int nq_group);
+int attn_qtiles(int hd, int nq_group, bool kv_bf16);
 bool attn_supported(int hd);
 void launch_attn(const AttnArgs &a, hipStream_t s);
 

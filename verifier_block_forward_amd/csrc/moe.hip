@@ -37,100 +37,127 @@ __device__ __forceinline__ void better_pair(float &v, int &i, float v2, int i2) 
     }
 }
 
-// One block: route every row, then build the slot list.
-__global__ __launch_bounds__(256) void k_moe_route(MoeRouteArgs a) {
-    __shared__ float z[1024];
-    __shared__ unsigned char taken[1024];
+// Routing in one block of 1024 threads. Rows go in passes of up to 16 (and
+// rows * E <= ROUTE_Z logits): every thread sums the router partials of its
+// (row, expert) entries into LDS, then wave w picks the top_k of the pass's row w
+// with cross-lane shuffles only, one pick per round and no block barrier between
+// picks. The touched experts are compacted in ascending order with a ballot
+// prefix, and each (slot, row) coefficient is written exactly once. A NaN logit
+// ranks as -inf, so every pick is an in-range expert.
+constexpr int ROUTE_THREADS = 1024;         // one thread per expert at E = 1024
+constexpr int ROUTE_WAVES = ROUTE_THREADS / 64;
+constexpr int ROUTE_Z = 8192;               // router logits held in LDS per pass
+constexpr int ROUTE_EPL = 1024 / 64;        // experts per lane at E = 1024
+
+__global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
+    __shared__ float z[ROUTE_Z];            // unscaled router sums, [pass row][E]
+    __shared__ float rscale[16];
     __shared__ unsigned char used[1024];
-    __shared__ float rv[4];
-    __shared__ int ri[4];
     __shared__ int esel[16 * DBF_MAX_TOPK_DEV];
     __shared__ float wsel[16 * DBF_MAX_TOPK_DEV];
-    __shared__ int slot_of[1024];
-    __shared__ int nsl;
+    __shared__ int sexp[1024];
+    __shared__ int wtot[ROUTE_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int E = a.E, K = a.top_k;
-    for (int e = tid; e < E; e += 256) used[e] = 0;
-    __syncthreads();
-    for (int m = 0; m < a.M; m++) {
-        const float s = moe_row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
-        for (int e = tid; e < E; e += 256) {
-            z[e] = s * sum_partials(a.p_router, a.ks_router, 16, E, m, e);
-            taken[e] = 0;
+    const int E = a.E, K = a.top_k, M = a.M;
+    const int rg = ROUTE_Z / E < ROUTE_WAVES ? ROUTE_Z / E : ROUTE_WAVES;  // >= 8
+    for (int e = tid; e < E; e += ROUTE_THREADS) used[e] = 0;
+    // row scale and shared-expert gate, one wave per row
+    if (wv < M) {
+        const float s = moe_row_scale(a.ssp + (size_t)wv * a.ncb, a.ncb, a.H, a.eps);
+        const float g = s * sum_partials(a.p_sgi, a.ks_sgi, 16, 1, wv, 0);
+        if (lane == 0) {
+            rscale[wv] = s;
+            a.shared_scale[wv] = sigmoidf_(g);
+        }
+    }
+    for (int m0 = 0; m0 < M; m0 += rg) {
+        const int rows = M - m0 < rg ? M - m0 : rg;
+        for (int i = tid; i < rows * E; i += ROUTE_THREADS) {
+            const int r = i / E;
+            z[i] = sum_partials(a.p_router, a.ks_router, 16, E, m0 + r, i - r * E);
         }
         __syncthreads();
-        for (int t = 0; t < K; t++) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int e = tid; e < E; e += 256)
-                if (!taken[e]) better_pair(bv, bi, z[e], e);
+        if (wv < rows) {
+            const int m = m0 + wv;
+            const float s = rscale[m];
+            float zr[ROUTE_EPL];
+            unsigned taken = 0;  // bit j: expert lane + 64 j is out of range or already picked
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float v2 = __shfl_xor(bv, o, 64);
-                const int i2 = __shfl_xor(bi, o, 64);
-                better_pair(bv, bi, v2, i2);
+            for (int j = 0; j < ROUTE_EPL; j++) {
+                const int e = lane + 64 * j;
+                float v = e < E ? s * z[wv * E + e] : 0.f;
+                zr[j] = v != v ? -INFINITY : v;
+                if (e >= E) taken |= 1u << j;
             }
-            if (lane == 0) {
-                rv[wv] = bv;
-                ri[wv] = bi;
+            float myv = 0.f;  // lane t keeps pick t
+            int myi = 0;
+            for (int t = 0; t < K; t++) {
+                float bv = -INFINITY;
+                int bi = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < ROUTE_EPL; j++)
+                    if (!((taken >> j) & 1u)) better_pair(bv, bi, zr[j], lane + 64 * j);
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const float v2 = __shfl_xor(bv, o, 64);
+                    const int i2 = __shfl_xor(bi, o, 64);
+                    better_pair(bv, bi, v2, i2);
+                }
+                // all lanes agree on (bv, bi); bi < E because K <= E untaken entries existed
+                if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+                if (lane == t) {
+                    myv = bv;
+                    myi = bi;
+                }
             }
-            __syncthreads();
-            if (tid == 0) {
-                float v = rv[0];
-                int i = ri[0];
-                for (int w = 1; w < 4; w++) better_pair(v, i, rv[w], ri[w]);
-                esel[m * DBF_MAX_TOPK_DEV + t] = i;
-                wsel[m * DBF_MAX_TOPK_DEV + t] = v;  // logit for now
-                taken[i] = 1;
-                used[i] = 1;
-            }
-            __syncthreads();
-        }
-        if (tid == 0) {
-            // renormalised top-k weights: softmax over the kept logits
-            const float zmax = wsel[m * DBF_MAX_TOPK_DEV];
+            // renormalised top-k weights: softmax over the kept logits, summed in pick order
+            const float zmax = __shfl(myv, 0, 64);
+            const float ex = lane < K ? expf(myv - zmax) : 0.f;
             float den = 0.f;
-            for (int t = 0; t < K; t++) {
-                const float e = expf(wsel[m * DBF_MAX_TOPK_DEV + t] - zmax);
-                wsel[m * DBF_MAX_TOPK_DEV + t] = e;
-                den += e;
+            for (int t = 0; t < K; t++) den += __shfl(ex, t, 64);
+            if (lane < K) {
+                esel[m * DBF_MAX_TOPK_DEV + lane] = myi;
+                wsel[m * DBF_MAX_TOPK_DEV + lane] = ex / den;
+                a.sel[m * K + lane] = myi;
+                used[myi] = 1;
             }
-            for (int t = 0; t < K; t++) {
-                wsel[m * DBF_MAX_TOPK_DEV + t] /= den;
-                a.sel[m * K + t] = esel[m * DBF_MAX_TOPK_DEV + t];
-            }
-        }
-        if (wv == 0) {
-            const float g = s * sum_partials(a.p_sgi, a.ks_sgi, 16, 1, m, 0);
-            if (lane == 0) a.shared_scale[m] = sigmoidf_(g);
         }
         __syncthreads();
     }
-    if (tid == 0) {
-        int n = 0;
-        for (int e = 0; e < E; e++) {
-            slot_of[e] = -1;
-            if (used[e]) {
-                slot_of[e] = n;
-                a.slot_expert[n] = e;
-                n++;
-            }
-        }
-        nsl = n;
-        *a.nslots = n;
+    // ascending slot list: ballot prefix over expert e = tid
+    const bool u = tid < E && used[tid];
+    const unsigned long long bal = __ballot(u);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[wv] = __popcll(bal);
+    __syncthreads();
+    int off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < ROUTE_WAVES; w++) {
+        const int c = wtot[w];
+        off += w < wv ? c : 0;
+        total += c;
     }
+    if (u) {
+        a.slot_expert[off + below] = tid;
+        sexp[off + below] = tid;
+    }
+    if (tid == 0) *a.nslots = total;
     __syncthreads();
-    for (int i = tid; i < nsl * 16; i += 256) a.coef[i] = 0.f;
-    __syncthreads();
-    if (tid < 16 && tid < a.M) {
-        const int m = tid;
-        for (int t = 0; t < K; t++)
-            a.coef[(size_t)slot_of[esel[m * DBF_MAX_TOPK_DEV + t]] * 16 + m] = wsel[m * DBF_MAX_TOPK_DEV + t];
+    // coefficient of (slot, row): the row's weight for the slot's expert, else 0
+    for (int i = tid; i < total * 16; i += ROUTE_THREADS) {
+        const int sl = i >> 4, m = i & 15;
+        float c = 0.f;
+        if (m < M) {
+            const int e = sexp[sl];
+            for (int t = 0; t < K; t++)
+                if (esel[m * DBF_MAX_TOPK_DEV + t] == e) c = wsel[m * DBF_MAX_TOPK_DEV + t];
+        }
+        a.coef[i] = c;
     }
 }
 
 void launch_moe_route(const MoeRouteArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
 }
 
 // Expert (and shared-expert) SwiGLU: h = silu(s_m * sum P_gate) * (s_m * sum P_up),
