@@ -101,7 +101,7 @@ struct AttnLds {
 // 32*st + 8g .. +7 of every 32-dim step st (the A operand of the score product).
 // F32 V: already in the A-operand order of the P*V product, v[4*dt + j] = V[key
 // 4g + j][dim 16*dt + r16] (each load instruction reads 4 key rows x 64 contiguous
-// bytes). BF16 V: like K, transposed through LDS later.
+// bytes). BF16 V: whole rows per load (attn_v_slot), transposed through LDS later.
 template <int HD, bool KVB>
 struct KvRaw;
 template <int HD>
@@ -114,6 +114,9 @@ struct KvRaw<HD, true> {
     uint4 k[HD / 32], v[HD / 32];
 };
 
+#ifndef DBF_ATT_VNT
+#define DBF_ATT_VNT 1
+#endif
 #ifndef DBF_ATT_WPE
 #define DBF_ATT_WPE 2
 #endif
@@ -136,6 +139,25 @@ constexpr int attn_prefetch() {
     return (KVB && HD <= 128) ? 2 : 1;
 }
 
+// BF16 V sub-tile element (row, col) that load st of lane (r16, g) fetches: whole
+// rows per load instruction (64 lanes x 8 elements), so every cache line is read by
+// one instruction; the rows are stored to LDS as they are and read back transposed.
+template <int HD>
+__device__ __forceinline__ void attn_v_slot(int st, int g, int r16, int &row, int &col) {
+    const int e = (64 * st + 16 * g + r16) * 8;
+    row = e / HD;
+    col = e % HD;
+}
+
+typedef unsigned int u32x4_att __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_v16(const uint16_t *p) {
+#if DBF_ATT_VNT
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_att *)p));
+#else
+    return *(const uint4 *)p;
+#endif
+}
+
 template <int HD, bool KVB>
 __device__ __forceinline__ void attn_load_k(KvRaw<HD, KVB> &r, const AttnArgs &a, size_t head_off,
                                             long long kb, long long n_all, int g, int r16) {
@@ -146,7 +168,11 @@ __device__ __forceinline__ void attn_load_k(KvRaw<HD, KVB> &r, const AttnArgs &a
         const size_t off = head_off + (size_t)krow * HD + 32 * st + 8 * g;
         if constexpr (KVB) {
             r.k[st] = *(const uint4 *)((const uint16_t *)a.cache_k + off);
-            r.v[st] = *(const uint4 *)((const uint16_t *)a.cache_v + off);
+            int row, col;
+            attn_v_slot<HD>(st, g, r16, row, col);
+            long long vrow = kb + row;
+            if (vrow > n_all - 1) vrow = n_all - 1;
+            r.v[st] = ld_v16((const uint16_t *)a.cache_v + head_off + (size_t)vrow * HD + col);
         } else {
             const float4 *kp = (const float4 *)((const float *)a.cache_k + off);
             r.k[2 * st] = kp[0];
@@ -171,13 +197,16 @@ __device__ __forceinline__ void attn_load_v(KvRaw<HD, KVB> &r, const AttnArgs &a
     }
 }
 
-// BF16 V rows -> this wave's LDS rows, as loaded: row r16 holds key r16, pitch VTW
-// elements (HD + 8: the 16 rows of a transposed read then fall on different banks).
+// BF16 V sub-tile -> this wave's LDS rows: row j holds key j, pitch VTW elements
+// (HD + 8: the 16 rows of a transposed read then fall on different banks).
 template <int HD, int VTW>
 __device__ __forceinline__ void attn_v_store(const KvRaw<HD, true> &r, uint16_t *vrows, int g, int r16) {
 #pragma unroll
-    for (int st = 0; st < HD / 32; st++)
-        *(uint4 *)(vrows + r16 * VTW + 32 * st + 8 * g) = r.v[st];
+    for (int st = 0; st < HD / 32; st++) {
+        int row, col;
+        attn_v_slot<HD>(st, g, r16, row, col);
+        *(uint4 *)(vrows + row * VTW + col) = r.v[st];
+    }
 }
 
 // The A operand of the P*V product for dims 16*dt..+15, read transposed out of the
@@ -204,6 +233,44 @@ __device__ __forceinline__ void attn_k_step(const KvRaw<HD, KVB> &r, int st, bf1
         split8(kf, kh, kl);
     }
 }
+
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 lane-swap instructions. Given two copies of a value, a swap
+// leaves this lane's value in one register and its partner's (lane ^ 16, resp.
+// lane ^ 32) in the other (layout checked with a probe on MI355X), so combining
+// the two reduces the pair without a trip through LDS; both lanes of a pair get
+// the same result. The swaps are written as inline assembly because this
+// compiler folds max(first output, second output) of the swap builtin into the
+// first output when both inputs are one value. The s_nop gives the two wait
+// states a swap needs after a VALU write of its operands.
+__device__ __forceinline__ void lane_swap16(float &x, float &y) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void lane_swap32(float &x, float &y) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ float group4_max(float x) {
+    float y = x;
+    lane_swap16(x, y);
+    x = fmaxf(x, y);
+    y = x;
+    lane_swap32(x, y);
+    return fmaxf(x, y);
+}
+__device__ __forceinline__ float group4_sum(float x) {
+    float y = x;
+    lane_swap16(x, y);
+    x = x + y;
+    y = x;
+    lane_swap32(x, y);
+    return x + y;
+}
+
+// The running max of a query moves only when a score passes it by more than
+// ATT_RESCALE (log2 units); until then probabilities are formed against the old
+// max and may reach 2^ATT_RESCALE. The result is the same softmax (acc and l share
+// the reference point), and the accumulator rescale runs on few sub-tiles.
+constexpr float ATT_RESCALE = 8.0f;
 
 // Order this wave's LDS writes before its following reads (and reads before later
 // writes). A wavefront's LDS instructions execute in issue order, so only the
@@ -287,7 +354,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
         qsm[(idx * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo);
     }
 
-    float m_run[QT], l_run[QT];
+    // BF16 caches keep the query operands in registers where they fit (the F32
+    // path needs those registers for its raw sub-tiles and re-reads them from LDS)
+    constexpr bool QREG = KVB && QT * HD <= 256;
+    bf16x8 qreg[QREG ? QT * S * 2 : 1];
+
+    float m_run[QT], l_run[QT];  // l_run: this lane's share; summed over the groups at the end
     f32x4 acc[QT][DT];
 #pragma unroll
     for (int t = 0; t < QT; t++) {
@@ -297,6 +369,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
         for (int d = 0; d < DT; d++) acc[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();  // queries staged
+    if constexpr (QREG) {
+#pragma unroll
+        for (int i = 0; i < QT * S * 2; i++) qreg[i] = __builtin_bit_cast(bf16x8, qsm[i * 64 + lane]);
+    }
+    // every query sees the keys up to lim_all; sub-tiles below it skip the mask
+    const long long lim_all = a.n_ctx + (a.bidir ? a.M - 1 : 0);
 
     for (int base = 0; base < n_sub; base += PF) {
 #pragma unroll
@@ -304,9 +382,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
             const int it = base + u;
             if (it >= n_sub) break;
             const long long kb = k_lo + (long long)it * ATT_KT;
-            if constexpr (KVB) attn_v_store<HD, VTW>(rb[u], vth, g, r16);
             const bool more = it + PF < n_sub;
             const long long kb_next = kb + (long long)PF * ATT_KT;
+            if constexpr (KVB) attn_v_store<HD, VTW>(rb[u], vth, g, r16);
             f32x4 sc[QT];
 #pragma unroll
             for (int t = 0; t < QT; t++) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -316,45 +394,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
                 attn_k_step<HD, KVB>(rb[u], st, kh, kl);
 #pragma unroll
                 for (int t = 0; t < QT; t++) {
-                    const bf16x8 qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
-                    const bf16x8 ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
+                    bf16x8 qh, ql;
+                    if constexpr (QREG) {
+                        qh = qreg[(t * S + st) * 2 + 0];
+                        ql = qreg[(t * S + st) * 2 + 1];
+                    } else {
+                        qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
+                        ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
+                    }
                     sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, sc[t], 0, 0, 0);
                     sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql, sc[t], 0, 0, 0);
                     if constexpr (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh, sc[t], 0, 0, 0);
                 }
             }
             if (more) attn_load_k<HD, KVB>(rb[u], a, head_off, kb_next, n_all, g, r16);
-            s16x4 ph[QT], pl[QT];
-            float alpha[QT];
+            // masked scores and their per-query max over the sub-tile
+            const bool full = kb + ATT_KT <= k_hi && kb + ATT_KT - 1 <= lim_all;  // wave-uniform
+            float sv[QT][4], mx[QT];
+            bool grow = false;
 #pragma unroll
             for (int t = 0; t < QT; t++) {
-                const long long lim = a.n_ctx + (a.bidir ? a.M - 1 : qm[t]);  // last visible key
-                float v[4];
-                float mx = -INFINITY;
+                if (full) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const long long kp = kb + 4 * g + i;
-                    v[i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
-                    mx = fmaxf(mx, v[i]);
+                    for (int i = 0; i < 4; i++) sv[t][i] = sc[t][i];
+                } else {
+                    const long long lim = a.n_ctx + (a.bidir ? a.M - 1 : qm[t]);  // last visible key
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const long long kp = kb + 4 * g + i;
+                        sv[t][i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
+                    }
                 }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float m_new = fmaxf(m_run[t], mx);
-                float al = 1.f, ps = 0.f;
+                mx[t] = group4_max(fmaxf(fmaxf(sv[t][0], sv[t][1]), fmaxf(sv[t][2], sv[t][3])));
+                grow |= mx[t] > m_run[t] + ATT_RESCALE;  // first finite score: m_run is -inf
+            }
+            if (__ballot(grow)) {  // move the reference point of every query, rescale acc and l
+#pragma unroll
+                for (int t = 0; t < QT; t++) {
+                    const float m_new = fmaxf(m_run[t], mx[t]);
+                    const float al = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[t] - m_new);
+                    l_run[t] *= al;
+#pragma unroll
+                    for (int d = 0; d < DT; d++) acc[t][d] *= al;
+                    m_run[t] = m_new;
+                }
+            }
+            s16x4 ph[QT], pl[QT];
+#pragma unroll
+            for (int t = 0; t < QT; t++) {
+                const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];  // all scores -inf: p = 0
+                float ps = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float p = m_new == -INFINITY ? 0.f : exp2f(v[i] - m_new);
+                    const float p = __builtin_amdgcn_exp2f(sv[t][i] - m_use);
                     ps += p;
                     const __bf16 h = (__bf16)p;
                     ph[t][i] = __builtin_bit_cast(short, h);
                     pl[t][i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
                 }
-                if (m_new != -INFINITY) al = exp2f(m_run[t] - m_new);
-                ps += __shfl_xor(ps, 16, 64);
-                ps += __shfl_xor(ps, 32, 64);
-                l_run[t] = l_run[t] * al + ps;
-                m_run[t] = m_new;
-                alpha[t] = al;
+                l_run[t] += ps;
             }
             if constexpr (KVB) wave_lds_sync();  // V rows of this sub-tile written by every lane
 #pragma unroll
@@ -373,7 +471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
                 }
 #pragma unroll
                 for (int t = 0; t < QT; t++) {
-                    f32x4 o = acc[t][d] * alpha[t];
+                    f32x4 o = acc[t][d];
                     o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[t], o, 0, 0, 0);
                     o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[t], o, 0, 0, 0);
                     if constexpr (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, ph[t], o, 0, 0, 0);
@@ -386,6 +484,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
     }
 
     // merge the four waves' (m, l, acc) through LDS (the loop buffers are dead now)
+#pragma unroll
+    for (int t = 0; t < QT; t++) l_run[t] = group4_sum(l_run[t]);
     __syncthreads();
     float4 *accb = (float4 *)smem;                       // [3][QT][DT][64]
     float2 *mlb = (float2 *)(smem + L::ACC_BYTES);      // [4][QT][64]
