@@ -162,6 +162,32 @@ def test_block_c1_tiled(orc):
     run_case(orc, configs.C1, prep=Prepared(configs.C1, tiled=True))
 
 
+def scale_cached_keys(inp, kv_dtype, ramp):
+    """Multiply cached key row p of every layer and head by ramp[p] (BF16 caches are
+    decoded, scaled and re-rounded)."""
+    k = inp["cache_k"]
+    C = ramp.size
+    if kv_dtype == "bf16":
+        f = (k[:, :, :C].astype(np.uint32) << 16).view(np.float32) * ramp[None, None, :, None]
+        k[:, :, :C] = synth.bf16_rne(f.astype(np.float32)).reshape(f.shape)
+    else:
+        k[:, :, :C] *= ramp[None, None, :, None].astype(np.float32)
+
+
+@pytest.mark.parametrize("kv_dtype,order", [("f32", "growing"), ("bf16", "growing"),
+                                            ("f32", "shrinking"), ("bf16", "shrinking")])
+def test_block_attention_score_range(orc, kv_dtype, order):
+    """Cached keys scaled by position (1 to 16 along 20,000 positions, several 16-key
+    sub-tiles per wave): with rising scores a query's running max keeps passing its
+    reference point, so the accumulator is rescaled many times inside one wave; with
+    falling scores the first sub-tile sets it for good."""
+    cfg = small(name=f"scores_{order}_{kv_dtype}", kv_dtype=kv_dtype, C=20000, M=5, R=3)
+    inp = synth.make_inputs(cfg)
+    ramp = np.linspace(1.0, 16.0, cfg.C)
+    scale_cached_keys(inp, kv_dtype, ramp if order == "growing" else ramp[::-1].copy())
+    run_case(orc, cfg, Prepared(cfg, inputs=inp))
+
+
 # ---------------------------------------------------------------------------
 # MoE FFN (MTP block with routed experts + shared expert)
 # ---------------------------------------------------------------------------
