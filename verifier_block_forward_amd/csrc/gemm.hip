@@ -424,14 +424,19 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
 }
 
 // The hidden rows come in as F32 [M][K]. The workgroup stages them through LDS in
-// chunks of HEAD_XCH k-steps: its 256 threads load a chunk once (16 rows x 64
+// chunks of HEAD_XCH k-steps: its threads load a chunk once (16 rows x 64
 // contiguous bytes per load instruction), split every value into the BF16 hi/lo
-// pair and store the chunk in the split-tile order, double-buffered; the four
-// waves then read their B operands from LDS as contiguous 1 KiB lines. The next
+// pair and store the chunk in the split-tile order, double-buffered; the waves
+// then read their B operands from LDS as contiguous 1 KiB lines. The next
 // chunk's loads are in flight while the current one feeds the matrix cores, and
 // the weight ring runs across chunk boundaries. Rows r >= M and columns past K
-// are zeros. The four waves merge their records in LDS, so the workgroup writes
-// one record per activation row, stored [16][workgroups].
+// are zeros. The waves merge their records in LDS, so the workgroup writes one
+// record per activation row, stored [16][workgroups].
+// One workgroup of HEAD_WAVES = 8 waves fills a CU (two waves per SIMD): its waves
+// advance through K together, held by the per-chunk barrier. With two 4-wave
+// workgroups per CU instead, the one whose loads were served first finished
+// about 45 us (a fifth of the launch) before the other, which then ran alone at
+// half occupancy.
 #ifndef DBF_HEAD_WPE
 #define DBF_HEAD_WPE 2
 #endif
@@ -444,18 +449,24 @@ constexpr int HEAD_PIPE = DBF_HEAD_PIPE;
 #endif
 constexpr int HEAD_XCH = DBF_HEAD_XCH;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
 static_assert(HEAD_XCH % HEAD_PIPE == 0, "chunk must hold whole pipeline rounds");
+#ifndef DBF_HEAD_WAVES
+#define DBF_HEAD_WAVES 8
+#endif
+constexpr int HEAD_WAVES = DBF_HEAD_WAVES;  // waves per workgroup, one 16*HEAD_NA-row unit each
+constexpr int HEAD_THREADS = 64 * HEAD_WAVES;
 
 // this thread's share of chunk c: HEAD_XPT float4 (row tid % 16, float4 columns
-// tid/16 + 16i); a chunk is 16 rows x HEAD_XCH*32 columns = HEAD_XCH*128 float4
-constexpr int HEAD_XPT = HEAD_XCH / 2;
-static_assert(HEAD_XCH % 2 == 0, "a chunk holds whole float4 pairs per thread");
+// tid/16 + (HEAD_THREADS/16)*i); a chunk is 16 rows x HEAD_XCH*32 columns =
+// HEAD_XCH*128 float4
+constexpr int HEAD_XPT = HEAD_XCH * 128 / HEAD_THREADS;
+static_assert(HEAD_XCH * 128 % HEAD_THREADS == 0, "a chunk splits evenly over the threads");
 __device__ __forceinline__ void head_x_load(float4 (&xr)[HEAD_XPT], const float *h, int M, int K, int c) {
     const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
     const bool rok = r < M;
     const float *row = h + (size_t)(rok ? r : 0) * K;
 #pragma unroll
     for (int i = 0; i < HEAD_XPT; i++) {
-        const int col = c * HEAD_XCH * 32 + 4 * (q + 16 * i);
+        const int col = c * HEAD_XCH * 32 + 4 * (q + (HEAD_THREADS / 16) * i);
         const bool ok = rok && col < K;  // K % 8 == 0: a float4 is all in or all out
         const float4 v = *(const float4 *)(row + (ok ? col : 0));
         xr[i].x = ok ? v.x : 0.f;
@@ -471,7 +482,7 @@ __device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[H
     const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
 #pragma unroll
     for (int i = 0; i < HEAD_XPT; i++) {
-        const int k = 4 * (q + 16 * i);  // local column
+        const int k = 4 * (q + (HEAD_THREADS / 16) * i);  // local column
         const int s = k >> 5, g = (k & 31) >> 3, j = k & 7;
         const float f[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
         uint32_t hw[2], lw[2];
@@ -487,15 +498,15 @@ __device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[H
     }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WPE))) void k_head(
+__global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WPE))) void k_head(
     const uint16_t *__restrict__ W, int tiled, const float *__restrict__ h, int V, int K, int M,
     float *__restrict__ logits, float4 *__restrict__ part, int units) {
     constexpr int NA = HEAD_NA, PIPE = HEAD_PIPE;
     constexpr int CHE = HEAD_XCH * 2 * 64 * 8;  // elements of one staged chunk
     __shared__ __align__(16) uint16_t xbuf[2][CHE];
-    __shared__ Top2 wrec[4][16];
+    __shared__ Top2 wrec[HEAD_WAVES][16];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int unit = blockIdx.x * 4 + wv;
+    const int unit = blockIdx.x * HEAD_WAVES + wv;
     const bool active = unit < units;
     const int r = lane & 15, g = lane >> 4;
     const int row0 = unit * 16 * NA;
@@ -598,18 +609,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WP
     __syncthreads();
     if (threadIdx.x < 16) {
         const int m = threadIdx.x;
-        const Top2 q = merge(merge(wrec[0][m], wrec[1][m]), merge(wrec[2][m], wrec[3][m]));
+        Top2 q = wrec[0][m];
+#pragma unroll
+        for (int w = 1; w < HEAD_WAVES; w++) q = merge(q, wrec[w][m]);
         part[(size_t)m * gridDim.x + blockIdx.x] = make_float4(q.v1, __int_as_float(q.i1), q.v2, 0.f);
     }
 }
 
 int head_units(int V) { return (V + 16 * HEAD_NA - 1) / (16 * HEAD_NA); }
-int head_blocks(int V) { return (head_units(V) + 3) / 4; }
+int head_blocks(int V) { return (head_units(V) + HEAD_WAVES - 1) / HEAD_WAVES; }
 
 void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M, float *logits,
                  float4 *part, hipStream_t s) {
     const int units = head_units(V);
-    hipLaunchKernelGGL(k_head, dim3(head_blocks(V)), dim3(256), 0, s, W, tiled, h, V, K, M, logits,
+    hipLaunchKernelGGL(k_head, dim3(head_blocks(V)), dim3(HEAD_THREADS), 0, s, W, tiled, h, V, K, M, logits,
                        part, units);
 }
 
