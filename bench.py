@@ -186,6 +186,9 @@ def main():
     block_ms = [e[0].elapsed_time(e[1]) for e in evs]
     head_ms = [e[1].elapsed_time(e[2]) for e in evs]
     acc_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    # per-step latency by events (first kernel of the block forward through the end
+    # of the accept walk): its spread over the timed steps
+    step_ev_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_step = wall * 1e3 / args.steps
     value = M * args.steps / wall
 
@@ -261,6 +264,8 @@ def main():
                   "ms_draft_block_forward": round(float(np.mean(block_ms)), 4),
                   "ms_lm_head_argmax": round(head_avg, 4),
                   "ms_accept_prefix": round(float(np.mean(acc_ms)), 4),
+                  "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev_ms, q)), 4)
+                                          for q in (10, 50, 90)],
                   "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
                   "graph_rows_per_s": round(M / (graph_ms * 1e-3), 1) if graph_ms else None,
                   "accept_result": result.cpu().tolist()},

@@ -74,14 +74,44 @@ int attn_qtiles(int hd, int nq_group, bool kv_bf16) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_att __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_att __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_att __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_split __attribute__((ext_vector_type(4)));
+
+// Two F32 values split into BF16 hi (round to nearest even) and lo = BF16(x - hi),
+// each pair packed in one dword (first value in the low half). Converting the
+// pair as a vector makes one v_cvt_pk_bf16_f32 per pair instead of one per value
+// plus a repack.
+__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo) {
+    const f32x2_att f = {a, b};
+    const bf16x2_att h = __builtin_convertvector(f, bf16x2_att);
+    const f32x2_att hf = __builtin_convertvector(h, f32x2_att);
+    const bf16x2_att l = __builtin_convertvector(f - hf, bf16x2_att);
+    hi = __builtin_bit_cast(unsigned, h);
+    lo = __builtin_bit_cast(unsigned, l);
+}
 
 __device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo) {
+    u32x4_split h, l;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const __bf16 h = (__bf16)v[j];
-        hi[j] = h;
-        lo[j] = (__bf16)(v[j] - (float)h);
+    for (int j = 0; j < 4; j++) {
+        unsigned a, b;
+        split2(v[2 * j], v[2 * j + 1], a, b);
+        h[j] = a;
+        l[j] = b;
     }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// four values (the 4-key operands of the P*V product) split into hi/lo
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, s16x4 &hi, s16x4 &lo) {
+    unsigned h0, l0, h1, l1;
+    split2(x0, x1, h0, l0);
+    split2(x2, x3, h1, l1);
+    hi = __builtin_bit_cast(s16x4, u32x2_att{h0, h1});
+    lo = __builtin_bit_cast(s16x4, u32x2_att{l0, l1});
 }
 
 template <int HD, int QT, bool KVB>
@@ -443,15 +473,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
 #pragma unroll
             for (int t = 0; t < QT; t++) {
                 const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];  // all scores -inf: p = 0
-                float ps = 0.f;
+                float p[4], ps = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float p = __builtin_amdgcn_exp2f(sv[t][i] - m_use);
-                    ps += p;
-                    const __bf16 h = (__bf16)p;
-                    ph[t][i] = __builtin_bit_cast(short, h);
-                    pl[t][i] = __builtin_bit_cast(short, (__bf16)(p - (float)h));
+                    p[i] = __builtin_amdgcn_exp2f(sv[t][i] - m_use);
+                    ps += p[i];
                 }
+                split4(p[0], p[1], p[2], p[3], ph[t], pl[t]);
                 l_run[t] += ps;
             }
             if constexpr (KVB) wave_lds_sync();  // V rows of this sub-tile written by every lane
@@ -461,13 +489,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
                 if constexpr (KVB) {
                     va = attn_v_operand<VTW>(vth, d, g, r16);
                 } else {
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const float x = rb[u].v[4 * d + j];
-                        const __bf16 hx = (__bf16)x;
-                        va[j] = __builtin_bit_cast(short, hx);
-                        vb[j] = __builtin_bit_cast(short, (__bf16)(x - (float)hx));
-                    }
+                    split4(rb[u].v[4 * d], rb[u].v[4 * d + 1], rb[u].v[4 * d + 2], rb[u].v[4 * d + 3], va, vb);
                 }
 #pragma unroll
                 for (int t = 0; t < QT; t++) {
