@@ -316,12 +316,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 // merged through LDS at the end, so the chunk writes a single (acc, m, l) partial.
 // Scores are formed transposed, S^T[key][q] = K Q^T (v_mfma_f32_16x16x32_bf16,
 // A = 16 keys x 32 dims straight from the cache rows, B = pre-scaled queries split
-// hi/lo in LDS). That accumulator layout (lane: keys 4g..4g+3 of query l%16) is the
-// B operand of v_mfma_f32_16x16x16_bf16 for O^T[d][q] += V^T[d][key] P^T[key][q],
-// so the probabilities never leave their lanes. The V^T operand (4 keys x 1 dim per
-// lane) is loaded straight in that order for F32 caches and split in registers;
-// BF16 caches store the V rows in LDS (a region private to the wave) and read the
-// operand back transposed with ds_read_b64_tr_b16. The key loop has no
+// hi/lo, staged in LDS and, for BF16 caches where they fit, held in registers).
+// That accumulator layout (lane: keys 4g..4g+3 of query l%16) is the B operand of
+// v_mfma_f32_16x16x16_bf16 for O^T[d][q] += V^T[d][key] P^T[key][q], so the
+// probabilities never leave their lanes. The V^T operand (4 keys x 1 dim per lane)
+// is loaded straight in that order for F32 caches and split in registers; BF16
+// caches load whole V rows, store them in LDS (a region private to the wave) and
+// read the operand back transposed with ds_read_b64_tr_b16. The key loop has no
 // workgroup barrier. F32 caches are split hi/lo (three products: hh, hl, lh); BF16
 // caches are exact (two products: h*K, l*K). The K/V loads of the first sub-tiles
 // are issued before the queries are staged, so their latency overlaps the staging.
