@@ -573,6 +573,131 @@ int orc_accept_prefix(const int32_t *drafts, const int32_t *target, int K, const
     return ORC_OK;
 }
 
+/* Sampling from softmax(z / T) by inverse CDF. p_i = exp(z_i/T - max)/sum, in
+ * F64; the draw is the smallest index whose running sum of p (index order)
+ * exceeds u, u in [0, 1) given by the caller (the random numbers are inputs).
+ * Where rounding leaves u at or past the last running sum, the draw is the last
+ * index of nonzero probability. */
+static void orc_softmax_t(const float *z, int V, double T, double *p) {
+    double m = -INFINITY;
+    for (int i = 0; i < V; i++) {
+        const double y = (double)z[i] / T;
+        if (y > m) m = y;
+    }
+    double s = 0.0;
+    for (int i = 0; i < V; i++) {
+        p[i] = exp((double)z[i] / T - m);
+        s += p[i];
+    }
+    for (int i = 0; i < V; i++) p[i] /= s;
+}
+
+static int orc_icdf(const double *w, int V, double u) {
+    double tot = 0.0;
+    for (int i = 0; i < V; i++) tot += w[i];
+    const double tgt = u * tot;
+    double c = 0.0;
+    int last = 0;
+    for (int i = 0; i < V; i++) {
+        if (w[i] > 0.0) last = i;
+        c += w[i];
+        if (w[i] > 0.0 && c > tgt) return i;
+    }
+    return last;
+}
+
+/* One draw per row: token[m] ~ softmax(z[m] / T) with uniform u[m]; prob[m] (if
+ * not NULL) is the token's probability. */
+int orc_sample_tokens(const float *z, int M, int V, double T, const double *u, int32_t *token,
+                      double *prob) {
+    if (!z || !u || !token || M < 1 || V < 1 || !(T > 0.0) || !isfinite(T)) return ORC_EINVAL;
+    double *p = (double *)malloc((size_t)V * sizeof(double));
+    if (!p) return ORC_EINVAL;
+    for (int m = 0; m < M; m++) {
+        orc_softmax_t(z + (size_t)m * V, V, T, p);
+        const int t = orc_icdf(p, V, u[m]);
+        token[m] = t;
+        if (prob) prob[m] = p[t];
+    }
+    free(p);
+    return ORC_OK;
+}
+
+/* Sampled acceptance of one drafted token, MTP K = 1 ([ORCH] module doc,
+ * "Non-greedy (Metropolis-Hastings)": the page names stochastic acceptance on
+ * the MTP K = 1 path and gives no rule). The reading taken is the standard
+ * speculative-sampling rule, under which the next emitted token is distributed
+ * exactly as the target's softmax:
+ *   q = softmax(zq / T)        the drafter's distribution the draft d came from
+ *   p0 = softmax(zt[0] / T)    the target's distribution at the draft's position
+ *   p1 = softmax(zt[1] / T)    the target's distribution one position later
+ *   accept iff u0 * q(d) < p0(d), i.e. with probability min(1, p0(d) / q(d));
+ *   accepted: free token drawn from p1 with u1 (the bonus token);
+ *   rejected: free token drawn from max(0, p0 - q) / sum with u1 (from p0 when
+ *   that residual is all zero).
+ * result = {a (0 or 1), free_token, rollback = 1 - a, hit_eos, n_committed} as in
+ * the greedy walk; committed = [d, free] when accepted, [free] otherwise, cut
+ * after the first EOS (inclusive). info (if not NULL) = {q(d), p0(d), residual
+ * sum}. */
+int orc_accept_sampled(const float *zq, const float *zt, int V, double T, int32_t d, double u0,
+                       double u1, const int32_t *eos, int n_eos, int32_t *result, int32_t *committed,
+                       double *info) {
+    if (!zq || !zt || !result || V < 1 || d < 0 || d >= V || !(T > 0.0) || !isfinite(T) ||
+        n_eos < 0 || (n_eos > 0 && !eos))
+        return ORC_EINVAL;
+    double *q = (double *)malloc((size_t)V * sizeof(double));
+    double *p0 = (double *)malloc((size_t)V * sizeof(double));
+    double *p1 = (double *)malloc((size_t)V * sizeof(double));
+    if (!q || !p0 || !p1) {
+        free(q);
+        free(p0);
+        free(p1);
+        return ORC_EINVAL;
+    }
+    orc_softmax_t(zq, V, T, q);
+    orc_softmax_t(zt, V, T, p0);
+    orc_softmax_t(zt + V, V, T, p1);
+    const double qd = q[d], pd = p0[d];
+    const int a = u0 * qd < pd;
+    int free_tok;
+    double rsum = 0.0;
+    if (a) {
+        free_tok = orc_icdf(p1, V, u1);
+    } else {
+        for (int i = 0; i < V; i++) {
+            const double r = p0[i] - q[i];
+            q[i] = r > 0.0 ? r : 0.0;  /* q now holds the residual */
+            rsum += q[i];
+        }
+        free_tok = orc_icdf(rsum > 0.0 ? q : p0, V, u1);
+    }
+    if (info) {
+        info[0] = qd;
+        info[1] = pd;
+        info[2] = rsum;
+    }
+    const int32_t seq[2] = {d, free_tok};
+    const int32_t *c = a ? seq : seq + 1;
+    const int nc = a ? 2 : 1;
+    int n = 0, hit = 0;
+    for (int i = 0; i < nc; i++) {
+        if (committed) committed[n] = c[i];
+        n++;
+        for (int e = 0; e < n_eos; e++)
+            if (c[i] == eos[e]) hit = 1;
+        if (hit) break;
+    }
+    result[0] = a;
+    result[1] = free_tok;
+    result[2] = 1 - a;
+    result[3] = hit;
+    result[4] = n;
+    free(q);
+    free(p0);
+    free(p1);
+    return ORC_OK;
+}
+
 /* [ORCH] step 8: the rollback length saturates at zero on the page; removing
  * more rows than the cache holds is an error here. */
 int orc_kv_rollback(orc_cache *kv, int n) {

@@ -89,6 +89,11 @@ def _declare(L):
     L.orc_lm_head.restype = C.c_int
     L.orc_accept_prefix.argtypes = [I32, I32, C.c_int, I32, C.c_int, I32, I32]
     L.orc_accept_prefix.restype = C.c_int
+    L.orc_sample_tokens.argtypes = [F, C.c_int, C.c_int, C.c_double, D, I32, D]
+    L.orc_sample_tokens.restype = C.c_int
+    L.orc_accept_sampled.argtypes = [F, F, C.c_int, C.c_double, C.c_int32, C.c_double,
+                                     C.c_double, I32, C.c_int, I32, I32, D]
+    L.orc_accept_sampled.restype = C.c_int
     L.orc_kv_rollback.argtypes = [C.POINTER(OrcCache), C.c_int]
     L.orc_kv_rollback.restype = C.c_int
     L.orc_threads.restype = C.c_int
@@ -271,6 +276,43 @@ def accept_prefix(drafts, target, eos=()):
         raise ValueError(f"oracle accept_prefix rejected its arguments: {rc}")
     return {"accept_count": int(res[0]), "free_token": int(res[1]), "rollback": int(res[2]),
             "hit_eos": bool(res[3]), "committed": com[: res[4]].tolist()}
+
+
+def sample_tokens(logits, u, temperature=1.0):
+    """One draw per row from softmax(logits[m] / T) by inverse CDF with uniform u[m]
+    (oracle.c `orc_sample_tokens`). Returns (tokens [M] int32, probabilities [M])."""
+    z = _c(np.atleast_2d(logits), np.float32)
+    M, V = z.shape
+    uu = _c(np.asarray(u, np.float64).reshape(-1), np.float64)
+    assert uu.size == M
+    tok = np.zeros(M, np.int32)
+    prob = np.zeros(M, np.float64)
+    rc = lib().orc_sample_tokens(_p(z, F), M, V, float(temperature), _p(uu, D), _p(tok, I32),
+                                 _p(prob, D))
+    if rc != 0:
+        raise ValueError(f"oracle sample_tokens rejected its arguments: {rc}")
+    return tok, prob
+
+
+def accept_sampled(draft_logits, target_logits, draft, u0, u1, temperature=1.0, eos=()):
+    """Sampled acceptance of one drafted token, MTP K = 1 (oracle.c
+    `orc_accept_sampled`: the speculative-sampling reading)."""
+    zq = _c(np.asarray(draft_logits).reshape(-1), np.float32)
+    zt = _c(target_logits, np.float32)
+    V = zq.size
+    assert zt.shape == (2, V)
+    e = _c(np.asarray(eos, dtype=np.int32).reshape(-1), np.int32)
+    res = np.zeros(5, np.int32)
+    com = np.zeros(2, np.int32)
+    info = np.zeros(3, np.float64)
+    rc = lib().orc_accept_sampled(_p(zq, F), _p(zt, F), V, float(temperature), int(draft), float(u0),
+                                  float(u1), _p(e, I32) if e.size else C.cast(None, I32), e.size,
+                                  _p(res, I32), _p(com, I32), _p(info, D))
+    if rc != 0:
+        raise ValueError(f"oracle accept_sampled rejected its arguments: {rc}")
+    return {"accept_count": int(res[0]), "free_token": int(res[1]), "rollback": int(res[2]),
+            "hit_eos": bool(res[3]), "committed": com[: res[4]].tolist(),
+            "q_draft": float(info[0]), "p_draft": float(info[1]), "residual_sum": float(info[2])}
 
 
 def kv_rollback(seq_len: int, n: int) -> int:
