@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DBF_ABI_VERSION 2
+#define DBF_ABI_VERSION 3
 
 /* status codes */
 #define DBF_OK 0
@@ -76,6 +76,8 @@ extern "C" {
 #define DBF_MAX_CTX_LAYERS 8 /* captured target layers gathered on the device */
 #define DBF_MAX_R 16   /* new context rows per call */
 #define DBF_MAX_TOPK 16
+#define DBF_MAX_SAMPLE_ROWS 1024  /* rows per sample_tokens call */
+#define DBF_MAX_VOCAB (1 << 24)   /* logits per row for the sampling calls */
 
 /* Non-owning view of a device tensor: row-major, contiguous. */
 typedef struct {
@@ -249,6 +251,57 @@ int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const
 /* KV rollback ([ORCH] per-round step 8: drop the rejected positions). Host-side
  * metadata only: cache->seq_len -= n. DBF_ERANGE when n < 0 or n > seq_len. */
 int kv_rollback(dbf_kv_cache *cache, int32_t n);
+
+/* One draw per row from softmax(logits[m] / T) by inverse CDF (the drafter's
+ * sampled draft for the stochastic MTP K = 1 round named in the [ORCH] module
+ * doc, "Non-greedy (Metropolis-Hastings)"; its rule is not on the pages, see
+ * accept_sampled). Device pointers:
+ *   logits [M][V] F32 (e.g. lm_head_argmax's logits), u [M] F32 uniforms in [0, 1)
+ *   supplied by the caller (the library draws no random numbers);
+ *   token [M] int32 out: the smallest index whose running sum of probability, in
+ *   index order, exceeds u[m] (the last index of nonzero probability where
+ *   rounding leaves u[m] at the end);
+ *   prob [M] F32 out or NULL: the drawn token's probability.
+ * M in 1..DBF_MAX_SAMPLE_ROWS, V in 1..DBF_MAX_VOCAB, temperature in [1e-3, 1e3].
+ * Probabilities are formed in F32 (sums over fixed trees, so a draw is
+ * reproducible); a u within rounding of a cumulative boundary may land on either
+ * side of it. Non-finite logits give an unspecified token in [0, V).
+ * ws: at least sample_tokens_workspace_bytes(M, V) bytes, 256-byte aligned.
+ * Enqueued only (two kernels). */
+int sample_tokens(const float *logits, int32_t M, int32_t V, float temperature, const float *u,
+                  int32_t *token, float *prob, void *ws, size_t ws_bytes, void *stream);
+
+size_t sample_tokens_workspace_bytes(int32_t M, int32_t V);
+
+/* Sampled acceptance of one drafted token, MTP K = 1 ([ORCH] module doc,
+ * "Non-greedy (Metropolis-Hastings)": stochastic acceptance is named for this path
+ * without its rule; the rule taken is standard speculative sampling, under which
+ * the emitted token is distributed exactly as the target's softmax):
+ *   q = softmax(draft_logits / T), p0 = softmax(target_logits[0] / T),
+ *   p1 = softmax(target_logits[1] / T);
+ *   accepted iff u[0] * q(d) < p0(d), i.e. with probability min(1, p0(d)/q(d));
+ *   accepted: free token drawn from p1 with u[1] (the bonus token);
+ *   rejected: free token drawn from max(0, p0 - q), normalised, with u[1] (from p0
+ *   when that residual is empty).
+ * Draws are by inverse CDF as in sample_tokens. Device pointers:
+ *   draft_logits [V] F32 (the drafter's logits at the drafted position);
+ *   target_logits [2][V] F32 (the target's logits at the draft's position and the
+ *   next); draft [1] int32 (d, e.g. from sample_tokens); u [2] F32 uniforms;
+ *   eos [n_eos] int32 or NULL when n_eos == 0 (n_eos <= 1024);
+ *   result [5] int32 out: {accept_count a (0 or 1), free_token, rollback = 1 - a,
+ *          hit_eos, n_committed}, as accept_prefix;
+ *   committed [2] int32 out or NULL: [d, free_token] when accepted, [free_token]
+ *          otherwise, cut after the first EOS (inclusive).
+ * A draft outside [0, V) is not read: result = {-1, -1, -1, 0, 0}.
+ * V in 1..DBF_MAX_VOCAB, temperature in [1e-3, 1e3]; the acceptance test and the
+ * draws are formed in F32 (a u within rounding of a boundary may go either way).
+ * ws: at least accept_sampled_workspace_bytes(V) bytes, 256-byte aligned.
+ * Enqueued only (three kernels); no host synchronisation. */
+int accept_sampled(const float *draft_logits, const float *target_logits, int32_t V, float temperature,
+                   const int32_t *draft, const float *u, const int32_t *eos, int32_t n_eos,
+                   int32_t *result, int32_t *committed, void *ws, size_t ws_bytes, void *stream);
+
+size_t accept_sampled_workspace_bytes(int32_t V);
 
 /* Tiled weight layout. For a row-major BF16 weight [N, K] (or a batch [B, N, K] of
  * them, e.g. MoE experts), the tiled copy holds ceil(N/16) x ceil(K/32) blocks of

@@ -12,10 +12,11 @@ def test_exports_every_declared_symbol():
     names = dbf.declared_functions()
     assert set(names) >= {"draft_block_forward", "lm_head_argmax", "accept_prefix", "kv_rollback",
                           "draft_block_workspace_bytes", "lm_head_argmax_workspace_bytes",
-                          "dbf_last_error", "dbf_abi_version"}
+                          "sample_tokens", "sample_tokens_workspace_bytes", "accept_sampled",
+                          "accept_sampled_workspace_bytes", "dbf_last_error", "dbf_abi_version"}
     for n in names:
         assert hasattr(dbf.lib(), n), n
-    assert dbf.abi_version() == 2
+    assert dbf.abi_version() == 3
 
 
 def _cfg(name="c0", **kw):
@@ -227,3 +228,56 @@ def test_workspace_sizing_every_workload_and_moe_bounds():
     c = dbf.make_config(configs.get("c4"))
     c.n_experts = 2000
     assert dbf.draft_block_workspace_bytes(c, 1, 0) == 0
+
+
+def test_sampling_workspace_sizes():
+    for V in (1, 1000, 248320, 262144, 1 << 24):
+        n = dbf.sample_tokens_workspace_bytes(16, V)
+        assert n > 0 and n % 256 == 0
+        m = dbf.accept_sampled_workspace_bytes(V)
+        assert m > 0 and m % 256 == 0
+    assert dbf.sample_tokens_workspace_bytes(0, 100) == 0
+    assert dbf.sample_tokens_workspace_bytes(1025, 100) == 0
+    assert dbf.sample_tokens_workspace_bytes(1, 0) == 0
+    assert dbf.sample_tokens_workspace_bytes(1, (1 << 24) + 1) == 0
+    assert dbf.accept_sampled_workspace_bytes(0) == 0
+
+
+def _sample(M=4, V=1000, T=1.0, logits=0x1000, u=0x2000, token=0x3000, ws=0x100000, ws_bytes=1 << 20):
+    return dbf.lib().sample_tokens(_fake(logits) if logits else None, M, V, T, _fake(u) if u else None,
+                                   _fake(token) if token else None, None,
+                                   _fake(ws) if ws else None, ws_bytes, None)
+
+
+def test_sample_tokens_argument_errors():
+    assert _sample(logits=0) == dbf.EINVAL
+    assert _sample(u=0) == dbf.EINVAL
+    assert _sample(token=0) == dbf.EINVAL
+    assert _sample(M=0) == dbf.EINVAL
+    assert _sample(M=1025) == dbf.EINVAL
+    assert _sample(V=0) == dbf.ESHAPE
+    for T in (0.0, -1.0, 1e-4, 2e3, float("nan"), float("inf")):
+        assert _sample(T=T) == dbf.EINVAL, T
+    assert _sample(ws=0) == dbf.EWORKSPACE
+    assert _sample(ws=0x100010) == dbf.EWORKSPACE  # not 256-byte aligned
+    assert _sample(ws_bytes=16) == dbf.EWORKSPACE
+    assert "workspace" in dbf.last_error()
+
+
+def _accept(V=1000, T=1.0, zq=0x1000, zt=0x2000, d=0x3000, u=0x4000, res=0x5000, eos=None, n_eos=0,
+            ws=0x100000, ws_bytes=1 << 20):
+    f = lambda p: _fake(p) if p else None
+    return dbf.lib().accept_sampled(f(zq), f(zt), V, T, f(d), f(u), f(eos), n_eos, f(res), None, f(ws),
+                                    ws_bytes, None)
+
+
+def test_accept_sampled_argument_errors():
+    for k in ("zq", "zt", "d", "u", "res"):
+        assert _accept(**{k: 0}) == dbf.EINVAL, k
+    assert _accept(V=0) == dbf.ESHAPE
+    assert _accept(V=(1 << 24) + 1) == dbf.ESHAPE
+    assert _accept(T=0.0) == dbf.EINVAL
+    assert _accept(n_eos=1) == dbf.EINVAL  # eos list missing
+    assert _accept(n_eos=-1) == dbf.EINVAL
+    assert _accept(ws=0) == dbf.EWORKSPACE
+    assert _accept(ws_bytes=dbf.accept_sampled_workspace_bytes(1000) - 1) == dbf.EWORKSPACE

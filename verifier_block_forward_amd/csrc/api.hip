@@ -794,6 +794,124 @@ int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const
     return hip_check("accept_prefix launch");
 }
 
+// ---------------------------------------------------------------------------
+// Sampling from softmax(logits / T) and sampled acceptance of one draft
+static constexpr double LOG2E = 1.4426950408889634;
+
+static int check_temperature(float T) {
+    if (!(T >= 1e-3f && T <= 1e3f)) return fail(DBF_EINVAL, "temperature %g outside [1e-3, 1e3]", (double)T);
+    return DBF_OK;
+}
+
+static int check_ws(const void *ws, size_t ws_bytes, size_t need) {
+    if (!ws) return fail(DBF_EWORKSPACE, "workspace is null");
+    if ((uintptr_t)ws % 256) return fail(DBF_EWORKSPACE, "workspace not 256-byte aligned");
+    if (ws_bytes < need) return fail(DBF_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return DBF_OK;
+}
+
+size_t sample_tokens_workspace_bytes(int32_t M, int32_t V) {
+    if (M < 1 || M > DBF_MAX_SAMPLE_ROWS || V < 1 || V > DBF_MAX_VOCAB) return 0;
+    return align256((size_t)M * smp_blocks(V) * sizeof(float2));
+}
+
+int sample_tokens(const float *logits, int32_t M, int32_t V, float temperature, const float *u,
+                  int32_t *token, float *prob, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!logits || !u || !token) return fail(DBF_EINVAL, "logits, u and token are required");
+    if (M < 1 || M > DBF_MAX_SAMPLE_ROWS) return fail(DBF_EINVAL, "M = %d outside [1, %d]", M, DBF_MAX_SAMPLE_ROWS);
+    if (V < 1 || V > DBF_MAX_VOCAB) return fail(DBF_ESHAPE, "V = %d outside [1, %d]", V, DBF_MAX_VOCAB);
+    int rc = check_temperature(temperature);
+    if (rc) return rc;
+    if ((rc = check_ws(ws, ws_bytes, sample_tokens_workspace_bytes(M, V)))) return rc;
+    const int nb = smp_blocks(V);
+    const float c = (float)(LOG2E / (double)temperature);
+    float2 *stats = (float2 *)ws;
+    (void)hipGetLastError();
+    SmpStatArgs sa{};
+    sa.z[0] = logits;
+    sa.nptr = 1;
+    sa.ld = V;
+    sa.V = V;
+    sa.nb = nb;
+    sa.c = c;
+    sa.stats = stats;
+    launch_smp_stats(sa, M, (hipStream_t)stream);
+    SmpDrawArgs da{};
+    da.z = logits;
+    da.stats = stats;
+    da.u = u;
+    da.V = V;
+    da.nb = nb;
+    da.c = c;
+    da.token = token;
+    da.prob = prob;
+    launch_smp_draw(da, M, (hipStream_t)stream);
+    return hip_check("sample_tokens launch");
+}
+
+size_t accept_sampled_workspace_bytes(int32_t V) {
+    if (V < 1 || V > DBF_MAX_VOCAB) return 0;
+    const size_t nb = (size_t)smp_blocks(V);
+    return align256(3 * nb * sizeof(float2)) + align256(nb * sizeof(float));
+}
+
+int accept_sampled(const float *draft_logits, const float *target_logits, int32_t V, float temperature,
+                   const int32_t *draft, const float *u, const int32_t *eos, int32_t n_eos,
+                   int32_t *result, int32_t *committed, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    if (!draft_logits || !target_logits || !draft || !u || !result)
+        return fail(DBF_EINVAL, "draft_logits, target_logits, draft, u and result are required");
+    if (V < 1 || V > DBF_MAX_VOCAB) return fail(DBF_ESHAPE, "V = %d outside [1, %d]", V, DBF_MAX_VOCAB);
+    if (n_eos < 0 || n_eos > 1024 || (n_eos > 0 && !eos))
+        return fail(DBF_EINVAL, "eos list invalid (n_eos = %d)", n_eos);
+    int rc = check_temperature(temperature);
+    if (rc) return rc;
+    if ((rc = check_ws(ws, ws_bytes, accept_sampled_workspace_bytes(V)))) return rc;
+    const int nb = smp_blocks(V);
+    const float c = (float)(LOG2E / (double)temperature);
+    float2 *stats = (float2 *)ws;
+    float *rsum = (float *)((char *)ws + align256(3 * (size_t)nb * sizeof(float2)));
+    const float *zp0 = target_logits, *zp1 = target_logits + V;
+    (void)hipGetLastError();
+    SmpStatArgs sa{};
+    sa.z[0] = draft_logits;
+    sa.z[1] = zp0;
+    sa.z[2] = zp1;
+    sa.nptr = 3;
+    sa.V = V;
+    sa.nb = nb;
+    sa.c = c;
+    sa.stats = stats;
+    launch_smp_stats(sa, 3, (hipStream_t)stream);
+    SmpResidualArgs ra{};
+    ra.zq = draft_logits;
+    ra.zp = zp0;
+    ra.stats = stats;
+    ra.V = V;
+    ra.nb = nb;
+    ra.c = c;
+    ra.rsum = rsum;
+    launch_smp_residual(ra, (hipStream_t)stream);
+    SmpAcceptArgs aa{};
+    aa.zq = draft_logits;
+    aa.zp0 = zp0;
+    aa.zp1 = zp1;
+    aa.stats = stats;
+    aa.rsum = rsum;
+    aa.draft = draft;
+    aa.u = u;
+    aa.eos = eos;
+    aa.n_eos = n_eos;
+    aa.V = V;
+    aa.nb = nb;
+    aa.c = c;
+    aa.result = result;
+    aa.committed = committed;
+    launch_smp_accept(aa, (hipStream_t)stream);
+    return hip_check("accept_sampled launch");
+}
+
 size_t dbf_tiled_bytes(int64_t N, int64_t K) {
     if (N < 1 || K < 1) return 0;
     return tiled_elems(N, K) * sizeof(uint16_t);

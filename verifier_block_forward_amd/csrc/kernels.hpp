@@ -180,6 +180,55 @@ void launch_accept(const int32_t *drafts, const int32_t *target, int K, const in
                    int n_eos, int32_t *result, int32_t *committed, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Sampling from softmax(logits / T) and sampled acceptance (sample.hip)
+int smp_blocks(int V);  // segments per logits row
+
+struct SmpStatArgs {
+    const float *z[3];  // row r: z[r] (nptr == 3), or z[0] + r * ld (nptr == 1)
+    int nptr;
+    long long ld;
+    int V, nb;
+    float c;            // log2(e) / T
+    float2 *stats;      // out: [rows][nb] (max y, sum 2^(y - max)) per segment
+};
+void launch_smp_stats(const SmpStatArgs &a, int rows, hipStream_t s);
+
+struct SmpResidualArgs {
+    const float *zq, *zp;  // draft logits, target logits at the draft's position
+    const float2 *stats;   // [2][nb]: q's rows then p0's
+    int V, nb;
+    float c;
+    float *rsum;           // out: [nb] segment sums of max(0, p0 - q)
+};
+void launch_smp_residual(const SmpResidualArgs &a, hipStream_t s);
+
+struct SmpDrawArgs {
+    const float *z;        // [M][V]
+    const float2 *stats;   // [M][nb]
+    const float *u;        // [M]
+    int V, nb;
+    float c;
+    int32_t *token;        // out [M]
+    float *prob;           // out [M] or null
+};
+void launch_smp_draw(const SmpDrawArgs &a, int M, hipStream_t s);
+
+struct SmpAcceptArgs {
+    const float *zq, *zp0, *zp1;
+    const float2 *stats;   // [3][nb]: q, p0, p1
+    const float *rsum;     // [nb]
+    const int32_t *draft;  // [1]
+    const float *u;        // [2]
+    const int32_t *eos;
+    int n_eos;
+    int V, nb;
+    float c;
+    int32_t *result;       // out [5]
+    int32_t *committed;    // out [2] or null
+};
+void launch_smp_accept(const SmpAcceptArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // MoE FFN (moe.hip)
 // ---------------------------------------------------------------------------
 struct MoeRouteArgs {

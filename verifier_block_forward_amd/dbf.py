@@ -96,6 +96,17 @@ _lib.lm_head_argmax_workspace_bytes.restype = C.c_size_t
 _lib.accept_prefix.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
                                C.c_void_p, C.c_void_p, C.c_void_p]
 _lib.accept_prefix.restype = C.c_int
+_lib.sample_tokens.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
+                               C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+_lib.sample_tokens.restype = C.c_int
+_lib.sample_tokens_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+_lib.sample_tokens_workspace_bytes.restype = C.c_size_t
+_lib.accept_sampled.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p,
+                                C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                C.c_void_p]
+_lib.accept_sampled.restype = C.c_int
+_lib.accept_sampled_workspace_bytes.argtypes = [C.c_int32]
+_lib.accept_sampled_workspace_bytes.restype = C.c_size_t
 _lib.kv_rollback.argtypes = [C.POINTER(KVCache), C.c_int32]
 _lib.kv_rollback.restype = C.c_int
 _lib.dbf_tiled_bytes.argtypes = [C.c_int64, C.c_int64]
@@ -273,6 +284,34 @@ def accept_prefix(drafts, target, result, eos=None, committed=None, stream=None)
     n_eos = 0 if eos is None else eos.numel()
     _check(_lib.accept_prefix(_ptr(drafts), _ptr(target), K, _ptr(eos), n_eos, _ptr(result),
                               _ptr(committed), _stream(stream)))
+
+
+def sample_tokens_workspace_bytes(M: int, V: int) -> int:
+    return int(_lib.sample_tokens_workspace_bytes(M, V))
+
+
+def sample_tokens(logits, u, token, prob=None, temperature=1.0, ws=None, stream=None) -> None:
+    """One draw per row of logits [M, V] from softmax(logits / T), uniforms u [M]."""
+    M, V = logits.shape
+    _check(_lib.sample_tokens(_ptr(logits), M, V, float(temperature), _ptr(u), _ptr(token), _ptr(prob),
+                              _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)))
+
+
+def accept_sampled_workspace_bytes(V: int) -> int:
+    return int(_lib.accept_sampled_workspace_bytes(V))
+
+
+def accept_sampled(draft_logits, target_logits, draft, u, result, temperature=1.0, eos=None,
+                   committed=None, ws=None, stream=None) -> None:
+    """Sampled acceptance of one drafted token: draft_logits [V], target_logits [2, V],
+    draft [1] int32, u [2] uniforms, result [5] int32."""
+    V = draft_logits.numel()
+    n_eos = 0 if eos is None else eos.numel()
+    _check(_lib.accept_sampled(_ptr(draft_logits), _ptr(target_logits), V, float(temperature),
+                               _ptr(draft), _ptr(u), _ptr(eos), n_eos, _ptr(result), _ptr(committed),
+                               _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream)))
 
 
 def tiled_bytes(N: int, K: int) -> int:
