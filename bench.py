@@ -105,6 +105,11 @@ def main():
                     help="keep projection weights row-major instead of the tiled layout")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step captured in a HIP graph")
+    ap.add_argument("--sampled", action="store_true",
+                    help="MTP workloads: the sampled (speculative-sampling) round instead of the greedy "
+                         "walk -- lm_head logits, sample_tokens for the draft, accept_sampled against "
+                         "seeded target logits")
+    ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after the timed region (counter scale)")
     args = ap.parse_args()
@@ -120,6 +125,10 @@ def main():
     from verifier_block_forward_amd import configs, dbf, synth
 
     cfg = configs.get(args.config)
+    if args.sampled and cfg.kind != "mtp":
+        print("--sampled is the MTP K = 1 round (c2, c4, c4m4); DFlash drafts are verified greedily",
+              file=sys.stderr)
+        sys.exit(2)
     torch.cuda.set_device(0)
     dev = "cuda"
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
@@ -158,6 +167,21 @@ def main():
     drafts = argmax[1:] if cfg.kind == "dflash" else argmax[:1]
     lm_head = w_dev["lm_head"]
     stream = torch.cuda.current_stream()
+    if args.sampled:
+        # the sampled MTP round: the drafter's logits row, one draft drawn from it,
+        # and the speculative-sampling test against the target's logits at the
+        # draft's position and the next (seeded synthetic rows, correlated with the
+        # drafter's as a trained drafter's would be)
+        logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+        rng = np.random.default_rng(cfg.seed + 1000)
+        tl = rng.normal(0.0, 2.0, (2, V)).astype(np.float32)
+        target_logits = torch.from_numpy(tl).to(dev)
+        u_draft = torch.from_numpy(rng.random(M).astype(np.float32)).to(dev)
+        u_acc = torch.from_numpy(rng.random(2).astype(np.float32)).to(dev)
+        draft_tok = torch.empty(M, dtype=torch.int32, device=dev)
+        ws_smp = torch.empty(dbf.sample_tokens_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
+        ws_acc = torch.empty(dbf.accept_sampled_workspace_bytes(V), dtype=torch.uint8, device=dev)
+        smp_ev = []
 
     def step(ev=None):
         if ev is not None:
@@ -165,12 +189,27 @@ def main():
         dbf.draft_block_forward(ccfg, bw, kv, io, ws, stream)
         if ev is not None:
             ev[1].record(stream)
-        dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        dbf.accept_prefix(drafts, target, result, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+        if args.sampled:
+            dbf.lm_head_argmax(h_final, lm_head, argmax, logits, None, ws_head, stream)
+            if ev is not None:
+                ev[2].record(stream)
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            dbf.sample_tokens(logits, u_draft, draft_tok, None, args.temperature, ws_smp, stream)
+            if ev is not None:
+                e[0].record(stream)
+            dbf.accept_sampled(logits[M - 1], target_logits, draft_tok[M - 1:], u_acc, result,
+                               args.temperature, ws=ws_acc, stream=stream)
+            if ev is not None:
+                e[1].record(stream)
+                ev[3] = e[1]
+                smp_ev.append((ev[2], e[0], e[1]))
+        else:
+            dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, stream)
+            if ev is not None:
+                ev[2].record(stream)
+            dbf.accept_prefix(drafts, target, result, stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
         dbf.kv_rollback(kv, R + M)
 
     for _ in range(args.warmup):
@@ -201,8 +240,14 @@ def main():
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream()
             dbf.draft_block_forward(ccfg, bw, kv, io, ws, cs)
-            dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, cs)
-            dbf.accept_prefix(drafts, target, result, stream=cs)
+            if args.sampled:
+                dbf.lm_head_argmax(h_final, lm_head, argmax, logits, None, ws_head, cs)
+                dbf.sample_tokens(logits, u_draft, draft_tok, None, args.temperature, ws_smp, cs)
+                dbf.accept_sampled(logits[M - 1], target_logits, draft_tok[M - 1:], u_acc, result,
+                                   args.temperature, ws=ws_acc, stream=cs)
+            else:
+                dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, cs)
+                dbf.accept_prefix(drafts, target, result, stream=cs)
         dbf.kv_rollback(kv, R + M)
         for _ in range(args.warmup):
             g.replay()
@@ -271,6 +316,24 @@ def main():
                   "accept_result": result.cpu().tolist()},
         "cpu_baseline": cpu,
     }
+    if args.sampled:
+        st = [a.elapsed_time(b) for a, b, _ in smp_ev]
+        at = [b.elapsed_time(c) for _, b, c in smp_ev]
+        # algorithmic bytes: sample_tokens reads each logits row once for its
+        # statistics (the search reads one segment); accept_sampled reads three
+        # rows for statistics and two for the residual sums
+        sb, ab_acc = M * V * 4, 5 * V * 4
+        line["sampled"] = {
+            "temperature": args.temperature,
+            "ms_sample_tokens": round(float(np.mean(st)), 4),
+            "ms_accept_sampled": round(float(np.mean(at)), 4),
+            "bytes_sample_tokens": sb, "bytes_accept_sampled": ab_acc,
+            "gbps_sample_tokens": round(sb / (np.mean(st) * 1e-3) / 1e9, 1),
+            "gbps_accept_sampled": round(ab_acc / (np.mean(at) * 1e-3) / 1e9, 1),
+            "bound": "latency (a few MB per call: 3-4 dependent kernels of a few us)",
+            "logits_written_by_lm_head_bytes": M * V * 4,
+        }
+        line["metric"] = "drafted rows/sec (MTP K=1, sampled acceptance)"
     print(json.dumps(line), flush=True)
 
 
