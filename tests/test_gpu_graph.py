@@ -69,3 +69,45 @@ def test_graph_replay_matches_eager(name):
         for i, (got, want) in enumerate(zip(outs, ref)):
             assert t.equal(got, want), f"{name}: replay {rep}, output {i} differs from the eager step"
         print(f"  replay {rep}: bitwise equal", flush=True)
+
+
+def test_graph_replay_of_the_sampled_round():
+    """sample_tokens and accept_sampled captured in a graph: every replay, with eager
+    work between replays, reproduces the eager results bit for bit."""
+    from verifier_block_forward_amd import dbf
+    t = torch()
+    print("\n[graph] sampled round", flush=True)
+    rng = np.random.default_rng(9)
+    V, M = 50000, 3
+    z = t.from_numpy(rng.normal(0, 3, (M, V)).astype(np.float32)).cuda()
+    zt = t.from_numpy(rng.normal(0, 3, (2, V)).astype(np.float32)).cuda()
+    u = t.from_numpy(rng.random(M).astype(np.float32)).cuda()
+    u2 = t.from_numpy(rng.random(2).astype(np.float32)).cuda()
+    tok = t.empty(M, dtype=t.int32, device="cuda")
+    prob = t.empty(M, dtype=t.float32, device="cuda")
+    res = t.zeros(5, dtype=t.int32, device="cuda")
+    com = t.zeros(2, dtype=t.int32, device="cuda")
+    ws1 = t.empty(dbf.sample_tokens_workspace_bytes(M, V), dtype=t.uint8, device="cuda")
+    ws2 = t.empty(dbf.accept_sampled_workspace_bytes(V), dtype=t.uint8, device="cuda")
+
+    def step(stream):
+        dbf.sample_tokens(z, u, tok, prob, 0.9, ws1, stream)
+        dbf.accept_sampled(z[0], zt, tok[:1], u2, res, 0.9, committed=com, ws=ws2, stream=stream)
+
+    outs = (tok, prob, res, com)
+    step(t.cuda.current_stream())
+    t.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step(t.cuda.current_stream())
+    for rep in range(3):
+        float((t.randn(4096, device="cuda") * 2).sum().item())
+        tok.fill_(-1)
+        prob.fill_(float("nan"))
+        res.fill_(-7)
+        com.fill_(-7)
+        g.replay()
+        t.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(outs, ref)):
+            assert t.equal(got, want), f"replay {rep}, output {i} differs from the eager call"
