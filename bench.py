@@ -304,6 +304,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab["lm_head"],
                      "avg_launch_ms": round(head_avg, 4)},
         "block": {"algorithmic_bytes": ab["total"],
+                  "weights_resident_bytes": bw.resident_bytes(),
                   "gbps_event": round(ab["total"] / (block_total_ms * 1e-3) / 1e9, 1),
                   "gbps_wall": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
                   "ms_draft_block_forward": round(float(np.mean(block_ms)), 4),

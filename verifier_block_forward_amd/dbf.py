@@ -227,6 +227,20 @@ class BlockWeights:
                          layers=self.layers, final_norm=tensor(t.get("final_norm")),
                          embed=tensor(t.get("embed")))
 
+    def resident_bytes(self) -> int:
+        """Bytes of the block's own weights as uploaded ([TENS] page,
+        `DFlashModelTensors::gpu_resident_bytes`: the sum of every tensor's byte
+        length; projections BF16, norms F32). The embedding and lm_head belong to the
+        target, are shared by reference, and are not counted. Tiled weights count
+        their tiled storage."""
+        total = 0
+        for name, x in self.t.items():
+            if x is None or name in ("embed", "lm_head"):
+                continue
+            d = x.data if isinstance(x, Tiled) else x
+            total += d.numel() * d.element_size()
+        return total
+
 
 def make_cache(k, v, seq_len: int) -> KVCache:
     torch = _torch()
