@@ -440,12 +440,15 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
 #ifndef DBF_HEAD_WPE
 #define DBF_HEAD_WPE 2
 #endif
+// weight stages in flight per wave, and k-steps per staged chunk of the hidden
+// rows: 2 and 4 measured best with 8-wave workgroups (A/B in the c1 step against
+// 4/8, 1/8, 2/8, 2/16, 4/16, 4/4 and 3/12)
 #ifndef DBF_HEAD_PIPE
-#define DBF_HEAD_PIPE 4
+#define DBF_HEAD_PIPE 2
 #endif
 constexpr int HEAD_PIPE = DBF_HEAD_PIPE;
 #ifndef DBF_HEAD_XCH
-#define DBF_HEAD_XCH 8
+#define DBF_HEAD_XCH 4
 #endif
 constexpr int HEAD_XCH = DBF_HEAD_XCH;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
 static_assert(HEAD_XCH % HEAD_PIPE == 0, "chunk must hold whole pipeline rounds");
