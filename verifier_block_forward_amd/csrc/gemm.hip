@@ -91,8 +91,10 @@ __device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], 
 #undef DBF_LOAD_STAGE
 }
 
+// weight stages in flight per wave: 3 measured best in the c1 step (A/B against
+// 2, 4 and 6 with the LDS-staged ring at 1-4)
 #ifndef DBF_GEMM_PIPE
-#define DBF_GEMM_PIPE 4
+#define DBF_GEMM_PIPE 3
 #endif
 constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
 
@@ -187,11 +189,12 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
 // share (segment, k-slice) and own consecutive row tiles, so the slice's split
 // activations are read once per workgroup (not once per wave) and each wave's
 // registers hold only weights, in a ring of LPIPE stages. A launch of these
-// kernels asks for tens of MB at once; the ring is kept short (3 stages measured
-// best on MI355X) because more requests in flight only lengthen the queue that
-// the activation loads, which gate the first product, wait in.
+// kernels asks for tens of MB at once; the ring is kept short (2 stages measured
+// best in the c1 step, against 1, 3 and 4) because more requests in flight only
+// lengthen the queue that the activation loads, which gate the first product,
+// wait in.
 #ifndef DBF_LPIPE
-#define DBF_LPIPE 3
+#define DBF_LPIPE 2
 #endif
 constexpr int LPIPE = DBF_LPIPE;
 constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
