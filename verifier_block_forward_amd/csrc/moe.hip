@@ -203,27 +203,71 @@ void launch_moe_swiglu(const MoeSwigluArgs &a, hipStream_t s) {
 
 // x = x1 + sum_slots coef[slot][m] * down_slot + shared_scale[m] * down_shared; then the
 // same outputs as the column kernel (copies, split of x * w, norm partials).
+// The routed sum reads each selected slot's down partials. The row's selected
+// slots come from one wave-wide load of the coefficients per 64 slots and a
+// ballot, and up to MOE_CB slots have their partials loaded together, so a row
+// pays about one memory round trip per MOE_CB experts (and per slice) instead of
+// one per expert. Additions keep the order slot ascending, slice ascending.
+constexpr int MOE_CB = 8;
+
 __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 64 + lane;
-    const bool row_ok = m < a.M;
+    const bool row_ok = m < a.M;  // wave-uniform
     const bool ok = row_ok && k < a.H;
+    const int kc = k < a.H ? k : a.H - 1;  // lanes past H load a valid column, unused
     float v = 0.f;
-    if (ok) {
-        v = a.base[(size_t)m * a.H + k];
+    if (row_ok) {
         const int ns = *a.nslots;
+        const size_t col = (size_t)m * a.H + kc;
+        const size_t pstride = (size_t)16 * a.H;  // between slices
+        // shared expert first: its loads go out with the routed ones
+        const float ysh = a.shared_scale[m] * sum_partials(a.psd, a.ks_sh, 16, a.H, m, kc);
         float y = 0.f;
-        for (int sl = 0; sl < ns; sl++) {
-            const float c = a.coef[(size_t)sl * 16 + m];
-            if (c != 0.f)
-                y += c * sum_partials(a.pd + (size_t)sl * a.ks * 16 * a.H, a.ks, 16, a.H, m, k);
+        for (int s0 = 0; s0 < ns; s0 += 64) {
+            const int sl = s0 + lane;
+            const float c = sl < ns ? a.coef[(size_t)sl * 16 + m] : 0.f;
+            unsigned long long bal = __ballot(c != 0.f);
+            while (bal) {
+                int js[MOE_CB];
+                float cs[MOE_CB];
+                int nb = 0;
+#pragma unroll
+                for (int j = 0; j < MOE_CB; j++) {
+                    js[j] = s0;
+                    cs[j] = 0.f;
+                    if (bal) {
+                        const int b = __ffsll((long long)bal) - 1;
+                        bal &= bal - 1;
+                        js[j] = s0 + b;
+                        cs[j] = __shfl(c, b, 64);
+                        nb = j + 1;
+                    }
+                }
+                float acc[MOE_CB];
+#pragma unroll
+                for (int j = 0; j < MOE_CB; j++) acc[j] = 0.f;
+                for (int t = 0; t < a.ks; t++) {
+                    float x[MOE_CB];
+#pragma unroll
+                    for (int j = 0; j < MOE_CB; j++)
+                        x[j] = a.pd[((size_t)js[j] * a.ks + t) * pstride + col];
+#pragma unroll
+                    for (int j = 0; j < MOE_CB; j++) acc[j] += j < nb ? x[j] : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < MOE_CB; j++)
+                    if (j < nb) y += cs[j] * acc[j];
+            }
         }
-        y += a.shared_scale[m] * sum_partials(a.psd, a.ks_sh, 16, a.H, m, k);
-        v += y;
-        if (a.out) a.out[(size_t)m * a.H + k] = v;
-        if (a.copy0) a.copy0[(size_t)m * a.H + k] = v;
-        if (a.copy1) a.copy1[(size_t)m * a.H + k] = v;
+        y += ysh;
+        if (ok) {
+            v = a.base[(size_t)m * a.H + k] + y;
+            if (a.out) a.out[(size_t)m * a.H + k] = v;
+            if (a.copy0) a.copy0[(size_t)m * a.H + k] = v;
+            if (a.copy1) a.copy1[(size_t)m * a.H + k] = v;
+        }
     }
     if (row_ok && a.ssp_out) {
         const float ss = wave_sum(v * v);
