@@ -42,6 +42,26 @@ __device__ __forceinline__ bf16x8 ldw16(const uint16_t *p) {
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
+// Workgroup order across the XCDs. Workgroups are handed to the 8 XCDs round-robin
+// (hardware index b runs on XCD b % 8), and each XCD has its own L2. With the remap,
+// the logical index of b is its rank within its XCD plus the count of workgroups on
+// lower XCDs, so consecutive logical indices -- which share a k-slice of the
+// activations -- sit on one XCD and its L2. A bijection on [0, n) for any n.
+#ifndef DBF_XCD_REMAP
+#define DBF_XCD_REMAP 1
+#endif
+constexpr int N_XCD = 8;
+__device__ __forceinline__ int xcd_logical(int b, int n) {
+#if DBF_XCD_REMAP
+    const int q = n / N_XCD, r = n % N_XCD;
+    const int x = b % N_XCD, i = b / N_XCD;
+    return x * q + (x < r ? x : r) + i;
+#else
+    (void)n;
+    return b;
+#endif
+}
+
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16((a), (b), (c), 0, 0, 0)
 
 // Accumulate the NA x NB tile product over k-steps [s0, s1), software-pipelined:
@@ -101,7 +121,7 @@ constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
 template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
-    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int unit = xcd_logical(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
     if (unit >= args.total_units) return;
     int si = 0;
 #pragma unroll 1
@@ -203,7 +223,7 @@ template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     extern __shared__ __align__(16) uint4 xl[];  // NB * kslice_steps * 2 KiB (<= LDS_X_BYTES)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wg = blockIdx.x;
+    const int wg = xcd_logical(blockIdx.x, gridDim.x);
     int si = 0;
 #pragma unroll 1
     for (int i = 1; i < args.nseg; i++)
