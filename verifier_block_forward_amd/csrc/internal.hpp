@@ -87,33 +87,38 @@ __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf
 // round trips instead of one per few partials.
 constexpr int PARTIAL_BATCH = 16;
 
-// NV sums sharing ks and the partial stride: out[v] = sum_t base[v][t * stride]
-template <int NV>
+// NV sums sharing ks and the partial stride: out[v] = sum_t base[v][t * stride],
+// loaded B partials at a time. The additions run in increasing t whatever B is.
+template <int NV, int B = PARTIAL_BATCH>
 __device__ __forceinline__ void sum_partials_n(const float *const base[NV], int ks, size_t stride,
                                                float out[NV]) {
 #pragma unroll
     for (int v = 0; v < NV; v++) out[v] = 0.f;
-    for (int t0 = 0; t0 < ks; t0 += PARTIAL_BATCH) {
-        float x[NV][PARTIAL_BATCH];
+    for (int t0 = 0; t0 < ks; t0 += B) {
+        float x[NV][B];
 #pragma unroll
-        for (int u = 0; u < PARTIAL_BATCH; u++) {
+        for (int u = 0; u < B; u++) {
             const int t = t0 + u < ks ? t0 + u : ks - 1;
 #pragma unroll
             for (int v = 0; v < NV; v++) x[v][u] = base[v][(size_t)t * stride];
         }
 #pragma unroll
-        for (int u = 0; u < PARTIAL_BATCH; u++)
+        for (int u = 0; u < B; u++)
 #pragma unroll
             for (int v = 0; v < NV; v++) out[v] += t0 + u < ks ? x[v][u] : 0.f;
     }
 }
 
-// element (row, col) summed over the ks partials of a [ks][rows][N] buffer
+// element (row, col) summed over the ks partials of a [ks][rows][N] buffer. Up to
+// 24 partials (the long-K projections split 22 ways) take one round trip.
 __device__ __forceinline__ float sum_partials(const float *p, int ks, int rows, int N, int row,
                                               int col) {
     const float *b[1] = {p + (size_t)row * N + col};
     float o[1];
-    sum_partials_n<1>(b, ks, (size_t)rows * N, o);
+    if (ks > PARTIAL_BATCH)
+        sum_partials_n<1, 24>(b, ks, (size_t)rows * N, o);
+    else
+        sum_partials_n<1>(b, ks, (size_t)rows * N, o);
     return o[0];
 }
 
