@@ -608,6 +608,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
     const int ngrp = 256 / hd;
     const int d = tid % hd, grp = tid / hd;
     const bool valid = m < a.M;
+    // the gate value goes out with the partial loads instead of after the merge
+    const float gv = valid && a.g && grp == 0 ? a.g[(size_t)m * K + h * hd + d] : 0.f;
     float mr = -INFINITY, lr = 0.f, orun = 0.f;
     if (valid) {
         const size_t stride = (size_t)a.M * a.nq * rec;
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
             lsum += lq * e;
         }
         o = osum / lsum;
-        if (a.g) o *= sigmoidf_(a.g[(size_t)m * K + h * hd + d]);
+        if (a.g) o *= sigmoidf_(gv);
     }
     split_store(a.xs, m, h * hd + d, o);
     if (h == a.nq - 1) {

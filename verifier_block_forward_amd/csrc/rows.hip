@@ -15,13 +15,25 @@
 namespace dbf {
 
 // Row scale from the per-column-block partial sums of squares; called by a whole
-// wavefront (lane-strided sum, then a fixed xor tree).
-__device__ __forceinline__ float row_scale(const float *ssp_row, int ncb, int H, float eps) {
+// wavefront (lane-strided sum, then a fixed xor tree). Split in two so that a
+// kernel can issue the first load (this lane's element of the first 64) together
+// with its other independent loads, and finish the sum after one wait for all.
+__device__ __forceinline__ float row_scale_first(const float *ssp_row, int ncb) {
     const int lane = threadIdx.x & 63;
-    float s = 0.f;
-    for (int i = lane; i < ncb; i += 64) s += ssp_row[i];
+    return lane < ncb ? ssp_row[lane] : 0.f;
+}
+
+__device__ __forceinline__ float row_scale_finish(float first, const float *ssp_row, int ncb, int H,
+                                                  float eps) {
+    const int lane = threadIdx.x & 63;
+    float s = first;
+    for (int i = lane + 64; i < ncb; i += 64) s += ssp_row[i];
     s = wave_sum(s);
     return 1.0f / sqrtf(s / (float)H + eps);
+}
+
+__device__ __forceinline__ float row_scale(const float *ssp_row, int ncb, int H, float eps) {
+    return row_scale_finish(row_scale_first(ssp_row, ncb), ssp_row, ncb, H, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -34,6 +46,12 @@ __device__ __forceinline__ int colsum_row_groups(const ColArgs &a) {
     return a.xs ? 4 : (a.M + 3) / 4;  // split tiles need all 16 rows written
 }
 
+// Input modes: SRC_BASE when the rows come from `base` (or are zero), SRC_ANY for
+// the token gather and the captured-layer gather. The base-only form has no branch
+// joins between its independent loads, so the compiler issues them together.
+constexpr int SRC_ANY = 0, SRC_BASE = 1;
+
+template <int SRC>
 __device__ __forceinline__ void colsum_body(const ColArgs &a) {
     if ((int)blockIdx.x >= (a.H + 63) / 64 || (int)blockIdx.y >= colsum_row_groups(a)) return;
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -41,26 +59,43 @@ __device__ __forceinline__ void colsum_body(const ColArgs &a) {
     const int k = blockIdx.x * 64 + lane;
     const bool row_ok = m < a.M;
     const bool ok = row_ok && k < a.H;
+    // Loads that depend on no other load go out first (this lane's share of the
+    // row-scale partials, the base or gathered value, the token id, the norm
+    // weight), then the split-K partials in one batch, so a single wait covers them
+    // all; the row scales are reduced after it.
+    const bool sc0on = row_ok && a.p0 && a.ssp0, sc1on = row_ok && a.p1 && a.ssp1;
+    const float *sr0 = a.ssp0 + (size_t)m * a.ncb_in, *sr1 = a.ssp1 + (size_t)m * a.ncb_in;
+    float f0 = 0.f, f1 = 0.f, bv = 0.f, wk = 1.f;
+    int tok = 0;
+    if (sc0on) f0 = row_scale_first(sr0, a.ncb_in);
+    if (sc1on) f1 = row_scale_first(sr1, a.ncb_in);
+    if (ok) {
+        if constexpr (SRC == SRC_BASE) {
+            if (a.base) bv = a.base[(size_t)m * a.ldb + k];
+        } else if (a.tokens) {
+            tok = a.tokens[m];
+        } else if (a.base) {
+            bv = a.base[(size_t)m * a.ldb + k];
+        } else if (a.gsrc[0]) {
+            const int t = k / a.gH;
+            bv = a.gsrc[t][(size_t)(a.grow0 + m) * a.gld + (k - t * a.gH)];
+        }
+        if (a.xs && a.w) wk = a.w[k];
+    }
     float v = 0.f;
     if (row_ok) {
-        // the partial sums' loads go out first; the row scales (a wave reduction of
-        // the norm partials) are formed while they are in flight
         float s0 = 0.f, s1 = 0.f;
         if (ok && a.p0) s0 = sum_partials(a.p0, a.ks0, a.rows0, a.H, m, k);
         if (ok && a.p1) s1 = sum_partials(a.p1, a.ks1, a.rows1, a.H, m, k);
         float sc0 = 1.f, sc1 = 1.f;
-        if (a.p0 && a.ssp0) sc0 = row_scale(a.ssp0 + (size_t)m * a.ncb_in, a.ncb_in, a.H, a.eps0);
-        if (a.p1 && a.ssp1) sc1 = row_scale(a.ssp1 + (size_t)m * a.ncb_in, a.ncb_in, a.H, a.eps1);
+        if (sc0on) sc0 = row_scale_finish(f0, sr0, a.ncb_in, a.H, a.eps0);
+        if (sc1on) sc1 = row_scale_finish(f1, sr1, a.ncb_in, a.H, a.eps1);
         if (ok) {
-            if (a.tokens) {
-                int t = a.tokens[m];
-                t = t < 0 ? 0 : (t >= a.V ? a.V - 1 : t);
+            if (SRC != SRC_BASE && a.tokens) {
+                const int t = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
                 v = bf16_to_f32(a.embed[(size_t)t * a.H + k]);
-            } else if (a.base) {
-                v = a.base[(size_t)m * a.ldb + k];
-            } else if (a.gsrc[0]) {
-                const int t = k / a.gH;
-                v = a.gsrc[t][(size_t)(a.grow0 + m) * a.gld + (k - t * a.gH)];
+            } else {
+                v = bv;  // base or gathered value (0 when neither is given)
             }
             if (a.p0) v += sc0 * s0;
             if (a.p1) v += sc1 * s1;
@@ -73,15 +108,16 @@ __device__ __forceinline__ void colsum_body(const ColArgs &a) {
             if (lane == 0) a.ssp_out[(size_t)m * a.ncb_out + blockIdx.x] = ss;
         }
     }
-    if (a.xs && k < ((a.H + 31) & ~31)) split_store(a.xs, m, k, ok ? v * (a.w ? a.w[k] : 1.f) : 0.f);
+    if (a.xs && k < ((a.H + 31) & ~31)) split_store(a.xs, m, k, ok ? v * wk : 0.f);
 }
 
-__global__ __launch_bounds__(256) void k_colsum(ColArgs a) { colsum_body(a); }
+template <int SRC>
+__global__ __launch_bounds__(256) void k_colsum(ColArgs a) { colsum_body<SRC>(a); }
 
 // two independent column jobs in one launch (blockIdx.z selects the job)
 __global__ __launch_bounds__(256) void k_colsum2(ColArgs a0, ColArgs a1) {
-    if (blockIdx.z == 0) colsum_body(a0);
-    else colsum_body(a1);
+    if (blockIdx.z == 0) colsum_body<SRC_ANY>(a0);
+    else colsum_body<SRC_ANY>(a1);
 }
 
 static dim3 colsum_grid(const ColArgs &a) {
@@ -89,7 +125,10 @@ static dim3 colsum_grid(const ColArgs &a) {
 }
 
 void launch_colsum(const ColArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_colsum, colsum_grid(a), dim3(256), 0, s, a);
+    if (!a.tokens && !a.gsrc[0])
+        hipLaunchKernelGGL(k_colsum<SRC_BASE>, colsum_grid(a), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_colsum<SRC_ANY>, colsum_grid(a), dim3(256), 0, s, a);
 }
 
 void launch_colsum2(const ColArgs &a0, const ColArgs &a1, hipStream_t s) {
@@ -105,8 +144,11 @@ __global__ __launch_bounds__(256) void k_final_norm(const float *x, const float 
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     if (m >= M) return;
-    const float s = row_scale(ssp + (size_t)m * ncb, ncb, H, eps);
-    if (k < H) out[(size_t)m * H + k] = x[(size_t)m * H + k] * s * w[k];
+    const float *sr = ssp + (size_t)m * ncb;
+    const float f = row_scale_first(sr, ncb);  // in flight with the row and weight loads
+    const float xv = k < H ? x[(size_t)m * H + k] : 0.f, wv = k < H ? w[k] : 0.f;
+    const float s = row_scale_finish(f, sr, ncb, H, eps);
+    if (k < H) out[(size_t)m * H + k] = xv * s * wv;
 }
 
 void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
@@ -173,6 +215,18 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
     }
     const size_t stride = (size_t)rows * N;
     const size_t rowoff = (size_t)prow * N + (size_t)head * hd + lane;
+    // the row-scale share, the head-norm weights and the RoPE frequencies go out
+    // with the partials (one wait)
+    const float f = row_scale_first(sspr, a.ncb);
+    const int half = a.rotary_dim / 2;
+    float wnv[CPL];
+    double ifr[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+        const int d = lane + 64 * i;
+        wnv[i] = wn[d];
+        ifr[i] = d < 2 * half ? a.inv_freq[d < half ? d : d - half] : 0.0;
+    }
     float raw[CPL], side[CPL] = {};
     if (src2 && ks2 == ks) {
         const float *bb[2 * CPL];
@@ -199,7 +253,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
             sum_partials_n<CPL>(bb, ks2, stride, side);
         }
     }
-    const float s = row_scale(sspr, a.ncb, a.H, a.eps);  // while the partials arrive
+    const float s = row_scale_finish(f, sspr, a.ncb, a.H, a.eps);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; i++) {
@@ -211,10 +265,9 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
 #pragma unroll
     for (int i = 0; i < CPL; i++) {
         const int d = lane + 64 * i;
-        vec[d] = raw[i] * hs * wn[d];
+        vec[d] = raw[i] * hs * wnv[i];
     }
     __syncthreads();
-    const int half = a.rotary_dim / 2;
     const size_t cache_off = ((size_t)head * a.capacity + pos) * hd;
     const double two_pi = 6.283185307179586;
 #pragma unroll
@@ -222,9 +275,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
         const int d = lane + 64 * i;
         float val = vec[d];
         if (d < 2 * half) {
-            const int j = d < half ? d : d - half;
             const float pv = vec[d < half ? d + half : d - half];
-            const double ang = (double)pos * a.inv_freq[j];
+            const double ang = (double)pos * ifr[i];
             const double red = fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);  // |red| <= pi
             float sv, c;
             sincosf((float)red, &sv, &c);
@@ -261,8 +313,10 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
     const int Ip = (a.I + 31) & ~31;
     float h = 0.f;
     if (m < a.M) {
+        const float *sr = a.ssp + (size_t)m * a.ncb;
+        const float f = row_scale_first(sr, a.ncb);  // in flight with the partials
         float g = 0.f, u = 0.f;
-        if (k < a.I) {  // partial loads first, row scale while they are in flight
+        if (k < a.I) {
             if (a.ksg == a.ksu) {
                 const size_t off = (size_t)m * a.I + k;
                 const float *b[2] = {a.pg + off, a.pu + off};
@@ -275,7 +329,7 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
                 u = sum_partials(a.pu, a.ksu, 16, a.I, m, k);
             }
         }
-        const float s = row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
+        const float s = row_scale_finish(f, sr, a.ncb, a.H, a.eps);
         if (k < a.I) {
             g *= s;
             u *= s;
