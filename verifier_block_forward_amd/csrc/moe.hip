@@ -21,10 +21,19 @@
 
 namespace dbf {
 
-__device__ __forceinline__ float moe_row_scale(const float *ssp_row, int ncb, int H, float eps) {
+// Row scale from the norm partials, in two halves: the first load (this lane's
+// element of the first 64) goes out with a kernel's other independent loads, and
+// the lane-strided sum and its fixed xor tree follow after one wait.
+__device__ __forceinline__ float moe_scale_first(const float *ssp_row, int ncb) {
     const int lane = threadIdx.x & 63;
-    float s = 0.f;
-    for (int i = lane; i < ncb; i += 64) s += ssp_row[i];
+    return lane < ncb ? ssp_row[lane] : 0.f;
+}
+
+__device__ __forceinline__ float moe_scale_finish(float first, const float *ssp_row, int ncb, int H,
+                                                  float eps) {
+    const int lane = threadIdx.x & 63;
+    float s = first;
+    for (int i = lane + 64; i < ncb; i += 64) s += ssp_row[i];
     s = wave_sum(s);
     return 1.0f / sqrtf(s / (float)H + eps);
 }
@@ -61,20 +70,27 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
     const int E = a.E, K = a.top_k, M = a.M;
     const int rg = ROUTE_Z / E < ROUTE_WAVES ? ROUTE_Z / E : ROUTE_WAVES;  // >= 8
     for (int e = tid; e < E; e += ROUTE_THREADS) used[e] = 0;
-    // row scale and shared-expert gate, one wave per row
+    // row scale and shared-expert gate, one wave per row: the norm partials and the
+    // gate's split-K partials load together; the scale is finished after the first
+    // pass's router sums (rows <= 16 = ROUTE_WAVES, so one wave per row)
+    const float *sr = a.ssp + (size_t)(wv < M ? wv : 0) * a.ncb;
+    float f = 0.f, gsum = 0.f;
     if (wv < M) {
-        const float s = moe_row_scale(a.ssp + (size_t)wv * a.ncb, a.ncb, a.H, a.eps);
-        const float g = s * sum_partials(a.p_sgi, a.ks_sgi, 16, 1, wv, 0);
-        if (lane == 0) {
-            rscale[wv] = s;
-            a.shared_scale[wv] = sigmoidf_(g);
-        }
+        f = moe_scale_first(sr, a.ncb);
+        gsum = sum_partials(a.p_sgi, a.ks_sgi, 16, 1, wv, 0);
     }
     for (int m0 = 0; m0 < M; m0 += rg) {
         const int rows = M - m0 < rg ? M - m0 : rg;
         for (int i = tid; i < rows * E; i += ROUTE_THREADS) {
             const int r = i / E;
             z[i] = sum_partials(a.p_router, a.ks_router, 16, E, m0 + r, i - r * E);
+        }
+        if (m0 == 0 && wv < M) {
+            const float s = moe_scale_finish(f, sr, a.ncb, a.H, a.eps);
+            if (lane == 0) {
+                rscale[wv] = s;
+                a.shared_scale[wv] = sigmoidf_(s * gsum);
+            }
         }
         __syncthreads();
         if (wv < rows) {
@@ -143,11 +159,12 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
     }
     if (tid == 0) *a.nslots = total;
     __syncthreads();
-    // coefficient of (slot, row): the row's weight for the slot's expert, else 0
-    for (int i = tid; i < total * 16; i += ROUTE_THREADS) {
+    // coefficient of (slot, row): the row's weight for the slot's expert, else 0;
+    // slots past the touched ones get 0, so a reader needs no slot count
+    for (int i = tid; i < a.max_slots * 16; i += ROUTE_THREADS) {
         const int sl = i >> 4, m = i & 15;
         float c = 0.f;
-        if (m < M) {
+        if (sl < total && m < M) {
             const int e = sexp[sl];
             for (int t = 0; t < K; t++)
                 if (esel[m * DBF_MAX_TOPK_DEV + t] == e) c = wsel[m * DBF_MAX_TOPK_DEV + t];
@@ -166,15 +183,19 @@ void launch_moe_route(const MoeRouteArgs &a, hipStream_t s) {
 __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
     const int slot = blockIdx.z;
     const bool shared = slot == a.max_slots;
-    if (!shared && slot >= *a.nslots) return;
+    // the slot count, the row-scale share and the partials load together: a slot
+    // past the count reads its (allocated, unused) partials and leaves afterwards
+    const int ns = shared ? 0 : *a.nslots;
     const int I = shared ? a.Is : a.Ie;
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     const int Ip = (I + 31) & ~31;
     float h = 0.f;
+    const float *sr = a.ssp + (size_t)(m < a.M ? m : 0) * a.ncb;
+    const float f = m < a.M ? moe_scale_first(sr, a.ncb) : 0.f;
     if (m < a.M) {
         float g = 0.f, u = 0.f;
-        if (k < I) {  // partial loads first; the row scale forms while they arrive
+        if (k < I) {
             const float *pg = shared ? a.psg : a.pg + (size_t)slot * a.ks * 16 * I;
             const float *pu = shared ? a.psu : a.pu + (size_t)slot * a.ks * 16 * I;
             const size_t off = (size_t)m * I + k;
@@ -185,13 +206,14 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
             u = o[1];
         }
         // whole wave (wave-uniform m) forms the row scale: no lane has left yet
-        const float s = moe_row_scale(a.ssp + (size_t)m * a.ncb, a.ncb, a.H, a.eps);
+        const float s = moe_scale_finish(f, sr, a.ncb, a.H, a.eps);
         if (k < I) {
             g *= s;
             u *= s;
             h = g / (1.0f + expf(-g)) * u;
         }
     }
+    if (!shared && slot >= ns) return;  // whole block: slot is uniform
     uint16_t *xs = shared ? a.xs_sh : a.xs_e + (size_t)slot * (split_tile_bytes(a.Ie) / 2);
     if (k < Ip) split_store(xs, m, k, h);
 }
@@ -218,8 +240,11 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
     const bool ok = row_ok && k < a.H;
     const int kc = k < a.H ? k : a.H - 1;  // lanes past H load a valid column, unused
     float v = 0.f;
+    // the base value and the norm weight go out with the first loads
+    const float bv = ok ? a.base[(size_t)m * a.H + k] : 0.f;
+    const float wk = ok && a.xs && a.w ? a.w[k] : 1.f;
     if (row_ok) {
-        const int ns = *a.nslots;
+        const int ns = a.max_slots;  // coefficients past the touched slots are 0
         const size_t col = (size_t)m * a.H + kc;
         const size_t pstride = (size_t)16 * a.H;  // between slices
         // shared expert first: its loads go out with the routed ones
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
         }
         y += ysh;
         if (ok) {
-            v = a.base[(size_t)m * a.H + k] + y;
+            v = bv + y;
             if (a.out) a.out[(size_t)m * a.H + k] = v;
             if (a.copy0) a.copy0[(size_t)m * a.H + k] = v;
             if (a.copy1) a.copy1[(size_t)m * a.H + k] = v;
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
         const float ss = wave_sum(v * v);
         if (lane == 0) a.ssp_out[(size_t)m * a.ncb + blockIdx.x] = ss;
     }
-    if (a.xs && k < ((a.H + 31) & ~31)) split_store(a.xs, m, k, ok ? v * (a.w ? a.w[k] : 1.f) : 0.f);
+    if (a.xs && k < ((a.H + 31) & ~31)) split_store(a.xs, m, k, ok ? v * wk : 0.f);
 }
 
 void launch_moe_combine(const MoeCombineArgs &a, hipStream_t s) {
