@@ -121,12 +121,23 @@ constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
 template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
-    const int unit = xcd_logical(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
-    if (unit >= args.total_units) return;
+    // wave index through readfirstlane: the unit, the segment lookup and the
+    // segment's fields are then scalar (kernel-argument loads, not vector loads)
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    int ub[GEMM_MAXSEG];  // every segment boundary, loaded with the grid size
+#pragma unroll
+    for (int i = 0; i < GEMM_MAXSEG; i++) ub[i] = args.seg[i].unit_begin;
+    const int nblk = gridDim.x, nseg = args.nseg, total = args.total_units;
+    __builtin_amdgcn_sched_barrier(0);  // keep those loads ahead of their first use: one trip
+    const int unit = xcd_logical(blockIdx.x, nblk) * 4 + wv;
     int si = 0;
-#pragma unroll 1
-    for (int i = 1; i < args.nseg; i++)
-        if (unit >= args.seg[i].unit_begin) si = i;
+#pragma unroll
+    for (int i = 1; i < GEMM_MAXSEG; i++)
+        if (i < nseg && unit >= ub[i]) si = i;
+    // segment chosen before the exit test, so the boundary loads are not sunk below
+    // it into a second round trip
+    asm volatile("" : "+s"(si));
+    if (unit >= total) return;
     const GemmSeg &sg = args.seg[si];
     int local = unit - sg.unit_begin;
     const uint16_t *Wbase = sg.W;
@@ -223,11 +234,16 @@ template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     extern __shared__ __align__(16) uint4 xl[];  // NB * kslice_steps * 2 KiB (<= LDS_X_BYTES)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int wg = xcd_logical(blockIdx.x, gridDim.x);
+    int ub[GEMM_MAXSEG];  // every segment boundary, loaded with the grid size
+#pragma unroll
+    for (int i = 0; i < GEMM_MAXSEG; i++) ub[i] = args.seg[i].unit_begin;
+    const int nblk = gridDim.x, nseg = args.nseg;
+    __builtin_amdgcn_sched_barrier(0);  // keep those loads ahead of their first use: one trip
+    const int wg = xcd_logical(blockIdx.x, nblk);
     int si = 0;
-#pragma unroll 1
-    for (int i = 1; i < args.nseg; i++)
-        if (wg >= args.seg[i].unit_begin) si = i;
+#pragma unroll
+    for (int i = 1; i < GEMM_MAXSEG; i++)
+        if (i < nseg && wg >= ub[i]) si = i;
     const GemmSeg &sg = args.seg[si];
     int local = wg - sg.unit_begin;  // workgroup units: (tile group, ks) per slot
     const int groups = (sg.tiles + 3) / 4;
