@@ -328,6 +328,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // are issued before the queries are staged, so their latency overlaps the staging.
 template <int HD, int QT, bool KVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD, QT, KVB>()))) void k_attn(AttnArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.q), "s"(a.cache_k), "s"(a.cache_v), "s"(a.kv_bf16), "s"(a.capacity),
+                 "s"(a.n_ctx), "s"(a.M), "s"(a.nq), "s"(a.nkv), "s"(a.chunk), "s"(a.bidir), "s"(a.part));
     using L = AttnLds<HD, QT, KVB>;
     constexpr int S = L::S, DT = L::DT, VTW = L::VTW;
     constexpr int PF = attn_prefetch<HD, KVB>();
@@ -602,6 +605,8 @@ void launch_attn(const AttnArgs &a, hipStream_t s) {
 constexpr int CMB_BATCH = 16;
 
 __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.part), "s"(a.n_chunks), "s"(a.M), "s"(a.nq), "s"(a.hd), "s"(a.g), "s"(a.xs));
     __shared__ float sm_m[256], sm_l[256], sm_o[256];
     const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int hd = a.hd, K = a.nq * hd, rec = hd + ATT_PART_EXTRA;
@@ -680,6 +685,8 @@ void launch_attn_combine(const CombineArgs &a, hipStream_t s) {
 __global__ __launch_bounds__(64) void k_accept(const int32_t *d, const int32_t *t, int K,
                                                const int32_t *eos, int n_eos, int32_t *res,
                                                int32_t *committed) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(d), "s"(t), "s"(K), "s"(eos), "s"(n_eos), "s"(res), "s"(committed));
     const int lane = threadIdx.x;
     int a = K;
     for (int base = 0; base < K; base += 64) {

@@ -543,6 +543,8 @@ __device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[H
 __global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WPE))) void k_head(
     const uint16_t *__restrict__ W, int tiled, const float *__restrict__ h, int V, int K, int M,
     float *__restrict__ logits, float4 *__restrict__ part, int units) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(W), "s"(tiled), "s"(h), "s"(V), "s"(K), "s"(M), "s"(logits), "s"(part), "s"(units));
     constexpr int NA = HEAD_NA, PIPE = HEAD_PIPE;
     constexpr int CHE = HEAD_XCH * 2 * 64 * 8;  // elements of one staged chunk
     __shared__ __align__(16) uint16_t xbuf[2][CHE];
@@ -704,6 +706,8 @@ void launch_tile(const uint16_t *src, uint16_t *dst, long long batch, int N, int
 __global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ part, int blocks,
                                                      int32_t *__restrict__ argmax,
                                                      float *__restrict__ margin) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(part), "s"(blocks), "s"(argmax), "s"(margin));
     const int m = blockIdx.x;
     Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
     const float4 *pm = part + (size_t)m * blocks;

@@ -80,6 +80,14 @@ __device__ __forceinline__ float block_sum_256(float v, float *sh4) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Kernel arguments are read with scalar loads, and the compiler fetches each one
+// where a branch first needs it, so a kernel that tests several pointers pays a
+// chain of dependent scalar round trips before its first global load. The row
+// kernels therefore start with an empty asm statement that takes every argument
+// they read as an "s" (scalar register) operand: all the loads go out together and
+// one wait covers them. One statement per kernel, not one per value: separate
+// statements were scheduled one wait apart in some kernels.
+
 // Split-K partial sums. A projection writes its ks partial products as
 // [ks][rows][N] F32; consumers add them in increasing ks order. The loads go out
 // in batches of PARTIAL_BATCH (indexes past ks re-read the last partial and are

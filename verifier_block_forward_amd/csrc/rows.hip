@@ -53,6 +53,17 @@ constexpr int SRC_ANY = 0, SRC_BASE = 1;
 
 template <int SRC>
 __device__ __forceinline__ void colsum_body(const ColArgs &a) {
+    // the arguments into scalar registers in one round trip
+    if constexpr (SRC == SRC_BASE)
+        asm volatile("" ::"s"(a.M), "s"(a.H), "s"(a.base), "s"(a.ldb), "s"(a.p0), "s"(a.ks0), "s"(a.rows0),
+                     "s"(a.ssp0), "s"(a.eps0), "s"(a.p1), "s"(a.ks1), "s"(a.rows1), "s"(a.ssp1), "s"(a.eps1),
+                     "s"(a.ncb_in), "s"(a.out), "s"(a.copy0), "s"(a.copy1), "s"(a.w), "s"(a.xs),
+                     "s"(a.ssp_out), "s"(a.ncb_out));
+    else
+        asm volatile("" ::"s"(a.M), "s"(a.H), "s"(a.base), "s"(a.ldb), "s"(a.p0), "s"(a.ks0), "s"(a.rows0),
+                     "s"(a.ssp0), "s"(a.eps0), "s"(a.p1), "s"(a.ks1), "s"(a.rows1), "s"(a.ssp1), "s"(a.eps1),
+                     "s"(a.ncb_in), "s"(a.out), "s"(a.copy0), "s"(a.copy1), "s"(a.w), "s"(a.xs),
+                     "s"(a.ssp_out), "s"(a.ncb_out), "s"(a.tokens), "s"(a.embed), "s"(a.V));
     if ((int)blockIdx.x >= (a.H + 63) / 64 || (int)blockIdx.y >= colsum_row_groups(a)) return;
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -139,8 +150,10 @@ void launch_colsum2(const ColArgs &a0, const ColArgs &a1, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Final norm: h_final = x * s_m (.) w.
-__global__ __launch_bounds__(256) void k_final_norm(const float *x, const float *ssp, int ncb, int M,
-                                                    int H, const float *w, float eps, float *out) {
+__global__ __launch_bounds__(256) void k_final_norm(const float *x, const float *ssp, const float *w,
+                                                    float *out, int ncb, int M, int H, float eps) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(x), "s"(ssp), "s"(w), "s"(out), "s"(ncb), "s"(M), "s"(H), "s"(eps));
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     if (m >= M) return;
@@ -154,8 +167,8 @@ __global__ __launch_bounds__(256) void k_final_norm(const float *x, const float 
 void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
                        float *out, hipStream_t s) {
     const int ncb = (H + 63) / 64;
-    hipLaunchKernelGGL(k_final_norm, dim3(ncb, (M + 3) / 4), dim3(256), 0, s, x, ssp, ncb, M, H, w,
-                       eps, out);
+    hipLaunchKernelGGL(k_final_norm, dim3(ncb, (M + 3) / 4), dim3(256), 0, s, x, ssp, w, out, ncb, M, H,
+                       eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -173,6 +186,12 @@ void launch_final_norm(const float *x, const float *ssp, int M, int H, const flo
 // rows first. DFlash context rows sit at positions P0+r, block rows at P0+R+m.
 template <int CPL>
 __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.pq), "s"(a.pk), "s"(a.pv), "s"(a.pg), "s"(a.ksq), "s"(a.ksk), "s"(a.ksv),
+                 "s"(a.ksg), "s"(a.rows_kv), "s"(a.kv_block_row0), "s"(a.ssp_x), "s"(a.ssp_ctx),
+                 "s"(a.ncb), "s"(a.H), "s"(a.q_norm), "s"(a.k_norm), "s"(a.eps), "s"(a.rotary_dim),
+                 "s"(a.M), "s"(a.R), "s"(a.nq), "s"(a.nkv), "s"(a.P0), "s"(a.q_out), "s"(a.g_out),
+                 "s"(a.cache_k), "s"(a.cache_v), "s"(a.kv_bf16), "s"(a.capacity));
     __shared__ float vec[64 * CPL];
     const int lane = threadIdx.x;
     const int hd = 64 * CPL, qt = a.nq * hd, kt = a.nkv * hd;
@@ -308,6 +327,9 @@ void launch_qkv_post(const QkvPostArgs &a, hipStream_t s) {
 // SwiGLU: h = silu(s_m * sum P_gate) * (s_m * sum P_up), split for the down
 // projection (s_m: RMSNorm scale of the FFN input row).
 __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.pg), "s"(a.pu), "s"(a.ksg), "s"(a.ksu), "s"(a.ssp), "s"(a.ncb), "s"(a.H),
+                 "s"(a.eps), "s"(a.M), "s"(a.I), "s"(a.xs));
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     const int Ip = (a.I + 31) & ~31;
