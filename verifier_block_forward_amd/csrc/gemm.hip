@@ -146,9 +146,13 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     if (sg.slots > 0) {  // grouped: this unit's matrix is the slot's expert
         const int per = sg.tiles * sg.ksplit;
         const int slot = local / per;
-        if (slot >= *sg.nslots) return;
+        // the slot count and the slot's expert load together (slot < slots, so the
+        // entry is in bounds; it is used only for a slot below the count)
+        const int ns = *sg.nslots, ex = sg.slot_expert[slot];
+        asm volatile("" ::"s"(ns), "s"(ex));
+        if (slot >= ns) return;
         local -= slot * per;
-        Wbase += (size_t)sg.slot_expert[slot] * (size_t)sg.w_stride;
+        Wbase += (size_t)ex * (size_t)sg.w_stride;
         xsb0 += (size_t)slot * (size_t)sg.xs_stride;
         outb += (size_t)slot * (size_t)sg.out_stride;
     }
@@ -253,9 +257,13 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     if (sg.slots > 0) {
         const int per = groups * sg.ksplit;
         const int slot = local / per;
-        if (slot >= *sg.nslots) return;  // whole workgroup leaves together
+        // the slot count and the slot's expert load together (slot < slots, so the
+        // entry is in bounds; it is used only for a slot below the count)
+        const int ns = *sg.nslots, ex = sg.slot_expert[slot];
+        asm volatile("" ::"s"(ns), "s"(ex));
+        if (slot >= ns) return;  // whole workgroup leaves together
         local -= slot * per;
-        Wbase += (size_t)sg.slot_expert[slot] * (size_t)sg.w_stride;
+        Wbase += (size_t)ex * (size_t)sg.w_stride;
         xsb0 += (size_t)slot * (size_t)sg.xs_stride;
         outb += (size_t)slot * (size_t)sg.out_stride;
     }

@@ -59,6 +59,10 @@ constexpr int ROUTE_Z = 8192;               // router logits held in LDS per pas
 constexpr int ROUTE_EPL = 1024 / 64;        // experts per lane at E = 1024
 
 __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.p_router), "s"(a.ks_router), "s"(a.p_sgi), "s"(a.ks_sgi), "s"(a.ssp), "s"(a.ncb),
+                 "s"(a.H), "s"(a.eps), "s"(a.M), "s"(a.E), "s"(a.top_k), "s"(a.max_slots), "s"(a.nslots),
+                 "s"(a.slot_expert), "s"(a.coef), "s"(a.shared_scale), "s"(a.sel));
     __shared__ float z[ROUTE_Z];            // unscaled router sums, [pass row][E]
     __shared__ float rscale[16];
     __shared__ unsigned char used[1024];
@@ -181,6 +185,10 @@ void launch_moe_route(const MoeRouteArgs &a, hipStream_t s) {
 // split for the down projections. Grid (cols/64, 4 row groups, max_slots + 1); the
 // last z-slice is the shared expert.
 __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.pg), "s"(a.pu), "s"(a.ks), "s"(a.psg), "s"(a.psu), "s"(a.ks_sh), "s"(a.ssp),
+                 "s"(a.ncb), "s"(a.H), "s"(a.eps), "s"(a.M), "s"(a.Ie), "s"(a.Is), "s"(a.max_slots),
+                 "s"(a.nslots), "s"(a.xs_e), "s"(a.xs_sh));
     const int slot = blockIdx.z;
     const bool shared = slot == a.max_slots;
     // the slot count, the row-scale share and the partials load together: a slot
@@ -233,6 +241,10 @@ void launch_moe_swiglu(const MoeSwigluArgs &a, hipStream_t s) {
 constexpr int MOE_CB = 8;
 
 __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.base), "s"(a.pd), "s"(a.ks), "s"(a.psd), "s"(a.ks_sh), "s"(a.coef),
+                 "s"(a.shared_scale), "s"(a.M), "s"(a.H), "s"(a.max_slots), "s"(a.out), "s"(a.copy0),
+                 "s"(a.copy1), "s"(a.w), "s"(a.xs), "s"(a.ssp_out), "s"(a.ncb));
     const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 64 + lane;
