@@ -301,15 +301,15 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
 
     bf16x8 wb[LPIPE][NA];
     const bool tiled = sg.tiled;
+    // Loads only: columns past K (row-major weights) re-read column 0 here and are
+    // zeroed where the stage is consumed. A select right after the load made the
+    // compiler wait for every load in flight at the end of each ring pass.
 #define DBF_LOAD_W(u, step)                                                     \
     do {                                                                        \
         const int sc_ = (step) < s1 ? (step) : s1 - 1;                          \
         const bool in_ = tiled || 32 * sc_ + 8 * g < K;                         \
         const int col_ = in_ ? wstep * sc_ : 0;                                 \
-        _Pragma("unroll") for (int a = 0; a < NA; a++) {                        \
-            const bf16x8 v_ = ldw16(wrow[a] + col_);                            \
-            wb[u][a] = in_ ? v_ : zero8();                                      \
-        }                                                                       \
+        _Pragma("unroll") for (int a = 0; a < NA; a++) wb[u][a] = ldw16(wrow[a] + col_); \
     } while (0)
     // Stage the activation slice (per tile, steps [s0, s1) are contiguous, 2 KiB each):
     // this thread's share is loaded first, the weight ring is issued behind it, and
@@ -346,6 +346,10 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
         for (int u = 0; u < LPIPE; u++) {
             const int j = base + u;
             if (j < n) {
+                const bool in_ = tiled || 32 * (s0 + j) + 8 * g < K;
+                bf16x8 w[NA];
+#pragma unroll
+                for (int a = 0; a < NA; a++) w[a] = in_ ? wb[u][a] : zero8();
 #pragma unroll
                 for (int b = 0; b < NB; b++) {
                     if (b >= nb) continue;
@@ -353,8 +357,8 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
                     const bf16x8 xlo = __builtin_bit_cast(bf16x8, xl[b * per + (j * 2 + 1) * 64 + lane]);
 #pragma unroll
                     for (int a = 0; a < NA; a++) {
-                        acc[a][b] = MFMA(wb[u][a], xh, acc[a][b]);
-                        acc[a][b] = MFMA(wb[u][a], xlo, acc[a][b]);
+                        acc[a][b] = MFMA(w[a], xh, acc[a][b]);
+                        acc[a][b] = MFMA(w[a], xlo, acc[a][b]);
                     }
                 }
             }
