@@ -337,7 +337,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
     __shared__ __align__(16) unsigned char smem[L::BYTES];
     uint4 *qsm = (uint4 *)smem;
 
-    const int w = threadIdx.x >> 6;
+    // scalar wave index: the key range, the sub-tile count and every branch on them
+    // are then scalar (no exec-mask branches around the reloads)
+    const int w = wave_id();
     const int lane = threadIdx.x & 63;
     uint16_t *vth = (uint16_t *)(smem + L::Q_BYTES + (KVB ? w * L::VPLANE : 0));  // BF16 caches
     const int r16 = lane & 15, g = lane >> 4;

@@ -121,9 +121,9 @@ constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
 template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
-    // wave index through readfirstlane: the unit, the segment lookup and the
-    // segment's fields are then scalar (kernel-argument loads, not vector loads)
-    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // scalar wave index: the unit, the segment lookup and the segment's fields are
+    // then scalar (kernel-argument loads, not vector loads)
+    const int wv = wave_id();
     int ub[GEMM_MAXSEG];  // every segment boundary, loaded with the grid size
 #pragma unroll
     for (int i = 0; i < GEMM_MAXSEG; i++) ub[i] = args.seg[i].unit_begin;
@@ -237,7 +237,7 @@ constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 K
 template <int NA, int NB>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     extern __shared__ __align__(16) uint4 xl[];  // NB * kslice_steps * 2 KiB (<= LDS_X_BYTES)
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     int ub[GEMM_MAXSEG];  // every segment boundary, loaded with the grid size
 #pragma unroll
     for (int i = 0; i < GEMM_MAXSEG; i++) ub[i] = args.seg[i].unit_begin;
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(DB
     constexpr int CHE = HEAD_XCH * 2 * 64 * 8;  // elements of one staged chunk
     __shared__ __align__(16) uint16_t xbuf[2][CHE];
     __shared__ Top2 wrec[HEAD_WAVES][16];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int unit = blockIdx.x * HEAD_WAVES + wv;
     const bool active = unit < units;
     const int r = lane & 15, g = lane >> 4;

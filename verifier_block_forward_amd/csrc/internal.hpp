@@ -80,6 +80,11 @@ __device__ __forceinline__ float block_sum_256(float v, float *sh4) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// This thread's wavefront within the workgroup, as a value the compiler knows to
+// be uniform across the wave (readfirstlane): indexes and branches derived from it
+// stay in scalar registers instead of vector registers and exec-mask branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Kernel arguments are read with scalar loads, and the compiler fetches each one
 // where a branch first needs it, so a kernel that tests several pointers pays a
 // chain of dependent scalar round trips before its first global load. The row

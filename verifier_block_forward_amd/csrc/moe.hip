@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
     // past the count reads its (allocated, unused) partials and leaves afterwards
     const int ns = shared ? 0 : *a.nslots;
     const int I = shared ? a.Is : a.Ie;
-    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int m = blockIdx.y * 4 + wave_id();
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     const int Ip = (I + 31) & ~31;
     float h = 0.f;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
     asm volatile("" ::"s"(a.base), "s"(a.pd), "s"(a.ks), "s"(a.psd), "s"(a.ks_sh), "s"(a.coef),
                  "s"(a.shared_scale), "s"(a.M), "s"(a.H), "s"(a.max_slots), "s"(a.out), "s"(a.copy0),
                  "s"(a.copy1), "s"(a.w), "s"(a.xs), "s"(a.ssp_out), "s"(a.ncb));
-    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int m = blockIdx.y * 4 + wave_id();
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 64 + lane;
     const bool row_ok = m < a.M;  // wave-uniform

@@ -65,7 +65,7 @@ __device__ __forceinline__ void colsum_body(const ColArgs &a) {
                      "s"(a.ncb_in), "s"(a.out), "s"(a.copy0), "s"(a.copy1), "s"(a.w), "s"(a.xs),
                      "s"(a.ssp_out), "s"(a.ncb_out), "s"(a.tokens), "s"(a.embed), "s"(a.V));
     if ((int)blockIdx.x >= (a.H + 63) / 64 || (int)blockIdx.y >= colsum_row_groups(a)) return;
-    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int m = blockIdx.y * 4 + wave_id();
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 64 + lane;
     const bool row_ok = m < a.M;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void k_final_norm(const float *x, const float 
                                                     float *out, int ncb, int M, int H, float eps) {
     // the arguments into scalar registers in one round trip
     asm volatile("" ::"s"(x), "s"(ssp), "s"(w), "s"(out), "s"(ncb), "s"(M), "s"(H), "s"(eps));
-    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int m = blockIdx.y * 4 + wave_id();
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     if (m >= M) return;
     const float *sr = ssp + (size_t)m * ncb;
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
     // the arguments into scalar registers in one round trip
     asm volatile("" ::"s"(a.pg), "s"(a.pu), "s"(a.ksg), "s"(a.ksu), "s"(a.ssp), "s"(a.ncb), "s"(a.H),
                  "s"(a.eps), "s"(a.M), "s"(a.I), "s"(a.xs));
-    const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int m = blockIdx.y * 4 + wave_id();
     const int k = blockIdx.x * 64 + (threadIdx.x & 63);
     const int Ip = (a.I + 31) & ~31;
     float h = 0.f;
