@@ -126,9 +126,14 @@ __device__ __forceinline__ float block_scanf(float v, SmpShared &sh) {
 // ---------------------------------------------------------------------------
 // per-segment statistics of one row: (max y, sum exp2(y - max)), y = z * c
 __global__ __launch_bounds__(SMP_THREADS) void k_smp_stats(SmpStatArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.z[0]), "s"(a.z[1]), "s"(a.z[2]), "s"(a.nptr), "s"(a.ld), "s"(a.V), "s"(a.nb),
+                 "s"(a.c), "s"(a.stats));
     __shared__ SmpShared sh;
     const int b = blockIdx.x, row = blockIdx.y;
-    const float *z = a.nptr > 1 ? a.z[row] : a.z[0] + (size_t)row * a.ld;
+    // row pointer chosen among the loaded arguments (no indexed argument load)
+    const float *zr = row == 0 ? a.z[0] : (row == 1 ? a.z[1] : a.z[2]);
+    const float *z = a.nptr > 1 ? zr : a.z[0] + (size_t)row * a.ld;
     const int seg = smp_seg(a.V, a.nb);
     const int lo = b * seg, hi = min(a.V, lo + seg);
     float m = -INFINITY;
@@ -171,6 +176,8 @@ __device__ __forceinline__ float resid_w(float zq, float zp, float c, const RowT
 
 // per-segment sums of the residual (segment b)
 __global__ __launch_bounds__(SMP_THREADS) void k_smp_residual(SmpResidualArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.zq), "s"(a.zp), "s"(a.stats), "s"(a.V), "s"(a.nb), "s"(a.c), "s"(a.rsum));
     __shared__ SmpShared sh;
     const int b = blockIdx.x;
     const RowTotal q = row_total(a.stats, a.nb, sh);
@@ -254,6 +261,9 @@ __device__ int smp_search(float w, int V, int nb, float u, WFn wfn, SmpShared &s
 
 // one draw per row
 __global__ __launch_bounds__(SMP_THREADS) void k_smp_draw(SmpDrawArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.z), "s"(a.stats), "s"(a.u), "s"(a.V), "s"(a.nb), "s"(a.c), "s"(a.token),
+                 "s"(a.prob));
     __shared__ SmpShared sh;
     const int row = blockIdx.x;
     const float *z = a.z + (size_t)row * a.V;
@@ -273,6 +283,9 @@ void launch_smp_draw(const SmpDrawArgs &a, int M, hipStream_t s) {
 
 // acceptance test and free token, one workgroup
 __global__ __launch_bounds__(SMP_THREADS) void k_smp_accept(SmpAcceptArgs a) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.zq), "s"(a.zp0), "s"(a.zp1), "s"(a.stats), "s"(a.rsum), "s"(a.draft), "s"(a.u),
+                 "s"(a.eos), "s"(a.n_eos), "s"(a.V), "s"(a.nb), "s"(a.c), "s"(a.result), "s"(a.committed));
     __shared__ SmpShared sh;
     const int t = threadIdx.x;
     const int d = *a.draft;
