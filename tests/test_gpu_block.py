@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from verifier_block_forward_amd import configs, synth
-from tests.gpu_harness import Prepared, compare_block
+from tests.gpu_harness import Prepared, compare_block, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -234,6 +234,29 @@ def test_block_moe_small(orc, cfg):
 
 def test_block_moe_tiled(orc):
     run_moe_case(orc, small_moe(name="moe_tiled", M=4), tiled=True)
+
+
+def test_block_moe_fewer_experts_after_more(orc):
+    """A call that touches fewer experts than the previous call on the same workspace:
+    the routing of the second call must not pick up the first call's coefficients
+    or expert partials for the slots it does not use."""
+    cfg = small_moe(name="moe_shrink", M=8)
+    prep = Prepared(cfg)
+    first = orc.block_forward(cfg, prep.w_host, prep.in_host)
+    prep.run()  # many distinct experts (8 independent rows)
+    # second call: every input row the same, so the rows (which still differ after
+    # the causal attention) route to far fewer experts
+    inp = dict(prep.in_host)
+    inp["x0"] = np.repeat(prep.in_host["x0"][:1], cfg.M, axis=0)
+    inp["ctx"] = np.repeat(prep.in_host["ctx"][:1], cfg.M, axis=0)
+    want = orc.block_forward(cfg, prep.w_host, inp)
+    n_first = len(np.unique(first["moe_sel"]))
+    n_second = len(np.unique(want["moe_sel"]))
+    assert n_second < n_first, (n_first, n_second)  # 6 after 16 with these seeds
+    assert want["moe_gap"].min() > 1e-4, f"near-tie in the router: gap {want['moe_gap'].min()}"
+    got = prep.run(x0=to_dev(inp["x0"]), ctx=to_dev(inp["ctx"]))
+    gk, gv = prep.cache_host(*got["cache"])
+    compare_block(cfg, got, want, cfg.C, cfg.C + cfg.M, (gk, gv), (want["cache_k"], want["cache_v"]))
 
 
 @pytest.mark.slow
