@@ -69,7 +69,7 @@ extern "C" {
 #define DBF_FFN_MOE 1
 
 /* block attention masks */
-#define DBF_MASK_CAUSAL 0 /* block row i sees block rows <= i (the spec reading) */
+#define DBF_MASK_CAUSAL 0 /* block row i sees block rows <= i (causal within the block; the default) */
 #define DBF_MASK_BIDIR 1  /* every block row sees all M block rows (block-diffusion reading) */
 
 #define DBF_MAX_M 16   /* block rows per call (K+1 <= 16) */
