@@ -80,6 +80,25 @@ __device__ __forceinline__ float block_sum_256(float v, float *sh4) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// RMSNorm row scale s_m = 1/sqrt(mean x^2 + eps) from the per-64-column partial sums
+// of squares of the row, formed by a whole wavefront (lane-strided sum, then a
+// fixed xor tree). Split in two so that a kernel can issue the first load (this
+// lane's element of the first 64) together with its other independent loads, and
+// finish the sum after one wait for all of them.
+__device__ __forceinline__ float row_scale_first(const float *ssp_row, int ncb) {
+    const int lane = threadIdx.x & 63;
+    return lane < ncb ? ssp_row[lane] : 0.f;
+}
+
+__device__ __forceinline__ float row_scale_finish(float first, const float *ssp_row, int ncb, int H,
+                                                  float eps) {
+    const int lane = threadIdx.x & 63;
+    float s = first;
+    for (int i = lane + 64; i < ncb; i += 64) s += ssp_row[i];
+    s = wave_sum(s);
+    return 1.0f / sqrtf(s / (float)H + eps);
+}
+
 // This thread's wavefront within the workgroup, as a value the compiler knows to
 // be uniform across the wave (readfirstlane): indexes and branches derived from it
 // stay in scalar registers instead of vector registers and exec-mask branches.

@@ -21,23 +21,6 @@
 
 namespace dbf {
 
-// Row scale from the norm partials, in two halves: the first load (this lane's
-// element of the first 64) goes out with a kernel's other independent loads, and
-// the lane-strided sum and its fixed xor tree follow after one wait.
-__device__ __forceinline__ float moe_scale_first(const float *ssp_row, int ncb) {
-    const int lane = threadIdx.x & 63;
-    return lane < ncb ? ssp_row[lane] : 0.f;
-}
-
-__device__ __forceinline__ float moe_scale_finish(float first, const float *ssp_row, int ncb, int H,
-                                                  float eps) {
-    const int lane = threadIdx.x & 63;
-    float s = first;
-    for (int i = lane + 64; i < ncb; i += 64) s += ssp_row[i];
-    s = wave_sum(s);
-    return 1.0f / sqrtf(s / (float)H + eps);
-}
-
 // (value, index) with ties to the lower index
 __device__ __forceinline__ void better_pair(float &v, int &i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) {
@@ -80,7 +63,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
     const float *sr = a.ssp + (size_t)(wv < M ? wv : 0) * a.ncb;
     float f = 0.f, gsum = 0.f;
     if (wv < M) {
-        f = moe_scale_first(sr, a.ncb);
+        f = row_scale_first(sr, a.ncb);
         gsum = sum_partials(a.p_sgi, a.ks_sgi, 16, 1, wv, 0);
     }
     for (int m0 = 0; m0 < M; m0 += rg) {
@@ -90,7 +73,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
             z[i] = sum_partials(a.p_router, a.ks_router, 16, E, m0 + r, i - r * E);
         }
         if (m0 == 0 && wv < M) {
-            const float s = moe_scale_finish(f, sr, a.ncb, a.H, a.eps);
+            const float s = row_scale_finish(f, sr, a.ncb, a.H, a.eps);
             if (lane == 0) {
                 rscale[wv] = s;
                 a.shared_scale[wv] = sigmoidf_(s * gsum);
@@ -200,7 +183,7 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
     const int Ip = (I + 31) & ~31;
     float h = 0.f;
     const float *sr = a.ssp + (size_t)(m < a.M ? m : 0) * a.ncb;
-    const float f = m < a.M ? moe_scale_first(sr, a.ncb) : 0.f;
+    const float f = m < a.M ? row_scale_first(sr, a.ncb) : 0.f;
     if (m < a.M) {
         float g = 0.f, u = 0.f;
         if (k < I) {
@@ -214,7 +197,7 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
             u = o[1];
         }
         // whole wave (wave-uniform m) forms the row scale: no lane has left yet
-        const float s = moe_scale_finish(f, sr, a.ncb, a.H, a.eps);
+        const float s = row_scale_finish(f, sr, a.ncb, a.H, a.eps);
         if (k < I) {
             g *= s;
             u *= s;

@@ -14,28 +14,6 @@
 
 namespace dbf {
 
-// Row scale from the per-column-block partial sums of squares; called by a whole
-// wavefront (lane-strided sum, then a fixed xor tree). Split in two so that a
-// kernel can issue the first load (this lane's element of the first 64) together
-// with its other independent loads, and finish the sum after one wait for all.
-__device__ __forceinline__ float row_scale_first(const float *ssp_row, int ncb) {
-    const int lane = threadIdx.x & 63;
-    return lane < ncb ? ssp_row[lane] : 0.f;
-}
-
-__device__ __forceinline__ float row_scale_finish(float first, const float *ssp_row, int ncb, int H,
-                                                  float eps) {
-    const int lane = threadIdx.x & 63;
-    float s = first;
-    for (int i = lane + 64; i < ncb; i += 64) s += ssp_row[i];
-    s = wave_sum(s);
-    return 1.0f / sqrtf(s / (float)H + eps);
-}
-
-__device__ __forceinline__ float row_scale(const float *ssp_row, int ncb, int H, float eps) {
-    return row_scale_finish(row_scale_first(ssp_row, ncb), ssp_row, ncb, H, eps);
-}
-
 // ---------------------------------------------------------------------------
 // Generic column kernel. Grid (ncb = ceil(H/64), 4), 256 threads: wave w handles
 // row m = 4*blockIdx.y + w, lane the column blockIdx.x*64 + lane.
