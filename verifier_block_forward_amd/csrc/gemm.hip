@@ -111,14 +111,21 @@ __device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], 
 #undef DBF_LOAD_STAGE
 }
 
-// weight stages in flight per wave: 3 measured best in the c1 step (A/B against
-// 2, 4 and 6 with the LDS-staged ring at 1-4)
+// Stages in flight per wave, chosen per launch from its longest k-slice: 3 for
+// short slices (c1's O, down and fc: 6-20 steps; 2 and 4 were slower), 2 for
+// slices of GEMM_LONG_SLICE steps or more (c2's 24-42-step slices), where the
+// steady state dominates and a shorter queue of requests wins.
 #ifndef DBF_GEMM_PIPE
 #define DBF_GEMM_PIPE 3
 #endif
+#ifndef DBF_GEMM_PIPE_LONG
+#define DBF_GEMM_PIPE_LONG 2
+#endif
 constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
+constexpr int GEMM_PIPE_LONG = DBF_GEMM_PIPE_LONG;
+constexpr int GEMM_LONG_SLICE = 24;
 
-template <int NA, int NB>
+template <int NA, int NB, int PIPE>
 __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
     // scalar wave index: the unit, the segment lookup and the segment's fields are
@@ -196,11 +203,11 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
         f32x4 acc1[NA][1];
 #pragma unroll
         for (int a = 0; a < NA; a++) acc1[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        skinny_mainloop<NA, 1, GEMM_PIPE>(wrow, wstep, sg.tiled, xs1, K, s0, s1, lane, acc1);
+        skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs1, K, s0, s1, lane, acc1);
 #pragma unroll
         for (int a = 0; a < NA; a++) acc[a][0] = acc1[a][0];
     } else {
-        skinny_mainloop<NA, NB, GEMM_PIPE>(wrow, wstep, sg.tiled, xs, K, s0, s1, lane, acc);
+        skinny_mainloop<NA, NB, PIPE>(wrow, wstep, sg.tiled, xs, K, s0, s1, lane, acc);
     }
 
     const int nb = NB == 1 ? 1 : sg.nb;
@@ -419,7 +426,13 @@ static void go(const GemmArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), lds, s, a);
     } else {
         const int blocks = (a.total_units + 3) / 4;
-        hipLaunchKernelGGL((k_gemm_splitk<NA, NB>), dim3(blocks), dim3(256), 0, s, a);
+        int steps = 0;
+        for (int i = 0; i < a.nseg; i++)
+            if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
+        if (steps >= GEMM_LONG_SLICE)
+            hipLaunchKernelGGL((k_gemm_splitk<NA, NB, GEMM_PIPE_LONG>), dim3(blocks), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm_splitk<NA, NB, GEMM_PIPE>), dim3(blocks), dim3(256), 0, s, a);
     }
 }
 
