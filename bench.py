@@ -9,6 +9,17 @@ in HBM before the timed region. Prints one JSON line.
 Default workload: the DFlash-style drafter block, 5 layers, hidden 2816, 16 q / 8
 kv heads of 128, SwiGLU 8448, vocab 262144, K+1 = 16 block rows plus 16 new
 context rows over a 4096-position F32 KV cache.
+
+Beyond the timed steps (the headline rows/s), the line carries:
+  roofline      the lm_head kernel (the largest share of the bytes) and one entry
+                per kernel class (projections, attention, row kernels, lm_head),
+                each from kernel durations measured with HIP events bound to the
+                dispatches (the library's profiling switch) over the same steps;
+  cold          per-step latency with a 512 MiB buffer streamed before each step
+                (weights cannot sit in the 256 MB MALL or the L2);
+  r1            DFlash: the same step with R = 1 new context row;
+  graph         the step replayed from a HIP graph;
+  cpu_baseline  the oracle on the host cores (F64), one warm run then the median.
 """
 from __future__ import annotations
 
@@ -24,74 +35,98 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-HEAD_KERNEL = "k_head"
-HEAD_SOURCES = ["verifier_block_forward_amd/csrc/gemm.hip", "verifier_block_forward_amd/csrc/internal.hpp"]
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "lm_head_c1_counters.json")
+TARGET_FRAC = {"projections": 0.70, "attention": 0.50}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_c1.json")
+FLUSH_BYTES = 512 << 20
 
 
-def algorithmic_bytes(cfg, M: int, R: int, n_ctx: int) -> dict:
-    """Bytes the method must move per block: every touched BF16 weight once, the KV
-    rows read and written, the gathered embedding rows (norms/activations ~0)."""
+def class_bytes(cfg, M: int, R: int, n_ctx: int, touched=None) -> dict:
+    """Algorithmic bytes per step by kernel class: every touched BF16 weight once
+    (MoE: the router, the shared expert and its gate, and the distinct experts the
+    rows were routed to, counted per layer), the KV rows read and written, the
+    gathered embedding rows. Norm weights and activations are negligible."""
     H, L = cfg.hidden, cfg.n_layers
     qt, kt = cfg.q_total, cfg.kv_total
     kvb = 2 if cfg.kv_dtype == "bf16" else 4
-    b = {}
+    proj = 0
     if cfg.kind == "dflash":
-        b["input_proj"] = H * cfg.n_target_hidden * H * 2 if R > 0 else 0
-        b["embed_rows"] = M * H * 2 if cfg.block_input == "tokens" else 0
+        proj += H * cfg.n_target_hidden * H * 2 if R > 0 else 0
     else:
-        b["input_proj"] = 2 * H * H * 2
-    attn = (qt + 2 * kt + qt) * H * 2 + (qt * H * 2 if cfg.has_attn_gate else 0)
-    b["attn_proj"] = L * attn
+        proj += 2 * H * H * 2
+    proj += L * ((qt + 2 * kt + qt) * H * 2 + (qt * H * 2 if cfg.has_attn_gate else 0))
     if cfg.ffn_kind == "dense":
-        b["ffn"] = L * 3 * cfg.intermediate * H * 2
-    b["kv_read"] = L * (n_ctx + R + M) * kt * 2 * kvb
-    b["kv_write"] = L * (R + M) * kt * 2 * kvb
-    b["lm_head"] = cfg.vocab * H * 2
+        proj += L * 3 * cfg.intermediate * H * 2
+    else:
+        E, Ie, Is = cfg.n_experts, cfg.expert_intermediate, cfg.shared_intermediate
+        t = touched if touched is not None else [min(E, M * cfg.top_k)] * L
+        proj += L * (E * H * 2 + H * 2 + 3 * Is * H * 2) + sum(t) * 3 * Ie * H * 2
+    b = {
+        "projections": proj,
+        "attention": L * (n_ctx + R + M) * kt * 2 * kvb,
+        "row_kernels": L * (R + M) * kt * 2 * kvb
+        + (M * H * 2 if cfg.block_input == "tokens" else 0),
+        "lm_head": cfg.vocab * H * 2,
+    }
     b["total"] = sum(b.values())
     return b
 
 
-def kernel_source_hash() -> str:
+def source_hash(paths) -> str:
     h = hashlib.sha256()
-    for p in HEAD_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def counters_traffic():
-    """HBM bytes per lm_head launch from the committed rocprofv3 PMC summary, or None
-    when it is missing or was taken on a different kernel source."""
+def counters(config_name: str) -> dict:
+    """Per-kernel HBM traffic from the committed rocprofv3 PMC summary, keeping only
+    the kernels whose sources are unchanged since the counters were taken."""
     try:
         with open(COUNTERS_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
-        return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return d.get("traffic_bytes_per_launch")
+        return {}
+    if d.get("workload") != config_name:
+        return {}
+    out = {}
+    for name, k in d.get("kernels", {}).items():
+        if k.get("source_hash") == source_hash(k.get("sources", [])):
+            out[name] = k
+    return out
 
 
 def cpu_baseline(cfg, w_host, in_host, budget_s: float):
-    from oracle import oracle as orc
+    """The oracle (plain F64 C, OpenMP over independent outputs) on this host: one
+    warm run, then timed runs until the budget is spent (at least three); the value
+    is M rows over the median run."""
     import numpy as np
 
-    runs = 0
-    t0 = time.perf_counter()
-    ck, cv = in_host["cache_k"].copy(), in_host["cache_v"].copy()
-    while True:
+    from oracle import oracle as orc
+
+    def one():
+        ck, cv = in_host["cache_k"].copy(), in_host["cache_v"].copy()
+        t0 = time.perf_counter()
         out = orc.block_forward(cfg, w_host, in_host, cache_k=ck, cache_v=cv,
                                 seq_len=in_host["seq_len"])
         orc.lm_head(out["h_final"], w_host["lm_head"], want_logits=False)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": runs * cfg.M / el, "unit": "rows/s", "cores": orc.threads(), "kind": "oracle",
-            "sample": f"{runs} full block(s) of the benchmark workload ({cfg.M} rows, {cfg.n_layers} "
-                      f"layers, context {cfg.C}) + lm_head argmax over {cfg.vocab} rows, F64, "
-                      f"{el:.1f} s"}
+        return time.perf_counter() - t0
+
+    one()
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_start < budget_s:
+        times.append(one())
+    med = float(np.median(times))
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"value": round(cfg.M / med, 3), "unit": "rows/s", "cores": orc.threads(), "nproc": nproc,
+            "kind": "oracle", "ms_per_block": round(med * 1e3, 1), "runs": len(times),
+            "sample": f"the full benchmark block ({cfg.M} rows, {cfg.n_layers} layers, context "
+                      f"{cfg.C}) + lm_head argmax over {cfg.vocab} rows in F64; one warm run, then "
+                      f"the median of {len(times)} timed runs ({sum(times):.1f} s)"}
 
 
 def main():
@@ -105,6 +140,8 @@ def main():
                     help="keep projection weights row-major instead of the tiled layout")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step captured in a HIP graph")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the timed steps and the profiled pass (no cold, R=1, graph passes)")
     ap.add_argument("--sampled", action="store_true",
                     help="MTP workloads: the sampled (speculative-sampling) round instead of the greedy "
                          "walk -- lm_head logits, sample_tokens for the draft, accept_sampled against "
@@ -150,28 +187,37 @@ def main():
     inp = {k: up(v) for k, v in in_host.items() if isinstance(v, np.ndarray) and v.size}
     bw = dbf.BlockWeights(cfg, w_dev)
     ccfg = dbf.make_config(cfg)
-    M, R, H, V = cfg.M, cfg.R, cfg.hidden, cfg.vocab
+    M, R, H, V, L = cfg.M, cfg.R, cfg.hidden, cfg.vocab, cfg.n_layers
     ws = torch.empty(dbf.draft_block_workspace_bytes(ccfg, M, R), dtype=torch.uint8, device=dev)
     ws_head = torch.empty(dbf.lm_head_argmax_workspace_bytes(M, H, V), dtype=torch.uint8, device=dev)
     h_final = torch.empty((M, H), dtype=torch.float32, device=dev)
     argmax = torch.empty(M, dtype=torch.int32, device=dev)
     result = torch.zeros(5, dtype=torch.int32, device=dev)
+    moe_experts = torch.zeros(L, dtype=torch.int32, device=dev) if cfg.ffn_kind == "moe" else None
     ck, cv = inp["cache_k"], inp["cache_v"]
     kv = dbf.make_cache(ck, cv, in_host["seq_len"])
-    io = dbf.make_io(M, R, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"), ctx=inp.get("ctx"))
+    io = dbf.make_io(M, R, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"), ctx=inp.get("ctx"),
+                     moe_experts=moe_experts)
     K = cfg.K
-    # targets: the seeded accept pattern of the benchmark (first j drafts match)
-    drafts_ref = np.arange(K, dtype=np.int32)
-    target_np, _ = synth.accept_targets(drafts_ref, V, cfg.seed)
-    target = up(target_np)
     drafts = argmax[1:] if cfg.kind == "dflash" else argmax[:1]
     lm_head = w_dev["lm_head"]
     stream = torch.cuda.current_stream()
+
+    # One untimed step gives this workload's drafts; the accept targets are built from
+    # them with the seeded pattern (the first j drafts match, j uniform in 0..K), so
+    # every timed walk accepts exactly j drafts.
+    dbf.draft_block_forward(ccfg, bw, kv, io, ws, stream)
+    dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, stream)
+    dbf.kv_rollback(kv, R + M)
+    torch.cuda.synchronize()
+    target_np, accept_j = synth.accept_targets(drafts.cpu().numpy(), V, cfg.seed)
+    target = up(target_np)
+    touched = moe_experts.cpu().tolist() if moe_experts is not None else None
+
     if args.sampled:
         # the sampled MTP round: the drafter's logits row, one draft drawn from it,
         # and the speculative-sampling test against the target's logits at the
-        # draft's position and the next (seeded synthetic rows, correlated with the
-        # drafter's as a trained drafter's would be)
+        # draft's position and the next (seeded synthetic rows)
         logits = torch.empty((M, V), dtype=torch.float32, device=dev)
         rng = np.random.default_rng(cfg.seed + 1000)
         tl = rng.normal(0.0, 2.0, (2, V)).astype(np.float32)
@@ -181,41 +227,39 @@ def main():
         draft_tok = torch.empty(M, dtype=torch.int32, device=dev)
         ws_smp = torch.empty(dbf.sample_tokens_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
         ws_acc = torch.empty(dbf.accept_sampled_workspace_bytes(V), dtype=torch.uint8, device=dev)
-        smp_ev = []
 
-    def step(ev=None):
+    def step(ev=None, st=None, io_=io, R_=R):
+        st = stream if st is None else st
         if ev is not None:
-            ev[0].record(stream)
-        dbf.draft_block_forward(ccfg, bw, kv, io, ws, stream)
+            ev[0].record(st)
+        dbf.draft_block_forward(ccfg, bw, kv, io_, ws, st)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record(st)
         if args.sampled:
-            dbf.lm_head_argmax(h_final, lm_head, argmax, logits, None, ws_head, stream)
+            dbf.lm_head_argmax(h_final, lm_head, argmax, logits, None, ws_head, st)
             if ev is not None:
-                ev[2].record(stream)
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            dbf.sample_tokens(logits, u_draft, draft_tok, None, args.temperature, ws_smp, stream)
-            if ev is not None:
-                e[0].record(stream)
+                ev[2].record(st)
+            dbf.sample_tokens(logits, u_draft, draft_tok, None, args.temperature, ws_smp, st)
             dbf.accept_sampled(logits[M - 1], target_logits, draft_tok[M - 1:], u_acc, result,
-                               args.temperature, ws=ws_acc, stream=stream)
-            if ev is not None:
-                e[1].record(stream)
-                ev[3] = e[1]
-                smp_ev.append((ev[2], e[0], e[1]))
+                               args.temperature, ws=ws_acc, stream=st)
         else:
-            dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, stream)
+            dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, st)
             if ev is not None:
-                ev[2].record(stream)
-            dbf.accept_prefix(drafts, target, result, stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
-        dbf.kv_rollback(kv, R + M)
+                ev[2].record(st)
+            dbf.accept_prefix(drafts, target, result, stream=st)
+        if ev is not None:
+            ev[3].record(st)
+        dbf.kv_rollback(kv, R_ + M)
+
+    def new_events(n):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    # ---- timed region: K back-to-back steps (the headline)
+    evs = new_events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -225,41 +269,101 @@ def main():
     block_ms = [e[0].elapsed_time(e[1]) for e in evs]
     head_ms = [e[1].elapsed_time(e[2]) for e in evs]
     acc_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    # per-step latency by events (first kernel of the block forward through the end
-    # of the accept walk): its spread over the timed steps
     step_ev_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_step = wall * 1e3 / args.steps
     value = M * args.steps / wall
+    accept_result = result.cpu().tolist()
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
-    # The same step captured in a HIP graph and replayed (kv_rollback is host-side
-    # metadata: every replay rewrites the same cache rows, as the eager step does
-    # after its rollback).
-    graph_ms = None
-    if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream()
-            dbf.draft_block_forward(ccfg, bw, kv, io, ws, cs)
-            if args.sampled:
-                dbf.lm_head_argmax(h_final, lm_head, argmax, logits, None, ws_head, cs)
-                dbf.sample_tokens(logits, u_draft, draft_tok, None, args.temperature, ws_smp, cs)
-                dbf.accept_sampled(logits[M - 1], target_logits, draft_tok[M - 1:], u_acc, result,
-                                   args.temperature, ws=ws_acc, stream=cs)
-            else:
-                dbf.lm_head_argmax(h_final, lm_head, argmax, None, None, ws_head, cs)
-                dbf.accept_prefix(drafts, target, result, stream=cs)
-        dbf.kv_rollback(kv, R + M)
-        for _ in range(args.warmup):
-            g.replay()
+    # ---- the same steps with every kernel timed by events bound to its dispatch
+    n_prof = min(args.steps, 20)
+    dbf.profile_start(65536)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for _ in range(n_prof):
+        step()
+    torch.cuda.synchronize()
+    prof_wall_ms = (time.perf_counter() - tp0) * 1e3 / n_prof
+    recs = dbf.profile_stop(65536)
+    per_class_us = {}
+    per_kernel = {}
+    for cls, name, us in recs:
+        per_class_us[cls] = per_class_us.get(cls, 0.0) + us
+        k = per_kernel.setdefault(name, [0, 0.0])
+        k[0] += 1
+        k[1] += us
+
+    ab = class_bytes(cfg, M, R, in_host["seq_len"], touched)
+    cnt = counters(cfg.name)
+    classes = {}
+    for cls in ("projections", "attention", "row_kernels", "lm_head"):
+        us = per_class_us.get(cls, 0.0) / n_prof
+        gbps = ab[cls] / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        entry = {"bytes": ab[cls], "us_per_step": round(us, 2), "achieved_gbps": round(gbps, 1),
+                 "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        if cls in TARGET_FRAC:
+            entry["target"] = TARGET_FRAC[cls]
+            entry["meets_target"] = bool(gbps / PEAK_HBM_GBPS >= TARGET_FRAC[cls])
+        classes[cls] = entry
+    classes["other_us_per_step"] = round(sum(v for c, v in per_class_us.items()
+                                              if c not in classes) / n_prof, 2)
+    kernels = {n: {"launches_per_step": round(c / n_prof, 2), "avg_us": round(t / c, 2),
+                   "us_per_step": round(t / n_prof, 2)} for n, (c, t) in sorted(per_kernel.items())}
+    head_launch_us = per_kernel.get("k_head", [1, 0.0])
+    head_us = head_launch_us[1] / max(head_launch_us[0], 1)
+    head_gbps = ab["lm_head"] / (head_us * 1e-6) / 1e9 if head_us > 0 else 0.0
+    head_cnt = cnt.get("k_head")
+
+    extra = {}
+    if not args.no_extra:
+        # ---- cold caches: a 512 MiB buffer streamed (read and written) before each step
+        flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        cold = new_events(min(args.steps, 20))
+        for e in cold:
+            flush.add_(1.0)
+            step(e)
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
-        del g
+        cold_ms = np.array([e[0].elapsed_time(e[3]) for e in cold])
+        del flush
+        extra["cold"] = {"flush_bytes": FLUSH_BYTES, "steps": len(cold),
+                         "step_ms_p10_p50_p90": [round(float(np.percentile(cold_ms, q)), 4)
+                                                 for q in (10, 50, 90)],
+                         "rows_per_s_p50": round(M / (float(np.median(cold_ms)) * 1e-3), 1)}
+        # ---- R = 1 new context row (the smallest round: one draft accepted less than needed)
+        if cfg.kind == "dflash" and R > 1:
+            io1 = dbf.make_io(M, 1, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"),
+                              ctx=inp["ctx"][:1].contiguous())
+            for _ in range(args.warmup):
+                step(io_=io1, R_=1)
+            r1 = new_events(args.steps)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for e in r1:
+                step(e, io_=io1, R_=1)
+            torch.cuda.synchronize()
+            w1 = (time.perf_counter() - t1) * 1e3 / args.steps
+            b1 = class_bytes(cfg, M, 1, in_host["seq_len"], touched)["total"]
+            extra["r1"] = {"R": 1, "ms_per_step": round(w1, 4), "rows_per_s": round(M / (w1 * 1e-3), 1),
+                           "algorithmic_bytes": b1, "gbps": round(b1 / (w1 * 1e-3) / 1e9, 1)}
+        # ---- the step captured in a HIP graph and replayed (kv_rollback is host-side
+        # metadata: every replay rewrites the same cache rows, as the eager step does
+        # after its rollback)
+        if not args.no_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st=torch.cuda.current_stream())
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for _ in range(args.steps):
+                g.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            gms = g0.elapsed_time(g1) / args.steps
+            extra["graph"] = {"ms_per_step": round(gms, 4), "rows_per_s": round(M / (gms * 1e-3), 1)}
+            del g
 
     # plain copy of known size after the timed region: the reference dispatch that
     # scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes
@@ -271,14 +375,9 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    ab = algorithmic_bytes(cfg, M, R, in_host["seq_len"])
-    head_avg = float(np.mean(head_ms))
-    head_gbps = ab["lm_head"] / (head_avg * 1e-3) / 1e9
-    block_total_ms = float(np.mean(block_ms)) + head_avg + float(np.mean(acc_ms))
-    traffic = counters_traffic()
     print("[bench] timed; running the oracle baseline", file=sys.stderr, flush=True)
     cpu = cpu_baseline(cfg, w_host, in_host, args.cpu_baseline_seconds) \
-        if args.cpu_baseline_seconds > 0 else None
+        if args.cpu_baseline_seconds > 0 and not args.sampled else None
 
     line = {
         "metric": "drafted rows/sec (drafter block K+1=16) with achieved HBM GB/s vs roofline",
@@ -293,45 +392,42 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.description}", "layers": cfg.n_layers,
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "layers": L,
                    "hidden": H, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "vocab": V, "M": M, "R": R, "context": cfg.C, "kv_dtype": cfg.kv_dtype,
                    "weights": "bf16 row-major" if args.row_major else "bf16 tiled",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": f"{HEAD_KERNEL} (lm_head_argmax call)",
+        "roofline": {"bound": "hbm", "kernel": "k_head (lm_head)",
                      "achieved": round(head_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(head_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["lm_head"],
-                     "avg_launch_ms": round(head_avg, 4)},
+                     "traffic": head_cnt["traffic_bytes_per_launch"] if head_cnt else None,
+                     "algorithmic_bytes_per_launch": ab["lm_head"],
+                     "avg_launch_us": round(head_us, 2),
+                     "classes": classes,
+                     "class_timing": f"kernel durations from HIP events bound to each dispatch, "
+                                     f"{n_prof} steps ({prof_wall_ms:.4f} ms/step while timed)"},
         "block": {"algorithmic_bytes": ab["total"],
                   "weights_resident_bytes": bw.resident_bytes(),
-                  "gbps_event": round(ab["total"] / (block_total_ms * 1e-3) / 1e9, 1),
                   "gbps_wall": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
+                  "frac_wall": round(ab["total"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                   "ms_draft_block_forward": round(float(np.mean(block_ms)), 4),
-                  "ms_lm_head_argmax": round(head_avg, 4),
-                  "ms_accept_prefix": round(float(np.mean(acc_ms)), 4),
+                  "ms_lm_head_argmax": round(float(np.mean(head_ms)), 4),
+                  "ms_accept": round(float(np.mean(acc_ms)), 4),
                   "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev_ms, q)), 4)
                                           for q in (10, 50, 90)],
-                  "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
-                  "graph_rows_per_s": round(M / (graph_ms * 1e-3), 1) if graph_ms else None,
-                  "accept_result": result.cpu().tolist()},
+                  "launches_per_step": round(len(recs) / n_prof, 2),
+                  "accept_result": accept_result, "accept_expected": accept_j,
+                  "moe_experts_touched": touched},
+        "kernels": kernels,
+        **extra,
         "cpu_baseline": cpu,
     }
     if args.sampled:
-        st = [a.elapsed_time(b) for a, b, _ in smp_ev]
-        at = [b.elapsed_time(c) for _, b, c in smp_ev]
-        # algorithmic bytes: sample_tokens reads each logits row once for its
-        # statistics (the search reads one segment); accept_sampled reads three
-        # rows for statistics and two for the residual sums
         sb, ab_acc = M * V * 4, 5 * V * 4
         line["sampled"] = {
             "temperature": args.temperature,
-            "ms_sample_tokens": round(float(np.mean(st)), 4),
-            "ms_accept_sampled": round(float(np.mean(at)), 4),
+            "us_sampling_kernels_per_step": classes.get("other_us_per_step"),
             "bytes_sample_tokens": sb, "bytes_accept_sampled": ab_acc,
-            "gbps_sample_tokens": round(sb / (np.mean(st) * 1e-3) / 1e9, 1),
-            "gbps_accept_sampled": round(ab_acc / (np.mean(at) * 1e-3) / 1e9, 1),
-            "bound": "latency (a few MB per call: 3-4 dependent kernels of a few us)",
             "logits_written_by_lm_head_bytes": M * V * 4,
         }
         line["metric"] = "drafted rows/sec (MTP K=1, sampled acceptance)"

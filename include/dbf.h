@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DBF_ABI_VERSION 3
+#define DBF_ABI_VERSION 4
 
 /* status codes */
 #define DBF_OK 0
@@ -177,7 +177,10 @@ typedef struct {
  *               (MTP: must be 0).
  *   hidden_out  [M, H] F32 pre-norm hidden of the last layer, or NULL.
  *   h_final     [M, H] F32 final-normed hidden (required).
- *   layer_hidden [n_layers, M, H] F32 hidden after each layer, or NULL. */
+ *   layer_hidden [n_layers, M, H] F32 hidden after each layer, or NULL.
+ *   moe_experts [n_layers] int32 out, or NULL (MoE FFN only): the number of
+ *               distinct experts the layer's M rows were routed to, i.e. the
+ *               experts whose weights the layer read ([MTP] `MtpFfnWeightsGpu::Moe`). */
 typedef struct {
     const int32_t *tokens;
     const float *x0;
@@ -189,6 +192,7 @@ typedef struct {
     const float *const *ctx_layers;
     int64_t ctx_ld;
     int64_t ctx_row0;
+    int32_t *moe_experts;
 } dbf_block_io;
 
 /* Drafter block forward ([MTP] `forward_draft_with_hidden` and its helpers
@@ -314,6 +318,35 @@ size_t accept_sampled_workspace_bytes(int32_t V);
  * Pass the result as a dbf_tensor {dst, DBF_BF16_T16, same ndim and shape}. */
 size_t dbf_tiled_bytes(int64_t N, int64_t K);
 int dbf_tile_weight(const dbf_tensor *src, void *dst, void *stream);
+
+/* Kernel timing, for measurement only ([MTP] `forward_draft_with_hidden`: the
+ * per-sub-step profile the page takes with HF2Q_MTP_PROFILE). While profiling is
+ * on, every kernel the library launches, from any thread, carries a pair of HIP
+ * events bound to its dispatch (hipExtLaunchKernel), so its recorded duration is
+ * the kernel's own execution, without host or marker overhead. Calls made while
+ * profiling is on must not be captured into a HIP graph.
+ *   dbf_profile_start(max_records): clear the record list and time the next
+ *     max_records launches (1..DBF_PROF_MAX_RECORDS); later launches run untimed.
+ *   dbf_profile_stop(out, max_out, n_out): stop, wait for the timed kernels to
+ *     finish, copy up to max_out records (host array) in launch order and set
+ *     *n_out to the number of timed launches. */
+#define DBF_PROF_MAX_RECORDS 65536
+#define DBF_PROF_PROJ 0   /* skinny projections: fc/eh, Q/K/V/gate, O, FFN, router, experts */
+#define DBF_PROF_ATTN 1   /* attention over the KV cache and its chunk combine */
+#define DBF_PROF_ROWS 2   /* row kernels: residual sums, norms, RoPE + KV append, SwiGLU, MoE routing */
+#define DBF_PROF_HEAD 3   /* lm_head and its argmax reduction */
+#define DBF_PROF_ACCEPT 4 /* greedy accept walk */
+#define DBF_PROF_SAMPLE 5 /* sampling and sampled acceptance */
+#define DBF_PROF_OTHER 6  /* weight tiling */
+typedef struct {
+    int32_t cls;        /* DBF_PROF_* */
+    int32_t reserved_;
+    const char *kernel; /* static name of the kernel */
+    double us;          /* execution time, microseconds */
+} dbf_prof_record;
+
+int dbf_profile_start(int32_t max_records);
+int dbf_profile_stop(dbf_prof_record *out, int32_t max_out, int32_t *n_out);
 
 /* Description of the last error on the calling thread ("" when none). */
 const char *dbf_last_error(void);

@@ -84,6 +84,8 @@ class Prepared:
 
     def run(self, M=None, R=None, seq_len=None, cache=None, x0=None, ctx=None, tokens=None,
             want_layers=True, ctx_layers=None, ctx_row0=0):
+        """Returns the outputs as host arrays, the cache tensors and the dbf cache
+        struct; MoE workloads also return moe_experts (distinct experts per layer)."""
         from verifier_block_forward_amd import dbf
         t = torch()
         cfg = self.cfg
@@ -100,13 +102,17 @@ class Prepared:
             x0 = self.inp.get("x0")
         if ctx is None and ctx_layers is None:
             ctx = self.inp.get("ctx")
+        moe = t.full((cfg.n_layers,), -1, dtype=t.int32, device="cuda") if cfg.ffn_kind == "moe" else None
         io = dbf.make_io(M, R, h_final, tokens=tokens, x0=x0, ctx=ctx, hidden_out=hidden_out,
-                         layer_hidden=layers, ctx_layers=ctx_layers, ctx_row0=ctx_row0)
+                         layer_hidden=layers, ctx_layers=ctx_layers, ctx_row0=ctx_row0,
+                         moe_experts=moe)
         kv = dbf.make_cache(ck, cv, seq_len)
         dbf.draft_block_forward(self.ccfg, self.bw, kv, io, self.ws)
         t.cuda.synchronize()
         out = {"h_final": h_final.cpu().numpy(), "hidden_out": hidden_out.cpu().numpy(),
                "seq_len": kv.seq_len, "cache": (ck, cv), "kv": kv}
+        if moe is not None:
+            out["moe_experts"] = moe.cpu().numpy()
         if want_layers:
             out["layer_hidden"] = layers.cpu().numpy()
         return out

@@ -13,10 +13,11 @@ def test_exports_every_declared_symbol():
     assert set(names) >= {"draft_block_forward", "lm_head_argmax", "accept_prefix", "kv_rollback",
                           "draft_block_workspace_bytes", "lm_head_argmax_workspace_bytes",
                           "sample_tokens", "sample_tokens_workspace_bytes", "accept_sampled",
-                          "accept_sampled_workspace_bytes", "dbf_last_error", "dbf_abi_version"}
+                          "accept_sampled_workspace_bytes", "dbf_last_error", "dbf_abi_version",
+                          "dbf_profile_start", "dbf_profile_stop"}
     for n in names:
         assert hasattr(dbf.lib(), n), n
-    assert dbf.abi_version() == 3
+    assert dbf.abi_version() == 4
 
 
 def _cfg(name="c0", **kw):
@@ -281,3 +282,41 @@ def test_accept_sampled_argument_errors():
     assert _accept(n_eos=-1) == dbf.EINVAL
     assert _accept(ws=0) == dbf.EWORKSPACE
     assert _accept(ws_bytes=dbf.accept_sampled_workspace_bytes(1000) - 1) == dbf.EWORKSPACE
+
+
+
+def test_binding_checks_buffers_before_the_call():
+    """The binding refuses what the C ABI cannot see through a raw pointer: host
+    memory, non-contiguous views, wrong element types and buffers shorter than the
+    entry point writes. Each case below fails in the binding; no library call runs."""
+    import torch
+
+    i32 = torch.zeros(8, dtype=torch.int32)
+    f = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device memory"):
+        dbf.accept_prefix(i32[:3], i32[:4], i32[:5])
+    with pytest.raises(ValueError, match="device memory"):
+        dbf.lm_head_argmax(f, f, i32)
+    with pytest.raises(ValueError, match="device memory"):
+        dbf.make_cache(torch.zeros((1, 2, 8, 64)), torch.zeros((1, 2, 8, 64)), 0)
+    with pytest.raises(ValueError, match="required"):
+        dbf._need(None, "target", torch.int32)
+    dbf._need(None, "eos", torch.int32, optional=True)
+    with pytest.raises(ValueError, match="contiguous"):
+        dbf._check_layout(f.t(), "h", torch.float32)
+    with pytest.raises(ValueError, match="must be torch.int32"):
+        dbf._check_layout(torch.zeros(6, dtype=torch.int64), "target", torch.int32, 6)
+    with pytest.raises(ValueError, match="needs at least 6"):
+        dbf._check_layout(torch.zeros(5, dtype=torch.int32), "target", torch.int32, 6)
+    with pytest.raises(ValueError, match="2 dimensions"):
+        dbf._check_layout(torch.zeros(6, dtype=torch.float32), "h", torch.float32, ndim=2)
+    dbf._check_layout(torch.zeros(6, dtype=torch.int32), "target", torch.int32, 6)
+
+
+def test_profile_switch_host_side():
+    """The profiling switch validates its bound and, with nothing launched, stops with
+    no records (no device work is involved)."""
+    assert dbf.lib().dbf_profile_start(0) == dbf.EINVAL
+    assert dbf.lib().dbf_profile_start(70000) == dbf.EINVAL
+    dbf.profile_start(16)
+    assert dbf.profile_stop() == []

@@ -662,6 +662,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 ra.coef = coef;
                 ra.shared_scale = sscale;
                 ra.sel = at<int32_t>(ws, p.moe_sel);
+                ra.touched_out = io->moe_experts ? io->moe_experts + l : nullptr;
                 launch_moe_route(ra, st);
             }
             {

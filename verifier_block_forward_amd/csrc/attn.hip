@@ -144,12 +144,7 @@ struct KvRaw<HD, true> {
     uint4 k[HD / 32], v[HD / 32];
 };
 
-#ifndef DBF_ATT_VNT
-#define DBF_ATT_VNT 1
-#endif
-#ifndef DBF_ATT_WPE
-#define DBF_ATT_WPE 2
-#endif
+constexpr int ATT_WPE = 2;
 // Waves per SIMD the register allocation is sized for. The planner launches about
 // one workgroup per CU, so the F32-cache variants that would spill inside the key
 // loop at two waves per SIMD take the whole register file (one wave) instead. The
@@ -157,7 +152,7 @@ struct KvRaw<HD, true> {
 // in scratch outside the loop only, and measured faster than at one wave.
 template <int HD, int QT, bool KVB>
 constexpr int attn_wpe() {
-    return (!KVB && (HD == 256 || (HD == 64 && QT == 4))) ? 1 : DBF_ATT_WPE;
+    return (!KVB && (HD == 256 || (HD == 64 && QT == 4))) ? 1 : ATT_WPE;
 }
 
 // Sub-tiles held in registers ahead of use: every wave issues its first PF
@@ -181,11 +176,7 @@ __device__ __forceinline__ void attn_v_slot(int st, int g, int r16, int &row, in
 
 typedef unsigned int u32x4_att __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_v16(const uint16_t *p) {
-#if DBF_ATT_VNT
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_att *)p));
-#else
-    return *(const uint4 *)p;
-#endif
 }
 
 template <int HD, bool KVB>
@@ -574,10 +565,10 @@ template <int HD, bool KVB>
 static void go_attn(const AttnArgs &a, int qt, dim3 grid, hipStream_t s) {
     constexpr int CAP = attn_qt_cap(HD, KVB);
     if (qt == 1) {
-        hipLaunchKernelGGL((k_attn<HD, 1, KVB>), grid, dim3(256), 0, s, a);
+        launch_k(PROF_ATTN, "k_attn", (k_attn<HD, 1, KVB>), grid, dim3(256), 0, s, a);
     } else if constexpr (CAP >= 2) {
-        if (qt == 2) hipLaunchKernelGGL((k_attn<HD, 2, KVB>), grid, dim3(256), 0, s, a);
-        else if constexpr (CAP >= 4) hipLaunchKernelGGL((k_attn<HD, 4, KVB>), grid, dim3(256), 0, s, a);
+        if (qt == 2) launch_k(PROF_ATTN, "k_attn", (k_attn<HD, 2, KVB>), grid, dim3(256), 0, s, a);
+        else if constexpr (CAP >= 4) launch_k(PROF_ATTN, "k_attn", (k_attn<HD, 4, KVB>), grid, dim3(256), 0, s, a);
     }
 }
 
@@ -678,7 +669,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
 }
 
 void launch_attn_combine(const CombineArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_attn_combine, dim3(16, a.nq), dim3(256), 0, s, a);
+    launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine, dim3(16, a.nq), dim3(256), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -731,7 +722,7 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t *d, const int32_t *
 
 void launch_accept(const int32_t *drafts, const int32_t *target, int K, const int32_t *eos,
                    int n_eos, int32_t *result, int32_t *committed, hipStream_t s) {
-    hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, s, drafts, target, K, eos, n_eos, result,
+    launch_k(PROF_ACCEPT, "k_accept", k_accept, dim3(1), dim3(64), 0, s, drafts, target, K, eos, n_eos, result,
                        committed);
 }
 

@@ -47,19 +47,11 @@ __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, ma
 // the logical index of b is its rank within its XCD plus the count of workgroups on
 // lower XCDs, so consecutive logical indices -- which share a k-slice of the
 // activations -- sit on one XCD and its L2. A bijection on [0, n) for any n.
-#ifndef DBF_XCD_REMAP
-#define DBF_XCD_REMAP 1
-#endif
 constexpr int N_XCD = 8;
 __device__ __forceinline__ int xcd_logical(int b, int n) {
-#if DBF_XCD_REMAP
     const int q = n / N_XCD, r = n % N_XCD;
     const int x = b % N_XCD, i = b / N_XCD;
     return x * q + (x < r ? x : r) + i;
-#else
-    (void)n;
-    return b;
-#endif
 }
 
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16((a), (b), (c), 0, 0, 0)
@@ -115,14 +107,8 @@ __device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], 
 // short slices (c1's O, down and fc: 6-20 steps; 2 and 4 were slower), 2 for
 // slices of GEMM_LONG_SLICE steps or more (c2's 24-42-step slices), where the
 // steady state dominates and a shorter queue of requests wins.
-#ifndef DBF_GEMM_PIPE
-#define DBF_GEMM_PIPE 3
-#endif
-#ifndef DBF_GEMM_PIPE_LONG
-#define DBF_GEMM_PIPE_LONG 2
-#endif
-constexpr int GEMM_PIPE = DBF_GEMM_PIPE;
-constexpr int GEMM_PIPE_LONG = DBF_GEMM_PIPE_LONG;
+constexpr int GEMM_PIPE = 3;
+constexpr int GEMM_PIPE_LONG = 2;
 constexpr int GEMM_LONG_SLICE = 24;
 
 template <int NA, int NB, int PIPE>
@@ -235,10 +221,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
 // best in the c1 step, against 1, 3 and 4) because more requests in flight only
 // lengthen the queue that the activation loads, which gate the first product,
 // wait in.
-#ifndef DBF_LPIPE
-#define DBF_LPIPE 2
-#endif
-constexpr int LPIPE = DBF_LPIPE;
+constexpr int LPIPE = 2;
 constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
 
 template <int NA, int NB>
@@ -423,16 +406,16 @@ static void go(const GemmArgs &a, hipStream_t s) {
             const size_t b = (size_t)(NB > 1 ? a.seg[i].nb : 1) * a.seg[i].kslice_steps * 2048;
             if (b > lds) lds = b;
         }
-        hipLaunchKernelGGL((k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), lds, s, a);
+        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), lds, s, a);
     } else {
         const int blocks = (a.total_units + 3) / 4;
         int steps = 0;
         for (int i = 0; i < a.nseg; i++)
             if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
         if (steps >= GEMM_LONG_SLICE)
-            hipLaunchKernelGGL((k_gemm_splitk<NA, NB, GEMM_PIPE_LONG>), dim3(blocks), dim3(256), 0, s, a);
+            launch_k(PROF_PROJ, "k_gemm_splitk(long)", (k_gemm_splitk<NA, NB, GEMM_PIPE_LONG>), dim3(blocks), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((k_gemm_splitk<NA, NB, GEMM_PIPE>), dim3(blocks), dim3(256), 0, s, a);
+            launch_k(PROF_PROJ, "k_gemm_splitk", (k_gemm_splitk<NA, NB, GEMM_PIPE>), dim3(blocks), dim3(256), 0, s, a);
     }
 }
 
@@ -501,25 +484,13 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
 // workgroups per CU instead, the one whose loads were served first finished
 // about 45 us (a fifth of the launch) before the other, which then ran alone at
 // half occupancy.
-#ifndef DBF_HEAD_WPE
-#define DBF_HEAD_WPE 2
-#endif
 // weight stages in flight per wave, and k-steps per staged chunk of the hidden
 // rows: 2 and 4 measured best with 8-wave workgroups (A/B in the c1 step against
 // 4/8, 1/8, 2/8, 2/16, 4/16, 4/4 and 3/12)
-#ifndef DBF_HEAD_PIPE
-#define DBF_HEAD_PIPE 2
-#endif
-constexpr int HEAD_PIPE = DBF_HEAD_PIPE;
-#ifndef DBF_HEAD_XCH
-#define DBF_HEAD_XCH 4
-#endif
-constexpr int HEAD_XCH = DBF_HEAD_XCH;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
+constexpr int HEAD_PIPE = 2;
+constexpr int HEAD_XCH = 4;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
 static_assert(HEAD_XCH % HEAD_PIPE == 0, "chunk must hold whole pipeline rounds");
-#ifndef DBF_HEAD_WAVES
-#define DBF_HEAD_WAVES 8
-#endif
-constexpr int HEAD_WAVES = DBF_HEAD_WAVES;  // waves per workgroup, one 16*HEAD_NA-row unit each
+constexpr int HEAD_WAVES = 8;  // waves per workgroup, one 16*HEAD_NA-row unit each
 constexpr int HEAD_THREADS = 64 * HEAD_WAVES;
 
 // this thread's share of chunk c: HEAD_XPT float4 (row tid % 16, float4 columns
@@ -565,7 +536,7 @@ __device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[H
     }
 }
 
-__global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(DBF_HEAD_WPE))) void k_head(
+__global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_head(
     const uint16_t *__restrict__ W, int tiled, const float *__restrict__ h, int V, int K, int M,
     float *__restrict__ logits, float4 *__restrict__ part, int units) {
     // the arguments into scalar registers in one round trip
@@ -691,7 +662,7 @@ int head_blocks(int V) { return (head_units(V) + HEAD_WAVES - 1) / HEAD_WAVES; }
 void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M, float *logits,
                  float4 *part, hipStream_t s) {
     const int units = head_units(V);
-    hipLaunchKernelGGL(k_head, dim3(head_blocks(V)), dim3(HEAD_THREADS), 0, s, W, tiled, h, V, K, M, logits,
+    launch_k(PROF_HEAD, "k_head", k_head, dim3(head_blocks(V)), dim3(HEAD_THREADS), 0, s, W, tiled, h, V, K, M, logits,
                        part, units);
 }
 
@@ -722,7 +693,7 @@ size_t tiled_elems(long long N, long long K) {
 void launch_tile(const uint16_t *src, uint16_t *dst, long long batch, int N, int K, hipStream_t s) {
     const long long per = (long long)((N + 15) / 16) * ((K + 31) / 32);
     const long long total = per * batch;
-    hipLaunchKernelGGL(k_tile, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, src, dst, N, K,
+    launch_k(PROF_OTHER, "k_tile", k_tile, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, src, dst, N, K,
                        per, total);
 }
 
@@ -755,7 +726,7 @@ __global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ 
 
 void launch_head_reduce(const float4 *part, int blocks, int M, int32_t *argmax, float *margin,
                         hipStream_t s) {
-    hipLaunchKernelGGL(k_head_reduce, dim3(M), dim3(256), 0, s, part, blocks, argmax, margin);
+    launch_k(PROF_HEAD, "k_head_reduce", k_head_reduce, dim3(M), dim3(256), 0, s, part, blocks, argmax, margin);
 }
 
 }  // namespace dbf

@@ -1,11 +1,30 @@
 // kernels.hpp -- host-side launch interface of the libdbf kernels (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dbf {
+
+// ---------------------------------------------------------------------------
+// Launches. Every kernel goes through launch_k, which times it when profiling is
+// on (prof.hip): the start/stop events are then bound to the dispatch.
+// ---------------------------------------------------------------------------
+enum ProfClass { PROF_PROJ = 0, PROF_ATTN = 1, PROF_ROWS = 2, PROF_HEAD = 3, PROF_ACCEPT = 4,
+                 PROF_SAMPLE = 5, PROF_OTHER = 6 };
+bool prof_take(int cls, const char *name, hipEvent_t *e0, hipEvent_t *e1);
+
+template <typename... KArgs, typename... Args>
+inline void launch_k(int cls, const char *name, void (*k)(KArgs...), dim3 grid, dim3 block,
+                     size_t shmem, hipStream_t s, Args... args) {
+    hipEvent_t e0, e1;
+    if (prof_take(cls, name, &e0, &e1))
+        hipExtLaunchKernelGGL(k, grid, block, (uint32_t)shmem, s, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(k, grid, block, shmem, s, args...);
+}
 
 // ---------------------------------------------------------------------------
 // Skinny projection Y[m, o] = sum_k X[m, k] W[o, k] for up to 32 activation rows
@@ -61,12 +80,9 @@ void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s);
 // lm_head: logits = h W^T over V rows, with per-workgroup top-2 records for the
 // argmax, then a per-row reduction.
 // ---------------------------------------------------------------------------
-#ifndef DBF_HEAD_NA
-#define DBF_HEAD_NA 8
-#endif
-constexpr int HEAD_NA = DBF_HEAD_NA;  // 16*HEAD_NA vocabulary rows per wave unit
+constexpr int HEAD_NA = 8;  // 16*HEAD_NA vocabulary rows per wave unit
 int head_units(int V);
-int head_blocks(int V);  // workgroups of the head launch (4 wave units each)
+int head_blocks(int V);  // workgroups of the head launch (8 wave units each)
 // h: F32 [M][K] hidden rows; part: [16][head_blocks(V)] top-2 records
 void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M,
                  float *logits, float4 *part, hipStream_t s);
@@ -245,6 +261,7 @@ struct MoeRouteArgs {
     float *coef;            // out: [max_slots][16] routing weight of each row (0: not routed)
     float *shared_scale;    // out: [16] sigmoid(x . w_sg) per row
     int32_t *sel;           // out: [16][top_k] selected experts per row (descending weight)
+    int32_t *touched_out;   // out (nullable): copy of the distinct-expert count
 };
 void launch_moe_route(const MoeRouteArgs &a, hipStream_t s);
 

@@ -144,7 +144,10 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
         a.slot_expert[off + below] = tid;
         sexp[off + below] = tid;
     }
-    if (tid == 0) *a.nslots = total;
+    if (tid == 0) {
+        *a.nslots = total;
+        if (a.touched_out) *a.touched_out = total;
+    }
     __syncthreads();
     // coefficient of (slot, row): the row's weight for the slot's expert, else 0;
     // slots past the touched ones get 0, so a reader needs no slot count
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
 }
 
 void launch_moe_route(const MoeRouteArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
+    launch_k(PROF_ROWS, "k_moe_route", k_moe_route, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
 }
 
 // Expert (and shared-expert) SwiGLU: h = silu(s_m * sum P_gate) * (s_m * sum P_up),
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(MoeSwigluArgs a) {
 
 void launch_moe_swiglu(const MoeSwigluArgs &a, hipStream_t s) {
     const int I = a.Ie > a.Is ? a.Ie : a.Is;
-    hipLaunchKernelGGL(k_moe_swiglu, dim3((I + 63) / 64, 4, a.max_slots + 1), dim3(256), 0, s, a);
+    launch_k(PROF_ROWS, "k_moe_swiglu", k_moe_swiglu, dim3((I + 63) / 64, 4, a.max_slots + 1), dim3(256), 0, s, a);
 }
 
 // x = x1 + sum_slots coef[slot][m] * down_slot + shared_scale[m] * down_shared; then the
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeCombineArgs a) {
 
 void launch_moe_combine(const MoeCombineArgs &a, hipStream_t s) {
     const int ncb = (a.H + 63) / 64;
-    hipLaunchKernelGGL(k_moe_combine, dim3(ncb, a.xs ? 4 : (a.M + 3) / 4), dim3(256), 0, s, a);
+    launch_k(PROF_ROWS, "k_moe_combine", k_moe_combine, dim3(ncb, a.xs ? 4 : (a.M + 3) / 4), dim3(256), 0, s, a);
 }
 
 }  // namespace dbf

@@ -115,15 +115,15 @@ static dim3 colsum_grid(const ColArgs &a) {
 
 void launch_colsum(const ColArgs &a, hipStream_t s) {
     if (!a.tokens && !a.gsrc[0])
-        hipLaunchKernelGGL(k_colsum<SRC_BASE>, colsum_grid(a), dim3(256), 0, s, a);
+        launch_k(PROF_ROWS, "k_colsum", k_colsum<SRC_BASE>, colsum_grid(a), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(k_colsum<SRC_ANY>, colsum_grid(a), dim3(256), 0, s, a);
+        launch_k(PROF_ROWS, "k_colsum", k_colsum<SRC_ANY>, colsum_grid(a), dim3(256), 0, s, a);
 }
 
 void launch_colsum2(const ColArgs &a0, const ColArgs &a1, hipStream_t s) {
     const dim3 g0 = colsum_grid(a0), g1 = colsum_grid(a1);
     const dim3 g(g0.x > g1.x ? g0.x : g1.x, g0.y > g1.y ? g0.y : g1.y, 2);
-    hipLaunchKernelGGL(k_colsum2, g, dim3(256), 0, s, a0, a1);
+    launch_k(PROF_ROWS, "k_colsum2", k_colsum2, g, dim3(256), 0, s, a0, a1);
 }
 
 // ---------------------------------------------------------------------------
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_final_norm(const float *x, const float 
 void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
                        float *out, hipStream_t s) {
     const int ncb = (H + 63) / 64;
-    hipLaunchKernelGGL(k_final_norm, dim3(ncb, (M + 3) / 4), dim3(256), 0, s, x, ssp, w, out, ncb, M, H,
+    launch_k(PROF_ROWS, "k_final_norm", k_final_norm, dim3(ncb, (M + 3) / 4), dim3(256), 0, s, x, ssp, w, out, ncb, M, H,
                        eps);
 }
 
@@ -296,9 +296,9 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
 
 void launch_qkv_post(const QkvPostArgs &a, hipStream_t s) {
     const dim3 grid(a.M * a.nq + (a.R + a.M) * a.nkv);
-    if (a.hd == 64) hipLaunchKernelGGL(k_qkv_post<1>, grid, dim3(64), 0, s, a);
-    else if (a.hd == 128) hipLaunchKernelGGL(k_qkv_post<2>, grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL(k_qkv_post<4>, grid, dim3(64), 0, s, a);
+    if (a.hd == 64) launch_k(PROF_ROWS, "k_qkv_post", k_qkv_post<1>, grid, dim3(64), 0, s, a);
+    else if (a.hd == 128) launch_k(PROF_ROWS, "k_qkv_post", k_qkv_post<2>, grid, dim3(64), 0, s, a);
+    else launch_k(PROF_ROWS, "k_qkv_post", k_qkv_post<4>, grid, dim3(64), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void k_swiglu(SwigluArgs a) {
 }
 
 void launch_swiglu(const SwigluArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_swiglu, dim3((a.I + 63) / 64, 4), dim3(256), 0, s, a);
+    launch_k(PROF_ROWS, "k_swiglu", k_swiglu, dim3((a.I + 63) / 64, 4), dim3(256), 0, s, a);
 }
 
 }  // namespace dbf

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(SMP_THREADS) void k_smp_stats(SmpStatArgs a) {
 }
 
 void launch_smp_stats(const SmpStatArgs &a, int rows, hipStream_t s) {
-    hipLaunchKernelGGL(k_smp_stats, dim3(a.nb, rows), dim3(SMP_THREADS), 0, s, a);
+    launch_k(PROF_SAMPLE, "k_smp_stats", k_smp_stats, dim3(a.nb, rows), dim3(SMP_THREADS), 0, s, a);
 }
 
 // Row totals from the segment records: M = max m_b, S = sum_b s_b 2^(m_b - M).
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(SMP_THREADS) void k_smp_residual(SmpResidualArgs a)
 }
 
 void launch_smp_residual(const SmpResidualArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_smp_residual, dim3(a.nb), dim3(SMP_THREADS), 0, s, a);
+    launch_k(PROF_SAMPLE, "k_smp_residual", k_smp_residual, dim3(a.nb), dim3(SMP_THREADS), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(SMP_THREADS) void k_smp_draw(SmpDrawArgs a) {
 }
 
 void launch_smp_draw(const SmpDrawArgs &a, int M, hipStream_t s) {
-    hipLaunchKernelGGL(k_smp_draw, dim3(M), dim3(SMP_THREADS), 0, s, a);
+    launch_k(PROF_SAMPLE, "k_smp_draw", k_smp_draw, dim3(M), dim3(SMP_THREADS), 0, s, a);
 }
 
 // acceptance test and free token, one workgroup
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(SMP_THREADS) void k_smp_accept(SmpAcceptArgs a) {
 }
 
 void launch_smp_accept(const SmpAcceptArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(k_smp_accept, dim3(1), dim3(SMP_THREADS), 0, s, a);
+    launch_k(PROF_SAMPLE, "k_smp_accept", k_smp_accept, dim3(1), dim3(SMP_THREADS), 0, s, a);
 }
 
 }  // namespace dbf

@@ -80,7 +80,8 @@ class BlockIO(C.Structure):
     _fields_ = [("tokens", C.c_void_p), ("x0", C.c_void_p), ("ctx", C.c_void_p),
                 ("M", C.c_int32), ("R", C.c_int32), ("hidden_out", C.c_void_p),
                 ("h_final", C.c_void_p), ("layer_hidden", C.c_void_p),
-                ("ctx_layers", C.POINTER(C.c_void_p)), ("ctx_ld", C.c_int64), ("ctx_row0", C.c_int64)]
+                ("ctx_layers", C.POINTER(C.c_void_p)), ("ctx_ld", C.c_int64), ("ctx_row0", C.c_int64),
+                ("moe_experts", C.c_void_p)]
 
 
 _lib.draft_block_forward.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(KVCache),
@@ -113,6 +114,17 @@ _lib.dbf_tiled_bytes.argtypes = [C.c_int64, C.c_int64]
 _lib.dbf_tiled_bytes.restype = C.c_size_t
 _lib.dbf_tile_weight.argtypes = [C.POINTER(Tensor), C.c_void_p, C.c_void_p]
 _lib.dbf_tile_weight.restype = C.c_int
+
+
+class ProfRecord(C.Structure):
+    _fields_ = [("cls", C.c_int32), ("reserved_", C.c_int32), ("kernel", C.c_char_p),
+                ("us", C.c_double)]
+
+
+_lib.dbf_profile_start.argtypes = [C.c_int32]
+_lib.dbf_profile_start.restype = C.c_int
+_lib.dbf_profile_stop.argtypes = [C.POINTER(ProfRecord), C.c_int32, C.POINTER(C.c_int32)]
+_lib.dbf_profile_stop.restype = C.c_int
 _lib.dbf_last_error.restype = C.c_char_p
 _lib.dbf_abi_version.restype = C.c_int
 
@@ -151,6 +163,41 @@ def _torch():
 
 def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _check_layout(t, name, dtype, min_numel=0, ndim=None):
+    """Element type, contiguity, rank and length of a tensor the entry point reads or
+    writes through a raw pointer."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+
+
+def _need(t, name, dtype, min_numel=0, ndim=None, optional=False):
+    """Checks the C ABI cannot make on a raw pointer: a device tensor of the element
+    type the entry point reads, contiguous, holding at least min_numel elements."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    _check_layout(t, name, dtype, min_numel, ndim)
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be device memory (got {t.device})")
+
+
+def _need_ws(ws, need, name="workspace"):
+    torch = _torch()
+    _need(ws, name, torch.uint8)
+    if ws.numel() < need:
+        raise ValueError(f"{name} holds {ws.numel()} bytes, needs {need}")
 
 
 def _stream(stream):
@@ -244,19 +291,42 @@ class BlockWeights:
 
 def make_cache(k, v, seq_len: int) -> KVCache:
     torch = _torch()
-    dt = BF16 if k.dtype == torch.bfloat16 else F32 if k.dtype == torch.float32 else -1
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"cache dtype {k.dtype}: F32 or BF16")
+    _need(k, "cache k", k.dtype, ndim=4)
+    _need(v, "cache v", k.dtype, ndim=4)
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"cache k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
+    dt = BF16 if k.dtype == torch.bfloat16 else F32
     L, nkv, cap, hd = k.shape
     return KVCache(k=k.data_ptr(), v=v.data_ptr(), dtype=dt, n_layers=L, n_kv_heads=nkv,
                    head_dim=hd, capacity=cap, seq_len=seq_len)
 
 
 def make_io(M, R, h_final, tokens=None, x0=None, ctx=None, hidden_out=None,
-            layer_hidden=None, ctx_layers=None, ctx_row0=0) -> BlockIO:
+            layer_hidden=None, ctx_layers=None, ctx_row0=0, moe_experts=None) -> BlockIO:
     """ctx_layers: list of n_t device tensors [positions, >= H] F32 (captured target
     layers); the R context rows are gathered from positions ctx_row0.."""
+    torch = _torch()
+    _need(h_final, "h_final", torch.float32, ndim=2)
+    H = h_final.shape[1]
+    if h_final.shape[0] < M:
+        raise ValueError(f"h_final has {h_final.shape[0]} rows, needs {M}")
+    _need(tokens, "tokens", torch.int32, M, optional=True)
+    _need(x0, "x0", torch.float32, M * H, optional=True)
+    _need(ctx, "ctx", torch.float32, 0, optional=True)
+    _need(hidden_out, "hidden_out", torch.float32, M * H, optional=True)
+    _need(layer_hidden, "layer_hidden", torch.float32, M * H, optional=True)
+    _need(moe_experts, "moe_experts", torch.int32, 1, optional=True)
+    if ctx_layers is not None:
+        for i, t in enumerate(ctx_layers):
+            if t.device.type != "cuda" or t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1:
+                raise ValueError(f"ctx_layers[{i}] must be a device F32 [positions, H] row-major tensor")
+            if t.stride(0) != ctx_layers[0].stride(0):
+                raise ValueError("ctx_layers must share one row stride")
     io = BlockIO(tokens=_ptr(tokens), x0=_ptr(x0), ctx=_ptr(ctx), M=M, R=R,
                  hidden_out=_ptr(hidden_out), h_final=_ptr(h_final),
-                 layer_hidden=_ptr(layer_hidden))
+                 layer_hidden=_ptr(layer_hidden), moe_experts=_ptr(moe_experts))
     if ctx_layers is not None:
         arr = (C.c_void_p * len(ctx_layers))(*[t.data_ptr() for t in ctx_layers])
         io._ctx_arr = arr  # the host pointer array must outlive the call
@@ -276,6 +346,7 @@ def draft_block_workspace_bytes(cfg: Config, M: int, R: int) -> int:
 
 def draft_block_forward(cfg: Config, w: BlockWeights, cache: KVCache, io: BlockIO, ws,
                         stream=None) -> None:
+    _need_ws(ws, 0)
     _check(_lib.draft_block_forward(C.byref(cfg), C.byref(w.w), C.byref(cache), C.byref(io),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -285,7 +356,14 @@ def lm_head_argmax_workspace_bytes(M: int, H: int, V: int) -> int:
 
 
 def lm_head_argmax(h, lm_head, argmax, logits=None, top2_margin=None, ws=None, stream=None) -> None:
+    torch = _torch()
+    _need(h, "h", torch.float32, ndim=2)
     M, H = h.shape
+    V = lm_head.shape[0]
+    _need(argmax, "argmax", torch.int32, M)
+    _need(logits, "logits", torch.float32, M * V, optional=True)
+    _need(top2_margin, "top2_margin", torch.float32, M, optional=True)
+    _need_ws(ws, lm_head_argmax_workspace_bytes(M, H, V))
     lt = tensor(lm_head)
     _check(_lib.lm_head_argmax(_ptr(h), M, H, C.byref(lt), _ptr(argmax), _ptr(logits),
                                _ptr(top2_margin), _ptr(ws),
@@ -294,7 +372,13 @@ def lm_head_argmax(h, lm_head, argmax, logits=None, top2_margin=None, ws=None, s
 
 
 def accept_prefix(drafts, target, result, eos=None, committed=None, stream=None) -> None:
+    torch = _torch()
+    _need(drafts, "drafts", torch.int32)
     K = drafts.numel()
+    _need(target, "target", torch.int32, K + 1)
+    _need(result, "result", torch.int32, 5)
+    _need(eos, "eos", torch.int32, optional=True)
+    _need(committed, "committed", torch.int32, K + 1, optional=True)
     n_eos = 0 if eos is None else eos.numel()
     _check(_lib.accept_prefix(_ptr(drafts), _ptr(target), K, _ptr(eos), n_eos, _ptr(result),
                               _ptr(committed), _stream(stream)))
@@ -306,7 +390,13 @@ def sample_tokens_workspace_bytes(M: int, V: int) -> int:
 
 def sample_tokens(logits, u, token, prob=None, temperature=1.0, ws=None, stream=None) -> None:
     """One draw per row of logits [M, V] from softmax(logits / T), uniforms u [M]."""
+    torch = _torch()
+    _need(logits, "logits", torch.float32, ndim=2)
     M, V = logits.shape
+    _need(u, "u", torch.float32, M)
+    _need(token, "token", torch.int32, M)
+    _need(prob, "prob", torch.float32, M, optional=True)
+    _need_ws(ws, sample_tokens_workspace_bytes(M, V))
     _check(_lib.sample_tokens(_ptr(logits), M, V, float(temperature), _ptr(u), _ptr(token), _ptr(prob),
                               _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                               _stream(stream)))
@@ -320,7 +410,16 @@ def accept_sampled(draft_logits, target_logits, draft, u, result, temperature=1.
                    committed=None, ws=None, stream=None) -> None:
     """Sampled acceptance of one drafted token: draft_logits [V], target_logits [2, V],
     draft [1] int32, u [2] uniforms, result [5] int32."""
+    torch = _torch()
+    _need(draft_logits, "draft_logits", torch.float32)
     V = draft_logits.numel()
+    _need(target_logits, "target_logits", torch.float32, 2 * V)
+    _need(draft, "draft", torch.int32, 1)
+    _need(u, "u", torch.float32, 2)
+    _need(result, "result", torch.int32, 5)
+    _need(eos, "eos", torch.int32, optional=True)
+    _need(committed, "committed", torch.int32, 2, optional=True)
+    _need_ws(ws, accept_sampled_workspace_bytes(V))
     n_eos = 0 if eos is None else eos.numel()
     _check(_lib.accept_sampled(_ptr(draft_logits), _ptr(target_logits), V, float(temperature),
                                _ptr(draft), _ptr(u), _ptr(eos), n_eos, _ptr(result), _ptr(committed),
@@ -346,6 +445,27 @@ def tile_weight(t, stream=None) -> Tiled:
 
 def kv_rollback(cache: KVCache, n: int) -> None:
     _check(_lib.kv_rollback(C.byref(cache), n))
+
+
+PROF_CLASSES = ("projections", "attention", "row_kernels", "lm_head", "accept", "sampling", "other")
+
+
+def profile_start(max_records: int = 4096) -> None:
+    """Time the library's next max_records kernel launches (measurement only)."""
+    rc = _lib.dbf_profile_start(max_records)
+    if rc != 0:
+        raise DbfError(rc, f"profile_start({max_records}) refused")
+
+
+def profile_stop(max_records: int = 4096) -> list:
+    """Stop timing; returns [(class name, kernel name, microseconds)] in launch order."""
+    recs = (ProfRecord * max_records)()
+    n = C.c_int32(0)
+    rc = _lib.dbf_profile_stop(recs, max_records, C.byref(n))
+    if rc != 0:
+        raise DbfError(rc, "profile_stop: a timed kernel's events could not be read")
+    return [(PROF_CLASSES[recs[i].cls], recs[i].kernel.decode(), recs[i].us)
+            for i in range(min(n.value, max_records))]
 
 
 def abi_version() -> int:
