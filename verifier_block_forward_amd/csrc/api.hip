@@ -65,11 +65,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 struct Plan {
     int H, qt, kt, I, Kin, rd;
-    GemmPlan in, q, k, v, g, o, gate, up, down;
+    GemmPlan in, q, k, v, g, gate, up, down;
     size_t xres, x1, xs_blk, xs_T, xs_hctx, xs_h, xs_o, xs_ff, qbuf, gbuf, attn;
     size_t ssp_x, ssp_x1, ssp_ctx, ssp_e, ssp_h;
-    int ncb;
-    size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_o, p_gate, p_up, p_down;
+    int ncb, ncb16;  // row-scale partials per row: 64-column (row kernels) and 16-column (O epilogue)
+    size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_gate, p_up, p_down;
     // MoE
     int max_slots;
     GemmPlan router, sgi, shg, eg, ed, shd;
@@ -97,7 +97,6 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.k = gemm_plan_lds(p.kt, p.H, 2, TARGET_UNITS / 4, nbq);
     p.v = p.k;
     p.g = p.q;
-    p.o = gemm_plan(p.H, p.qt, na, TARGET_UNITS / 2);
     if (c.ffn_kind == DBF_FFN_DENSE) {
         p.gate = gemm_plan_lds(p.I, p.H, 2, TARGET_UNITS / 4, 1);
         p.up = p.gate;
@@ -120,8 +119,9 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.xs_o = take(split_tile_bytes(p.qt));
     p.xs_ff = take(split_tile_bytes(p.I > 0 ? p.I : 32));
     p.ncb = (p.H + 63) / 64;
+    p.ncb16 = (p.H + FULL_SSP_COLS - 1) / FULL_SSP_COLS;
     p.ssp_x = take((size_t)16 * p.ncb * f);
-    p.ssp_x1 = take((size_t)16 * p.ncb * f);
+    p.ssp_x1 = take((size_t)16 * p.ncb16 * f);
     p.ssp_ctx = take((size_t)16 * p.ncb * f);
     p.ssp_e = take((size_t)16 * p.ncb * f);
     p.ssp_h = take((size_t)16 * p.ncb * f);
@@ -134,7 +134,6 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.p_k = take((size_t)p.k.ksplit * rows_kv * p.kt * f);
     p.p_v = take((size_t)p.v.ksplit * rows_kv * p.kt * f);
     p.p_g = take((size_t)p.g.ksplit * 16 * p.qt * f);
-    p.p_o = take((size_t)p.o.ksplit * 16 * p.H * f);
     if (c.ffn_kind == DBF_FFN_DENSE) {
         p.p_gate = take((size_t)p.gate.ksplit * 16 * p.I * f);
         p.p_up = take((size_t)p.up.ksplit * 16 * p.I * f);
@@ -590,22 +589,20 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             launch_attn_combine(ca, st);
         }
         {
-            SegList sl;
-            sl.add(L.wo, H, qt, p.o, at<float>(ws, p.p_o), xs_o);
-            sl.launch(st);
-            // x1 = x + o Wo^T; split(x1 (.) post_norm) for the FFN
-            ColArgs a = col();
-            a.M = M;
-            a.base = xres;
-            a.ldb = H;
-            a.p0 = at<float>(ws, p.p_o);
-            a.ks0 = p.o.ksplit;
-            a.rows0 = 16;
-            a.out = x1;
-            a.w = (const float *)L.post_norm.data;
-            a.xs = xs_blk;
-            a.ssp_out = ssp_x1;
-            launch_colsum(a, st);
+            // x1 = x + o Wo^T; split(x1 (.) post_norm) and its sums of squares for the FFN
+            FullArgs fa{};
+            fa.W = (const uint16_t *)L.wo.data;
+            fa.tiled = L.wo.dtype == DBF_BF16_T16;
+            fa.xs = xs_o;
+            fa.N = H;
+            fa.K = qt;
+            fa.M = M;
+            fa.base = xres;
+            fa.out = x1;
+            fa.w = (const float *)L.post_norm.data;
+            fa.ssp_out = ssp_x1;
+            fa.xs_out = xs_blk;
+            launch_gemm_full(fa, st);
         }
         if (c.ffn_kind == DBF_FFN_DENSE) {
             {
@@ -619,7 +616,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 sa.ksg = p.gate.ksplit;
                 sa.ksu = p.up.ksplit;
                 sa.ssp = ssp_x1;
-                sa.ncb = ncb;
+                sa.ncb = p.ncb16;
                 sa.H = H;
                 sa.eps = eps;
                 sa.M = M;
@@ -650,7 +647,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 ra.p_sgi = at<float>(ws, p.p_sgi);
                 ra.ks_sgi = p.sgi.ksplit;
                 ra.ssp = ssp_x1;
-                ra.ncb = ncb;
+                ra.ncb = p.ncb16;
                 ra.H = H;
                 ra.eps = eps;
                 ra.M = M;
@@ -682,7 +679,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 sa.psu = at<float>(ws, p.p_shu);
                 sa.ks_sh = p.shg.ksplit;
                 sa.ssp = ssp_x1;
-                sa.ncb = ncb;
+                sa.ncb = p.ncb16;
                 sa.H = H;
                 sa.eps = eps;
                 sa.M = M;

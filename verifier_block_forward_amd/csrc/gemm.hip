@@ -371,6 +371,115 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
         }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-K projection with the residual epilogue (FullArgs in kernels.hpp). A
+// workgroup of FULL_W waves owns NT output tiles of 16 columns over all of K: wave w
+// streams k-steps [S w / FULL_W, S (w + 1) / FULL_W) of every tile with its own
+// activation slice (skinny_mainloop), the accumulators are summed through LDS in
+// wave order, and the workgroup finishes its complete outputs: the residual add, the
+// split of out (.) w for the next projection and the sums of squares of out. The
+// residual rows and norm weights the epilogue needs are loaded before the main loop.
+// NT = 1 when a wave has at most FULL_SHORT k-steps (more workgroups for short K),
+// else 2 (each wave's activation slice then feeds two weight tiles).
+constexpr int FULL_W = 8;       // waves per workgroup
+constexpr int FULL_SHORT = 16;  // k-steps per wave up to which one tile per workgroup is used
+
+template <int NT>
+__global__ __launch_bounds__(64 * FULL_W) void k_gemm_full(FullArgs a) {
+    static_assert(256 * NT <= 64 * FULL_W, "one epilogue element per thread");
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(a.W), "s"(a.tiled), "s"(a.xs), "s"(a.N), "s"(a.K), "s"(a.M), "s"(a.base),
+                 "s"(a.out), "s"(a.copy0), "s"(a.copy1), "s"(a.w), "s"(a.ssp_out), "s"(a.xs_out));
+    __shared__ float4 red[FULL_W][NT][64];
+    __shared__ float res[NT * 16][17];  // [output column of the workgroup][activation row], padded
+    __shared__ float sspp[FULL_W][16];  // per-wave sums of squares
+    const int lane = threadIdx.x & 63, wv = wave_id(), tid = threadIdx.x;
+    const int N = a.N, K = a.K, S = (K + 31) >> 5;
+    const int n0 = blockIdx.x * 16 * NT;
+    const int r = lane & 15, g = lane >> 4;
+
+    // epilogue element of this thread: activation row m, output column n
+    const int m = tid & 15, nl = tid >> 4, n = n0 + nl;
+    const bool has_e = tid < 256 * NT;
+    const bool in_e = has_e && m < a.M && n < N;
+    float bv = 0.f, wn = 1.f;
+    if (in_e) {
+        if (a.base) bv = a.base[(size_t)m * N + n];
+        if (a.w) wn = a.w[n];
+    }
+
+    const uint16_t *wrow[NT];
+    const int wstep = a.tiled ? 512 : 32;
+    const int T = (N + 15) >> 4;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const int tt = n0 / 16 + t;
+        if (a.tiled) {
+            const int tc = tt > T - 1 ? T - 1 : tt;  // tiles past N: re-read, result dropped
+            wrow[t] = a.W + ((size_t)tc * S * 64 + lane) * 8;
+        } else {
+            int row = tt * 16 + r;
+            if (row > N - 1) row = N - 1;
+            wrow[t] = a.W + (size_t)row * K + 8 * g;
+        }
+    }
+    f32x4 acc[NT][1];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int s0 = (S * wv) / FULL_W, s1 = (S * (wv + 1)) / FULL_W;
+    if (s1 > s0) {
+        const uint16_t *xs[1] = {a.xs};
+        skinny_mainloop<NT, 1, GEMM_PIPE>(wrow, wstep, a.tiled != 0, xs, K, s0, s1, lane, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        red[wv][t][lane] = make_float4(acc[t][0][0], acc[t][0][1], acc[t][0][2], acc[t][0][3]);
+    __syncthreads();
+    // sum the waves' accumulators in wave order: element (tile t, lane l, j) is output
+    // column 16 t + 4 (l / 16) + j of the workgroup for activation row l % 16
+    for (int e = tid; e < NT * 256; e += 64 * FULL_W) {
+        const int t = e >> 8, l = (e >> 2) & 63, j = e & 3;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < FULL_W; w++) sum += ((const float *)&red[w][t][l])[j];
+        res[t * 16 + 4 * (l >> 4) + j][l & 15] = sum;
+    }
+    __syncthreads();
+
+    float v = 0.f;
+    if (in_e) {
+        v = bv + res[nl][m];
+        a.out[(size_t)m * N + n] = v;
+        if (a.copy0) a.copy0[(size_t)m * N + n] = v;
+        if (a.copy1) a.copy1[(size_t)m * N + n] = v;
+    }
+    const int Np = (N + 31) & ~31;
+    if (has_e && n < Np) split_store(a.xs_out, m, n, v * wn);
+    if (a.ssp_out) {
+        // sum of squares over each 16-column tile: a wave's lanes hold 4 columns x 16
+        // rows; the four waves of a tile are then added in order
+        float ss = v * v;
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lane < 16) sspp[wv][lane] = ss;
+        __syncthreads();
+        if (tid < 16 * NT) {
+            const int t = tid >> 4, mm = tid & 15;
+            const float q = (sspp[4 * t][mm] + sspp[4 * t + 1][mm]) + (sspp[4 * t + 2][mm] + sspp[4 * t + 3][mm]);
+            const int blk = n0 / 16 + t, nblk = (N + 15) / 16;
+            if (blk < nblk) a.ssp_out[(size_t)mm * nblk + blk] = q;
+        }
+    }
+}
+
+void launch_gemm_full(const FullArgs &a, hipStream_t s) {
+    const int S = (a.K + 31) / 32, Np = (a.N + 31) & ~31;
+    if ((S + FULL_W - 1) / FULL_W <= FULL_SHORT)
+        launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<1>, dim3((Np + 15) / 16), dim3(64 * FULL_W), 0, s, a);
+    else
+        launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<2>, dim3((Np + 31) / 32), dim3(64 * FULL_W), 0, s, a);
+}
+
 GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {
     GemmPlan p{0, 0, 0, na, 0};
     if (N < 1 || K < 1 || na < 1) return p;  // empty projection: no units

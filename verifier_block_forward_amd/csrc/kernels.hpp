@@ -77,6 +77,29 @@ inline int plan_units(const GemmPlan &p) {
 void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Whole-K projection with the residual epilogue: one workgroup owns 16 or 32 output
+// columns and all of K, its waves split K and reduce through LDS in a fixed order,
+// so the workgroup holds complete outputs and finishes the row work itself:
+//   out = base + X W^T (the residual add); xs_out <- split(out (.) w) for the next
+//   projection; ssp_out[m][n / 16] <- sum of out^2 over each 16-column block (the
+//   row-scale partials of the next RMSNorm); copies of out on request.
+// xs_out is a split tile of K = N (padding columns and rows >= M written as zeros).
+// ---------------------------------------------------------------------------
+struct FullArgs {
+    const uint16_t *W;       // [N, K]
+    int tiled;               // DBF_BF16_T16 layout
+    const uint16_t *xs;      // split tile of the input, K columns, 16 rows
+    int N, K, M;
+    const float *base;       // [M][N] rows added to the product, or null
+    float *out, *copy0, *copy1;  // [M][N] (copies optional)
+    const float *w;          // norm weight [N] applied before the split, or null (1)
+    float *ssp_out;          // [16][ceil(N/16)], or null
+    uint16_t *xs_out;        // split tile, K = N
+};
+constexpr int FULL_SSP_COLS = 16;  // columns per sum-of-squares partial
+void launch_gemm_full(const FullArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // lm_head: logits = h W^T over V rows, with per-workgroup top-2 records for the
 // argmax, then a per-row reduction.
 // ---------------------------------------------------------------------------
@@ -152,6 +175,7 @@ struct QkvPostArgs {
     long long capacity;
 };
 void launch_qkv_post(const QkvPostArgs &a, hipStream_t s);
+
 
 struct SwigluArgs {
     const float *pg, *pu;
