@@ -541,6 +541,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             qa.ssp_x = ssp_x;
             qa.ssp_ctx = ssp_ctx;
             qa.ncb = ncb;
+            qa.ncb_ctx = ncb;
             qa.H = H;
             qa.q_norm = (const float *)L.q_norm.data;
             qa.k_norm = (const float *)L.k_norm.data;
@@ -741,7 +742,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 launch_moe_combine(a, st);
             }
             if (last)
-                launch_final_norm(xres, ssp_x, M, H, (const float *)w->final_norm.data, eps,
+                launch_final_norm(xres, ssp_x, ncb, M, H, (const float *)w->final_norm.data, eps,
                                   io->h_final, st);
         }
     }

@@ -381,10 +381,9 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
 // residual rows and norm weights the epilogue needs are loaded before the main loop.
 // NT = 1 when a wave has at most FULL_SHORT k-steps (more workgroups for short K),
 // else 2 (each wave's activation slice then feeds two weight tiles).
-constexpr int FULL_W = 8;       // waves per workgroup
 constexpr int FULL_SHORT = 16;  // k-steps per wave up to which one tile per workgroup is used
 
-template <int NT>
+template <int FULL_W, int NT>
 __global__ __launch_bounds__(64 * FULL_W) void k_gemm_full(FullArgs a) {
     static_assert(256 * NT <= 64 * FULL_W, "one epilogue element per thread");
     // the arguments into scalar registers in one round trip
@@ -473,11 +472,12 @@ __global__ __launch_bounds__(64 * FULL_W) void k_gemm_full(FullArgs a) {
 }
 
 void launch_gemm_full(const FullArgs &a, hipStream_t s) {
+    constexpr int W = 8;
     const int S = (a.K + 31) / 32, Np = (a.N + 31) & ~31;
-    if ((S + FULL_W - 1) / FULL_W <= FULL_SHORT)
-        launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<1>, dim3((Np + 15) / 16), dim3(64 * FULL_W), 0, s, a);
+    if ((S + W - 1) / W <= FULL_SHORT)
+        launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<W, 1>, dim3((Np + 15) / 16), dim3(64 * W), 0, s, a);
     else
-        launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<2>, dim3((Np + 31) / 32), dim3(64 * FULL_W), 0, s, a);
+        launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<W, 2>, dim3((Np + 31) / 32), dim3(64 * W), 0, s, a);
 }
 
 GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {

@@ -148,7 +148,8 @@ struct ColArgs {
 };
 void launch_colsum(const ColArgs &a, hipStream_t s);
 void launch_colsum2(const ColArgs &a0, const ColArgs &a1, hipStream_t s);  // independent jobs
-void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
+// ssp: [16][ncb] row-scale partials of x (ncb per row: 64- or 16-column partials)
+void launch_final_norm(const float *x, const float *ssp, int ncb, int M, int H, const float *w, float eps,
                        float *out, hipStream_t s);
 
 constexpr int ROPE_MAX_PAIRS = 128;  // rotary_dim <= 256
@@ -160,8 +161,8 @@ struct QkvPostArgs {
     const float *pg;   // [ksg][16][qt] or null
     int ksq, ksk, ksv, ksg, rows_kv, kv_block_row0;
     const float *ssp_x;    // block rows' norm partials [16][ncb]
-    const float *ssp_ctx;  // context rows' norm partials [16][ncb]
-    int ncb, H;
+    const float *ssp_ctx;  // context rows' norm partials [16][ncb_ctx]
+    int ncb, ncb_ctx, H;
     const float *q_norm, *k_norm;
     float eps;
     double inv_freq[ROPE_MAX_PAIRS];  // theta^(-2j/rotary_dim), j < rotary_dim/2, in F64

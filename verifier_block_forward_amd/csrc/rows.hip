@@ -142,11 +142,10 @@ __global__ __launch_bounds__(256) void k_final_norm(const float *x, const float 
     if (k < H) out[(size_t)m * H + k] = xv * s * wv;
 }
 
-void launch_final_norm(const float *x, const float *ssp, int M, int H, const float *w, float eps,
+void launch_final_norm(const float *x, const float *ssp, int ncb, int M, int H, const float *w, float eps,
                        float *out, hipStream_t s) {
-    const int ncb = (H + 63) / 64;
-    launch_k(PROF_ROWS, "k_final_norm", k_final_norm, dim3(ncb, (M + 3) / 4), dim3(256), 0, s, x, ssp, w, out, ncb, M, H,
-                       eps);
+    launch_k(PROF_ROWS, "k_final_norm", k_final_norm, dim3((H + 63) / 64, (M + 3) / 4), dim3(256), 0, s, x,
+             ssp, w, out, ncb, M, H, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -167,7 +166,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
     // the arguments into scalar registers in one round trip
     asm volatile("" ::"s"(a.pq), "s"(a.pk), "s"(a.pv), "s"(a.pg), "s"(a.ksq), "s"(a.ksk), "s"(a.ksv),
                  "s"(a.ksg), "s"(a.rows_kv), "s"(a.kv_block_row0), "s"(a.ssp_x), "s"(a.ssp_ctx),
-                 "s"(a.ncb), "s"(a.H), "s"(a.q_norm), "s"(a.k_norm), "s"(a.eps), "s"(a.rotary_dim),
+                 "s"(a.ncb), "s"(a.ncb_ctx), "s"(a.H), "s"(a.q_norm), "s"(a.k_norm), "s"(a.eps), "s"(a.rotary_dim),
                  "s"(a.M), "s"(a.R), "s"(a.nq), "s"(a.nkv), "s"(a.P0), "s"(a.q_out), "s"(a.g_out),
                  "s"(a.cache_k), "s"(a.cache_v), "s"(a.kv_bf16), "s"(a.capacity));
     __shared__ float vec[64 * CPL];
@@ -178,6 +177,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
     int row, head;         // row within its group (block rows or all kv rows), head index
     long long pos;
     const float *sspr;     // norm partials of the source row (its RMSNorm scale)
+    int ncb;               // partials per row in sspr
     const float *src, *src2, *wn;  // partials of the head and of its gate / value, head-norm weight
     int ks, ks2, prow, N, rows;
     if (isq) {
@@ -185,6 +185,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
         head = b % a.nq;
         pos = a.P0 + a.R + row;
         sspr = a.ssp_x + (size_t)row * a.ncb;
+        ncb = a.ncb;
         src = a.pq;
         ks = a.ksq;
         src2 = a.pg;
@@ -200,7 +201,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
         const bool ctx = row < a.R;
         const int m = ctx ? row : row - a.R;
         pos = ctx ? a.P0 + row : a.P0 + a.R + m;
-        sspr = (ctx ? a.ssp_ctx : a.ssp_x) + (size_t)m * a.ncb;
+        sspr = ctx ? a.ssp_ctx + (size_t)m * a.ncb_ctx : a.ssp_x + (size_t)m * a.ncb;
+        ncb = ctx ? a.ncb_ctx : a.ncb;
         src = a.pk;
         ks = a.ksk;
         src2 = a.pv;
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
     const size_t rowoff = (size_t)prow * N + (size_t)head * hd + lane;
     // the row-scale share, the head-norm weights and the RoPE frequencies go out
     // with the partials (one wait)
-    const float f = row_scale_first(sspr, a.ncb);
+    const float f = row_scale_first(sspr, ncb);
     const int half = a.rotary_dim / 2;
     float wnv[CPL];
     double ifr[CPL];
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(QkvPostArgs a) {
             sum_partials_n<CPL>(bb, ks2, stride, side);
         }
     }
-    const float s = row_scale_finish(f, sspr, a.ncb, a.H, a.eps);
+    const float s = row_scale_finish(f, sspr, ncb, a.H, a.eps);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; i++) {
