@@ -239,6 +239,24 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
 
 size_t lm_head_argmax_workspace_bytes(int32_t M, int32_t H, int32_t V);
 
+/* lm_head_argmax without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, results and errors as lm_head_argmax, whose
+ * kernels it runs; the records between its two kernels live in a static device
+ * array of DBF_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
+ * runs on until the process ends. The call allocates nothing.
+ *   V must be <= DBF_NOALLOC_MAX_VOCAB: a larger vocabulary is refused with
+ *   DBF_ERANGE before anything is enqueued.
+ *   Every call on one device shares that device's array: calls that may overlap on
+ *   one device (different streams, different threads) race and must be ordered by
+ *   the caller. Each call writes every record it reads, so nothing has to be cleared
+ *   between calls. The first call on a device looks the array's address up
+ *   (hipGetSymbolAddress) with that device current. */
+#define DBF_NOALLOC_MAX_VOCAB (1 << 20)
+#define DBF_NOALLOC_SCRATCH_BYTES 262144 /* = lm_head_argmax_workspace_bytes(16, H, DBF_NOALLOC_MAX_VOCAB) */
+int lm_head_argmax_noalloc(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head,
+                           int32_t *argmax, float *logits, float *top2_margin, void *stream);
+
 /* Greedy accept-prefix walk ([ORCH] module doc, "Greedy accept-walk consistency
  * invariant", and per-round steps 7-8). Device pointers:
  *   drafts [K] int32, target [K+1] int32 (the target's argmax at each position),

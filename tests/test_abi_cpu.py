@@ -320,3 +320,16 @@ def test_profile_switch_host_side():
     assert dbf.lib().dbf_profile_start(70000) == dbf.EINVAL
     dbf.profile_start(16)
     assert dbf.profile_stop() == []
+
+
+def test_noalloc_head_refuses_vocabulary_past_its_scratch():
+    """lm_head_argmax_noalloc refuses, before any device work, a vocabulary whose
+    records do not fit its static scratch (and takes the largest one that does)."""
+    assert dbf.lm_head_argmax_workspace_bytes(16, 2816, dbf.NOALLOC_MAX_VOCAB) == 262144
+    assert dbf.lm_head_argmax_workspace_bytes(16, 2816, dbf.NOALLOC_MAX_VOCAB + 1) > 262144
+    lm = dbf.Tensor(data=0x1000, dtype=dbf.BF16, ndim=2)
+    lm.shape[0], lm.shape[1] = dbf.NOALLOC_MAX_VOCAB + 1, 64
+    rc = dbf.lib().lm_head_argmax_noalloc(C.c_void_p(0x2000), 4, 64, C.byref(lm), C.c_void_p(0x3000),
+                                          None, None, None)
+    assert rc == dbf.ERANGE
+    assert "static" in dbf.last_error()

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/dbf.h"
@@ -756,9 +757,16 @@ size_t lm_head_argmax_workspace_bytes(int32_t M, int32_t H, int32_t V) {
     return align256((size_t)head_blocks(V) * 16 * sizeof(float4));
 }
 
-int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, int32_t *argmax,
-                   float *logits, float *top2_margin, void *ws, size_t ws_bytes, void *stream) {
-    g_err.clear();
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// lm_head + argmax. The checks and the launches are shared by the entry point
+// that takes the caller's workspace and the one that uses the library's static
+// device scratch (for callers that cannot allocate).
+namespace {
+
+int head_check(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, const int32_t *argmax,
+               int *V_out) {
     if (!h || !lm_head || !argmax) return fail(DBF_EINVAL, "h, lm_head and argmax are required");
     if (M < 1 || M > DBF_MAX_M) return fail(DBF_EINVAL, "M = %d outside [1, %d]", M, DBF_MAX_M);
     if (H < 8 || H % 8) return fail(DBF_ESHAPE, "H = %d must be a positive multiple of 8", H);
@@ -768,11 +776,12 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
         return fail(DBF_EDTYPE, "lm_head dtype %s, expected BF16 or BF16_T16", dtname(lm_head->dtype));
     if (!lm_head->data) return fail(DBF_EINVAL, "lm_head data is null");
     if (lm_head->shape[0] > 0x7fffffffLL) return fail(DBF_ESHAPE, "vocabulary too large");
-    const int V = (int)lm_head->shape[0];
-    const size_t need = lm_head_argmax_workspace_bytes(M, H, V);
-    if (!ws) return fail(DBF_EWORKSPACE, "workspace is null");
-    if ((uintptr_t)ws % 256) return fail(DBF_EWORKSPACE, "workspace not 256-byte aligned");
-    if (ws_bytes < need) return fail(DBF_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    *V_out = (int)lm_head->shape[0];
+    return DBF_OK;
+}
+
+int head_launch(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, int V, int32_t *argmax,
+                float *logits, float *top2_margin, void *ws, void *stream) {
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();
     float4 *part = (float4 *)ws;
@@ -780,6 +789,70 @@ int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_he
                 part, st);
     launch_head_reduce(part, head_blocks(V), M, argmax, top2_margin, st);
     return hip_check("lm_head_argmax launch");
+}
+
+}  // namespace
+
+// Static device scratch of lm_head_argmax_noalloc: the per-workgroup top-2 records
+// (V/1024 workgroups x 16 rows x 16 bytes). Each device the library runs on holds
+// its own copy for the life of the process. Host code never uses this name as an
+// address: the device address is taken once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[DBF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// device address of `scratch` on the current device (looked up on the first call)
+int scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DBF_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return fail(DBF_EHIP, "device %d outside the %d the static scratch supports", dev, SCRATCH_MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DBF_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DBF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lm_head_argmax(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, int32_t *argmax,
+                   float *logits, float *top2_margin, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    int V = 0;
+    CHECK(head_check(h, M, H, lm_head, argmax, &V));
+    const size_t need = lm_head_argmax_workspace_bytes(M, H, V);
+    if (!ws) return fail(DBF_EWORKSPACE, "workspace is null");
+    if ((uintptr_t)ws % 256) return fail(DBF_EWORKSPACE, "workspace not 256-byte aligned");
+    if (ws_bytes < need) return fail(DBF_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return head_launch(h, M, H, lm_head, V, argmax, logits, top2_margin, ws, stream);
+}
+
+int lm_head_argmax_noalloc(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head, int32_t *argmax,
+                           float *logits, float *top2_margin, void *stream) {
+    g_err.clear();
+    int V = 0;
+    CHECK(head_check(h, M, H, lm_head, argmax, &V));
+    const size_t need = lm_head_argmax_workspace_bytes(M, H, V);
+    if (need > DBF_NOALLOC_SCRATCH_BYTES)
+        return fail(DBF_ERANGE, "vocabulary %d needs %zu bytes of scratch, more than the static %d "
+                                "(lm_head_argmax_noalloc takes V <= %d)",
+                    V, need, DBF_NOALLOC_SCRATCH_BYTES, DBF_NOALLOC_MAX_VOCAB);
+    void *ptr = nullptr;
+    CHECK(scratch_address(&ptr));
+    return head_launch(h, M, H, lm_head, V, argmax, logits, top2_margin, ptr, stream);
 }
 
 int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const int32_t *eos,

@@ -31,6 +31,7 @@ KIND_DFLASH, KIND_MTP = 0, 1
 FFN_DENSE, FFN_MOE = 0, 1
 MAX_M = 16
 MAX_R = 16
+NOALLOC_MAX_VOCAB = 1 << 20
 
 
 class DbfError(RuntimeError):
@@ -92,6 +93,9 @@ _lib.draft_block_workspace_bytes.restype = C.c_size_t
 _lib.lm_head_argmax.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(Tensor), C.c_void_p,
                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
 _lib.lm_head_argmax.restype = C.c_int
+_lib.lm_head_argmax_noalloc.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(Tensor), C.c_void_p,
+                                        C.c_void_p, C.c_void_p, C.c_void_p]
+_lib.lm_head_argmax_noalloc.restype = C.c_int
 _lib.lm_head_argmax_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
 _lib.lm_head_argmax_workspace_bytes.restype = C.c_size_t
 _lib.accept_prefix.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
@@ -369,6 +373,20 @@ def lm_head_argmax(h, lm_head, argmax, logits=None, top2_margin=None, ws=None, s
                                _ptr(top2_margin), _ptr(ws),
                                0 if ws is None else ws.numel() * ws.element_size(),
                                _stream(stream)))
+
+
+def lm_head_argmax_noalloc(h, lm_head, argmax, logits=None, top2_margin=None, stream=None) -> None:
+    """lm_head_argmax on the library's static device scratch (no workspace argument)."""
+    torch = _torch()
+    _need(h, "h", torch.float32, ndim=2)
+    M, H = h.shape
+    V = lm_head.shape[0]
+    _need(argmax, "argmax", torch.int32, M)
+    _need(logits, "logits", torch.float32, M * V, optional=True)
+    _need(top2_margin, "top2_margin", torch.float32, M, optional=True)
+    lt = tensor(lm_head)
+    _check(_lib.lm_head_argmax_noalloc(_ptr(h), M, H, C.byref(lt), _ptr(argmax), _ptr(logits),
+                                       _ptr(top2_margin), _stream(stream)))
 
 
 def accept_prefix(drafts, target, result, eos=None, committed=None, stream=None) -> None:
