@@ -1,10 +1,12 @@
 """Benchmark of the drafter hot path on one MI355X.
 
 One step = one pass of the whole hot path over one block of synthetic input:
-draft_block_forward (input projection, every decoder layer, final norm) ->
-lm_head_argmax -> accept_prefix -> kv_rollback(R + M) (the rollback keeps the
-cache at the same length from step to step). All inputs and weights are resident
-in HBM before the timed region. Prints one JSON line.
+draft_block_forward (input projection, every decoder layer, final norm, and, in
+the same call, the shared lm_head argmax and the greedy accept walk) ->
+kv_rollback(R + M) (the rollback keeps the cache at the same length from step to
+step). --unfused runs the same step as three calls (draft_block_forward,
+lm_head_argmax, accept_prefix). All inputs and weights are resident in HBM before
+the timed region. Prints one JSON line.
 
 Default workload: the DFlash-style drafter block, 5 layers, hidden 2816, 16 q / 8
 kv heads of 128, SwiGLU 8448, vocab 262144, K+1 = 16 block rows plus 16 new
@@ -36,7 +38,6 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 TARGET_FRAC = {"projections": 0.70, "attention": 0.50}
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_c1.json")
 FLUSH_BYTES = 512 << 20
 
 
@@ -79,21 +80,20 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def counters(config_name: str) -> dict:
-    """Per-kernel HBM traffic from the committed rocprofv3 PMC summary, keeping only
-    the kernels whose sources are unchanged since the counters were taken."""
+def counters(config_name: str):
+    """HBM traffic per kernel and per class from the committed rocprofv3 PMC summary
+    of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), keeping only
+    what was measured on the current kernel sources: (kernels, classes)."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", f"counters_{config_name}.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
-        return {}
-    if d.get("workload") != config_name:
-        return {}
-    out = {}
-    for name, k in d.get("kernels", {}).items():
-        if k.get("source_hash") == source_hash(k.get("sources", [])):
-            out[name] = k
-    return out
+        return {}, {}
+    kernels = {name: k for name, k in d.get("kernels", {}).items()
+               if k.get("source_hash") == source_hash(k.get("sources", []))}
+    classes = {c: v["traffic_bytes_per_step"] for c, v in d.get("classes", {}).items()
+               if all(n in kernels for n in v["kernels"])}
+    return kernels, classes
 
 
 def cpu_baseline(cfg, w_host, in_host, budget_s: float):
@@ -146,6 +146,9 @@ def main():
                     help="MTP workloads: the sampled (speculative-sampling) round instead of the greedy "
                          "walk -- lm_head logits, sample_tokens for the draft, accept_sampled against "
                          "seeded target logits")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as separate draft_block_forward, lm_head_argmax and "
+                         "accept_prefix calls instead of one fused call")
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device copy run after the timed region (counter scale)")
@@ -213,6 +216,12 @@ def main():
     target_np, accept_j = synth.accept_targets(drafts.cpu().numpy(), V, cfg.seed)
     target = up(target_np)
     touched = moe_experts.cpu().tolist() if moe_experts is not None else None
+    fused = not (args.unfused or args.sampled)
+    if fused:
+        # the whole step in one call: block, shared head (final norm folded in) and walk
+        io_f = dbf.make_io(M, R, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"), ctx=inp.get("ctx"),
+                           moe_experts=moe_experts, lm_head=w_dev["lm_head"], argmax=argmax, target=target,
+                           accept_result=result)
 
     if args.sampled:
         # the sampled MTP round: the drafter's logits row, one draft drawn from it,
@@ -228,11 +237,17 @@ def main():
         ws_smp = torch.empty(dbf.sample_tokens_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
         ws_acc = torch.empty(dbf.accept_sampled_workspace_bytes(V), dtype=torch.uint8, device=dev)
 
-    def step(ev=None, st=None, io_=io, R_=R):
+    def step(ev=None, st=None, io_=None, R_=R):
         st = stream if st is None else st
         if ev is not None:
             ev[0].record(st)
-        dbf.draft_block_forward(ccfg, bw, kv, io_, ws, st)
+        if fused:
+            dbf.draft_block_forward(ccfg, bw, kv, io_ or io_f, ws, st)
+            if ev is not None:
+                ev[3].record(st)
+            dbf.kv_rollback(kv, R_ + M)
+            return
+        dbf.draft_block_forward(ccfg, bw, kv, io_ or io, ws, st)
         if ev is not None:
             ev[1].record(st)
         if args.sampled:
@@ -266,9 +281,6 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    block_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    head_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    acc_ms = [e[2].elapsed_time(e[3]) for e in evs]
     step_ev_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_step = wall * 1e3 / args.steps
     value = M * args.steps / wall
@@ -294,13 +306,14 @@ def main():
         k[1] += us
 
     ab = class_bytes(cfg, M, R, in_host["seq_len"], touched)
-    cnt = counters(cfg.name)
+    cnt, cnt_cls = counters(cfg.name)
     classes = {}
     for cls in ("projections", "attention", "row_kernels", "lm_head"):
         us = per_class_us.get(cls, 0.0) / n_prof
         gbps = ab[cls] / (us * 1e-6) / 1e9 if us > 0 else 0.0
         entry = {"bytes": ab[cls], "us_per_step": round(us, 2), "achieved_gbps": round(gbps, 1),
                  "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        entry["traffic"] = cnt_cls.get(cls)
         if cls in TARGET_FRAC:
             entry["target"] = TARGET_FRAC[cls]
             entry["meets_target"] = bool(gbps / PEAK_HBM_GBPS >= TARGET_FRAC[cls])
@@ -331,8 +344,12 @@ def main():
                          "rows_per_s_p50": round(M / (float(np.median(cold_ms)) * 1e-3), 1)}
         # ---- R = 1 new context row (the smallest round: one draft accepted less than needed)
         if cfg.kind == "dflash" and R > 1:
-            io1 = dbf.make_io(M, 1, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"),
-                              ctx=inp["ctx"][:1].contiguous())
+            ctx1 = inp["ctx"][:1].contiguous()
+            if fused:
+                io1 = dbf.make_io(M, 1, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"), ctx=ctx1,
+                                  lm_head=w_dev["lm_head"], argmax=argmax, target=target, accept_result=result)
+            else:
+                io1 = dbf.make_io(M, 1, h_final, tokens=inp.get("tokens"), x0=inp.get("x0"), ctx=ctx1)
             for _ in range(args.warmup):
                 step(io_=io1, R_=1)
             r1 = new_events(args.steps)
@@ -410,9 +427,8 @@ def main():
                   "weights_resident_bytes": bw.resident_bytes(),
                   "gbps_wall": round(ab["total"] / (ms_step * 1e-3) / 1e9, 1),
                   "frac_wall": round(ab["total"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                  "ms_draft_block_forward": round(float(np.mean(block_ms)), 4),
-                  "ms_lm_head_argmax": round(float(np.mean(head_ms)), 4),
-                  "ms_accept": round(float(np.mean(acc_ms)), 4),
+                  "calls": "draft_block_forward with the shared head and accept walk fused" if fused
+                  else "draft_block_forward, lm_head_argmax, accept_prefix",
                   "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev_ms, q)), 4)
                                           for q in (10, 50, 90)],
                   "launches_per_step": round(len(recs) / n_prof, 2),

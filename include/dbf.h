@@ -180,7 +180,23 @@ typedef struct {
  *   layer_hidden [n_layers, M, H] F32 hidden after each layer, or NULL.
  *   moe_experts [n_layers] int32 out, or NULL (MoE FFN only): the number of
  *               distinct experts the layer's M rows were routed to, i.e. the
- *               experts whose weights the layer read ([MTP] `MtpFfnWeightsGpu::Moe`). */
+ *               experts whose weights the layer read ([MTP] `MtpFfnWeightsGpu::Moe`).
+ * Optional fused shared head and accept walk, in the same call ([MTP]
+ * `forward_shared_head`: the final norm, lm_head and argmax submitted together;
+ * [ORCH] per-round steps 5-8). All NULL (and n_eos 0) when not wanted.
+ *   lm_head     BF16 or BF16_T16 [V, H] with V = cfg.vocab, or NULL. When given,
+ *               the call also computes the lm_head argmax of the M normed rows (the
+ *               final RMSNorm is folded into the head's staging, h_final is still
+ *               written, with the same bits as without the head) and writes
+ *   argmax      [M] int32 (required with lm_head) and
+ *   top2_margin [M] F32 or NULL, as lm_head_argmax would.
+ *   target      [K+1] int32 or NULL (needs lm_head): the target's argmax at each
+ *               drafted position; the greedy accept walk of the block's drafts then
+ *               runs as accept_prefix would, with drafts = argmax rows 1..M-1 and
+ *               K = M - 1 for DFlash, argmax row 0 and K = 1 for MTP ([ORCH]
+ *               per-round step 5; reading of the MTP M > 1 workload: row 0 drafts).
+ *   eos, n_eos  EOS ids (n_eos in 0..1024; eos may be NULL when n_eos is 0).
+ *   accept_result [5] int32 out (required with target), committed [K+1] out or NULL. */
 typedef struct {
     const int32_t *tokens;
     const float *x0;
@@ -193,6 +209,14 @@ typedef struct {
     int64_t ctx_ld;
     int64_t ctx_row0;
     int32_t *moe_experts;
+    const dbf_tensor *lm_head;
+    int32_t *argmax;
+    float *top2_margin;
+    const int32_t *target;
+    const int32_t *eos;
+    int32_t n_eos;
+    int32_t *accept_result;
+    int32_t *committed;
 } dbf_block_io;
 
 /* Drafter block forward ([MTP] `forward_draft_with_hidden` and its helpers

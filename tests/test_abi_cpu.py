@@ -333,3 +333,52 @@ def test_noalloc_head_refuses_vocabulary_past_its_scratch():
                                           None, None, None)
     assert rc == dbf.ERANGE
     assert "static" in dbf.last_error()
+
+
+def test_fused_head_fields_validated_before_launch():
+    """The optional shared head and accept walk of draft_block_forward are checked
+    with everything else, before any launch: lm_head shape and dtype, the outputs
+    each part needs, K >= 1 for the walk, and the EOS list."""
+    bc = configs.C0
+    cfg = dbf.make_config(bc)
+    w, _ = _weights_for(bc)
+    ok = dict(k=0x2000, v=0x3000, dtype=dbf.F32, n_layers=1, n_kv_heads=2, head_dim=64, capacity=100,
+              seq_len=3)
+
+    def lm(V, H, dt=dbf.BF16):
+        t = dbf.Tensor()
+        t.data, t.dtype, t.ndim = 0x10000, dt, 2
+        t.shape[0], t.shape[1] = V, H
+        return t
+
+    def run(M=4, **kw):
+        io = dbf.BlockIO(M=M, R=0, h_final=0x4000, x0=0x4000)
+        keep = []
+        for k, v in kw.items():
+            if k == "lm_head":
+                keep.append(v)
+                io.lm_head = C.pointer(v)
+            else:
+                setattr(io, k, v)
+        cache = dbf.KVCache(**ok)
+        rc, c = _call_block(cfg, io, cache=cache, w=w)
+        assert c.seq_len == 3  # nothing ran
+        return rc, dbf.last_error()
+
+    good = lm(bc.vocab, bc.hidden)
+    assert run(lm_head=lm(bc.vocab - 1, bc.hidden), argmax=0x5000)[0] == dbf.ESHAPE
+    assert run(lm_head=lm(bc.vocab, bc.hidden, dbf.F32), argmax=0x5000)[0] == dbf.EDTYPE
+    rc, msg = run(lm_head=good)
+    assert rc == dbf.EINVAL and "argmax" in msg
+    rc, msg = run(argmax=0x5000)
+    assert rc == dbf.EINVAL and "lm_head" in msg
+    rc, msg = run(target=0x6000, accept_result=0x7000)
+    assert rc == dbf.EINVAL and "lm_head" in msg
+    rc, msg = run(lm_head=good, argmax=0x5000, target=0x6000)
+    assert rc == dbf.EINVAL and "accept_result" in msg
+    rc, msg = run(M=1, lm_head=good, argmax=0x5000, target=0x6000, accept_result=0x7000)
+    assert rc == dbf.EINVAL and "M >= 2" in msg
+    rc, msg = run(lm_head=good, argmax=0x5000, target=0x6000, accept_result=0x7000, n_eos=2)
+    assert rc == dbf.EINVAL and "eos" in msg
+    rc, msg = run(lm_head=good, argmax=0x5000, accept_result=0x7000)
+    assert rc == dbf.EINVAL and "target" in msg

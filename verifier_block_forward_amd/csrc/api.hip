@@ -76,6 +76,7 @@ struct Plan {
     GemmPlan router, sgi, shg, eg, ed, shd;
     size_t p_router, p_sgi, p_shg, p_shu, p_eg, p_eu, p_ed, p_shd, xs_e, xs_sh;
     size_t moe_n, moe_slot, moe_coef, moe_sscale, moe_sel;
+    size_t head_part;  // fused head: per-workgroup top-2 records
     size_t total;
 };
 
@@ -167,6 +168,7 @@ Plan make_plan(const dbf_config &c, int M, int R) {
         p.moe_sscale = take(16 * f);
         p.moe_sel = take((size_t)16 * c.top_k * sizeof(int32_t));
     }
+    p.head_part = take((size_t)head_blocks(c.vocab) * 16 * sizeof(float4));
     p.total = off;
     return p;
 }
@@ -363,6 +365,24 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         if (!io->ctx) return fail(DBF_EINVAL, "io.ctx (prev_hidden) is null");
     }
     CHECK(validate_weights(c, w, io->tokens != nullptr));
+    int K_acc = 0;
+    if (io->lm_head) {
+        const dbf_tensor &lm = *io->lm_head;
+        CHECK(check_t(lm, "io.lm_head", DBF_BF16, 2, c.vocab, c.hidden));
+        if (!io->argmax) return fail(DBF_EINVAL, "io.argmax is required with io.lm_head");
+    }
+    if (io->target) {
+        if (!io->lm_head) return fail(DBF_EINVAL, "io.target needs io.lm_head (the drafts are its argmaxes)");
+        K_acc = c.kind == DBF_KIND_DFLASH ? M - 1 : 1;
+        if (K_acc < 1) return fail(DBF_EINVAL, "accept walk of a DFlash block needs M >= 2 (M = %d)", M);
+        if (!io->accept_result) return fail(DBF_EINVAL, "io.accept_result is required with io.target");
+        if (io->n_eos < 0 || io->n_eos > 1024 || (io->n_eos > 0 && !io->eos))
+            return fail(DBF_EINVAL, "io eos list invalid (n_eos = %d)", io->n_eos);
+    } else if (io->accept_result || io->committed || io->n_eos) {
+        return fail(DBF_EINVAL, "io.accept_result, io.committed and io.n_eos need io.target");
+    }
+    if (!io->lm_head && (io->argmax || io->top2_margin))
+        return fail(DBF_EINVAL, "io.argmax and io.top2_margin need io.lm_head");
     if (!cache || !cache->k || !cache->v) return fail(DBF_EINVAL, "cache or its buffers are null");
     if (cache->dtype != DBF_F32 && cache->dtype != DBF_BF16)
         return fail(DBF_EDTYPE, "cache dtype %s (F32 or BF16)", dtname(cache->dtype));
@@ -742,9 +762,20 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 a.ncb = ncb;
                 launch_moe_combine(a, st);
             }
-            if (last)
+            if (last && io->lm_head) {
+                // shared head: final norm folded into the lm_head staging, then the
+                // argmax reduction and the accept walk in one workgroup
+                HeadNorm nrm{(const float *)w->final_norm.data, ssp_x, ncb, eps, io->h_final};
+                float4 *part = at<float4>(ws, p.head_part);
+                launch_head((const uint16_t *)io->lm_head->data, io->lm_head->dtype == DBF_BF16_T16, xres,
+                            c.vocab, H, M, nullptr, part, &nrm, st);
+                AcceptArgs acc{io->target, K_acc, c.kind == DBF_KIND_DFLASH ? 1 : 0, io->eos, io->n_eos,
+                               io->accept_result, io->committed};
+                launch_head_finish(part, head_blocks(c.vocab), M, io->argmax, io->top2_margin, acc, st);
+            } else if (last) {
                 launch_final_norm(xres, ssp_x, ncb, M, H, (const float *)w->final_norm.data, eps,
                                   io->h_final, st);
+            }
         }
     }
     CHECK(hip_check("draft_block_forward launch"));
@@ -786,7 +817,7 @@ int head_launch(const float *h, int32_t M, int32_t H, const dbf_tensor *lm_head,
     (void)hipGetLastError();
     float4 *part = (float4 *)ws;
     launch_head((const uint16_t *)lm_head->data, lm_head->dtype == DBF_BF16_T16, h, V, H, M, logits,
-                part, st);
+                part, nullptr, st);
     launch_head_reduce(part, head_blocks(V), M, argmax, top2_margin, st);
     return hip_check("lm_head_argmax launch");
 }

@@ -680,44 +680,7 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t *d, const int32_t *
                                                int32_t *committed) {
     // the arguments into scalar registers in one round trip
     asm volatile("" ::"s"(d), "s"(t), "s"(K), "s"(eos), "s"(n_eos), "s"(res), "s"(committed));
-    const int lane = threadIdx.x;
-    int a = K;
-    for (int base = 0; base < K; base += 64) {
-        const int i = base + lane;
-        const bool mis = i < K && d[i] != t[i];
-        const unsigned long long b = __ballot(mis);
-        if (b) {
-            a = base + __ffsll((long long)b) - 1;
-            break;
-        }
-    }
-    int first_eos = a + 1;
-    if (n_eos > 0) {
-        for (int base = 0; base <= a; base += 64) {
-            const int i = base + lane;
-            bool ise = false;
-            if (i <= a) {
-                const int tok = t[i];
-                for (int e = 0; e < n_eos; e++) ise |= tok == eos[e];
-            }
-            const unsigned long long b = __ballot(ise);
-            if (b) {
-                first_eos = base + __ffsll((long long)b) - 1;
-                break;
-            }
-        }
-    }
-    const bool hit = first_eos <= a;
-    const int n = hit ? first_eos + 1 : a + 1;
-    if (committed)
-        for (int i = lane; i < n; i += 64) committed[i] = t[i];
-    if (lane == 0) {
-        res[0] = a;
-        res[1] = t[a];
-        res[2] = K - a;
-        res[3] = hit ? 1 : 0;
-        res[4] = n;
-    }
+    accept_walk(d, t, K, eos, n_eos, res, committed);
 }
 
 void launch_accept(const int32_t *drafts, const int32_t *target, int K, const int32_t *eos,

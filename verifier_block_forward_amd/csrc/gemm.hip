@@ -607,7 +607,15 @@ constexpr int HEAD_THREADS = 64 * HEAD_WAVES;
 // HEAD_XCH*128 float4
 constexpr int HEAD_XPT = HEAD_XCH * 128 / HEAD_THREADS;
 static_assert(HEAD_XCH * 128 % HEAD_THREADS == 0, "a chunk splits evenly over the threads");
-__device__ __forceinline__ void head_x_load(float4 (&xr)[HEAD_XPT], const float *h, int M, int K, int c) {
+// With the final RMSNorm folded in (PRE), h holds the pre-norm rows x: the load
+// also fetches the norm weight w of the same columns (wr), and head_x_apply then
+// forms x * s_m * w (the row scale s_m from rsc) in the order k_final_norm forms it,
+// so the hidden rows are the same bits; workgroup 0 also writes them out as h_final.
+// The first chunk is loaded before the row scales are formed, so the two round
+// trips overlap.
+template <bool PRE>
+__device__ __forceinline__ void head_x_load(float4 (&xr)[HEAD_XPT], float4 (&wr)[HEAD_XPT], const float *h,
+                                            int M, int K, int c, const HeadNorm &nrm) {
     const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
     const bool rok = r < M;
     const float *row = h + (size_t)(rok ? r : 0) * K;
@@ -616,10 +624,31 @@ __device__ __forceinline__ void head_x_load(float4 (&xr)[HEAD_XPT], const float 
         const int col = c * HEAD_XCH * 32 + 4 * (q + (HEAD_THREADS / 16) * i);
         const bool ok = rok && col < K;  // K % 8 == 0: a float4 is all in or all out
         const float4 v = *(const float4 *)(row + (ok ? col : 0));
+        if constexpr (PRE) wr[i] = *(const float4 *)(nrm.w + (ok ? col : 0));
         xr[i].x = ok ? v.x : 0.f;
         xr[i].y = ok ? v.y : 0.f;
         xr[i].z = ok ? v.z : 0.f;
         xr[i].w = ok ? v.w : 0.f;
+    }
+}
+
+template <bool PRE>
+__device__ __forceinline__ void head_x_apply(float4 (&xr)[HEAD_XPT], const float4 (&wr)[HEAD_XPT], int M, int K,
+                                             int c, const HeadNorm &nrm, const float *rsc) {
+    if constexpr (PRE) {
+        const int r = threadIdx.x & 15, q = threadIdx.x >> 4;
+        const float sc = rsc[r];
+#pragma unroll
+        for (int i = 0; i < HEAD_XPT; i++) {
+            const int col = c * HEAD_XCH * 32 + 4 * (q + (HEAD_THREADS / 16) * i);
+            float4 v = xr[i];
+            v.x = v.x * sc * wr[i].x;
+            v.y = v.y * sc * wr[i].y;
+            v.z = v.z * sc * wr[i].z;
+            v.w = v.w * sc * wr[i].w;
+            xr[i] = v;  // rows >= M and columns >= K stay 0
+            if (r < M && col < K && blockIdx.x == 0) *(float4 *)(nrm.h_out + (size_t)r * K + col) = v;
+        }
     }
 }
 
@@ -645,15 +674,18 @@ __device__ __forceinline__ void head_x_store(uint16_t *buf, const float4 (&xr)[H
     }
 }
 
+template <bool PRE>
 __global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_head(
     const uint16_t *__restrict__ W, int tiled, const float *__restrict__ h, int V, int K, int M,
-    float *__restrict__ logits, float4 *__restrict__ part, int units) {
+    float *__restrict__ logits, float4 *__restrict__ part, int units, HeadNorm nrm) {
     // the arguments into scalar registers in one round trip
-    asm volatile("" ::"s"(W), "s"(tiled), "s"(h), "s"(V), "s"(K), "s"(M), "s"(logits), "s"(part), "s"(units));
+    asm volatile("" ::"s"(W), "s"(tiled), "s"(h), "s"(V), "s"(K), "s"(M), "s"(logits), "s"(part), "s"(units),
+                 "s"(nrm.w), "s"(nrm.ssp), "s"(nrm.ncb), "s"(nrm.eps), "s"(nrm.h_out));
     constexpr int NA = HEAD_NA, PIPE = HEAD_PIPE;
     constexpr int CHE = HEAD_XCH * 2 * 64 * 8;  // elements of one staged chunk
     __shared__ __align__(16) uint16_t xbuf[2][CHE];
     __shared__ Top2 wrec[HEAD_WAVES][16];
+    __shared__ float rsc[16];  // PRE: row scales of the final RMSNorm
     const int lane = threadIdx.x & 63, wv = wave_id();
     const int unit = blockIdx.x * HEAD_WAVES + wv;
     const bool active = unit < units;
@@ -695,10 +727,22 @@ __global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int u = 0; u < PIPE; u++) DBF_HEAD_STAGE(u, u);
     }
-    float4 xr[HEAD_XPT];
-    head_x_load(xr, h, M, K, 0);
+    float4 xr[HEAD_XPT], wr[HEAD_XPT];
+    head_x_load<PRE>(xr, wr, h, M, K, 0, nrm);
+    if constexpr (PRE) {
+        // row scale of the final RMSNorm, from the rows' sum-of-squares partials:
+        // wave w forms rows w and w + HEAD_WAVES (whole waves, as k_final_norm)
+        for (int mm = wv; mm < 16; mm += HEAD_WAVES) {
+            const float *sr = nrm.ssp + (size_t)(mm < M ? mm : 0) * nrm.ncb;
+            const float f = row_scale_first(sr, nrm.ncb);
+            const float sc = row_scale_finish(f, sr, nrm.ncb, K, nrm.eps);
+            if (lane == 0) rsc[mm] = sc;
+        }
+        __syncthreads();
+    }
+    head_x_apply<PRE>(xr, wr, M, K, 0, nrm, rsc);
     head_x_store(xbuf[0], xr);
-    if (nch > 1) head_x_load(xr, h, M, K, 1);
+    if (nch > 1) head_x_load<PRE>(xr, wr, h, M, K, 1, nrm);
     __syncthreads();
     for (int c = 0; c < nch; c++) {
         if (active) {
@@ -722,8 +766,9 @@ __global__ __launch_bounds__(HEAD_THREADS) __attribute__((amdgpu_waves_per_eu(2)
             }
         }
         if (c + 1 < nch) {
+            head_x_apply<PRE>(xr, wr, M, K, c + 1, nrm, rsc);
             head_x_store(xbuf[(c + 1) & 1], xr);
-            if (c + 2 < nch) head_x_load(xr, h, M, K, c + 2);
+            if (c + 2 < nch) head_x_load<PRE>(xr, wr, h, M, K, c + 2, nrm);
         }
         __syncthreads();
     }
@@ -769,10 +814,14 @@ int head_units(int V) { return (V + 16 * HEAD_NA - 1) / (16 * HEAD_NA); }
 int head_blocks(int V) { return (head_units(V) + HEAD_WAVES - 1) / HEAD_WAVES; }
 
 void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M, float *logits,
-                 float4 *part, hipStream_t s) {
+                 float4 *part, const HeadNorm *nrm, hipStream_t s) {
     const int units = head_units(V);
-    launch_k(PROF_HEAD, "k_head", k_head, dim3(head_blocks(V)), dim3(HEAD_THREADS), 0, s, W, tiled, h, V, K, M, logits,
-                       part, units);
+    if (nrm)
+        launch_k(PROF_HEAD, "k_head", k_head<true>, dim3(head_blocks(V)), dim3(HEAD_THREADS), 0, s, W, tiled, h, V,
+                 K, M, logits, part, units, *nrm);
+    else
+        launch_k(PROF_HEAD, "k_head", k_head<false>, dim3(head_blocks(V)), dim3(HEAD_THREADS), 0, s, W, tiled, h,
+                 V, K, M, logits, part, units, HeadNorm{});
 }
 
 // ---------------------------------------------------------------------------
@@ -831,6 +880,45 @@ __global__ __launch_bounds__(256) void k_head_reduce(const float4 *__restrict__ 
         argmax[m] = r.i1;
         if (margin) margin[m] = r.v1 - r.v2;
     }
+}
+
+// One workgroup: wave m folds row m's records (as k_head_reduce, same total order),
+// then wave 0 runs the greedy accept walk of the drafts among those argmaxes
+// against the target's argmaxes (drafts: rows 1..M-1 when draft_row0 is 1, with
+// K = M - 1; row 0 with K = 1 otherwise).
+__global__ __launch_bounds__(1024) void k_head_finish(const float4 *__restrict__ part, int blocks, int M,
+                                                      int32_t *__restrict__ argmax, float *__restrict__ margin,
+                                                      AcceptArgs acc) {
+    // the arguments into scalar registers in one round trip
+    asm volatile("" ::"s"(part), "s"(blocks), "s"(M), "s"(argmax), "s"(margin), "s"(acc.target), "s"(acc.K),
+                 "s"(acc.first), "s"(acc.eos), "s"(acc.n_eos), "s"(acc.result), "s"(acc.committed));
+    __shared__ int32_t am[16];
+    const int lane = threadIdx.x & 63, m = wave_id();
+    if (m < M) {
+        Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+        const float4 *pm = part + (size_t)m * blocks;
+        for (int u = lane; u < blocks; u += 64) {
+            const float4 p = pm[u];
+            Top2 c{p.x, __float_as_int(p.y), p.z};
+            t = merge(t, c);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) t = merge(t, shfl_top2(t, o));
+        if (lane == 0) {
+            argmax[m] = t.i1;
+            am[m] = t.i1;
+            if (margin) margin[m] = t.v1 - t.v2;
+        }
+    }
+    __syncthreads();
+    if (m == 0 && acc.target)
+        accept_walk(am + acc.first, acc.target, acc.K, acc.eos, acc.n_eos, acc.result, acc.committed);
+}
+
+void launch_head_finish(const float4 *part, int blocks, int M, int32_t *argmax, float *margin,
+                        const AcceptArgs &acc, hipStream_t s) {
+    launch_k(PROF_HEAD, "k_head_finish", k_head_finish, dim3(1), dim3(1024), 0, s, part, blocks, M, argmax, margin,
+             acc);
 }
 
 void launch_head_reduce(const float4 *part, int blocks, int M, int32_t *argmax, float *margin,

@@ -154,4 +154,51 @@ __device__ __forceinline__ float sum_partials(const float *p, int ks, int rows, 
     return o[0];
 }
 
+// Greedy accept-prefix walk (hf2q dflash/qwen35_orchestrator.rs, module doc:
+// greedy accept-walk invariant; per-round steps 7-8), run by one whole wavefront:
+// a = length of the longest prefix with d[i] == t[i]; res = {a, t[a], K - a,
+// hit_eos, n_committed}; committed = t[0..a], cut after the first EOS (inclusive).
+// d may point to LDS (generic address).
+__device__ __forceinline__ void accept_walk(const int32_t *d, const int32_t *t, int K, const int32_t *eos,
+                                            int n_eos, int32_t *res, int32_t *committed) {
+    const int lane = threadIdx.x & 63;
+    int a = K;
+    for (int base = 0; base < K; base += 64) {
+        const int i = base + lane;
+        const bool mis = i < K && d[i] != t[i];
+        const unsigned long long b = __ballot(mis);
+        if (b) {
+            a = base + __ffsll((long long)b) - 1;
+            break;
+        }
+    }
+    int first_eos = a + 1;
+    if (n_eos > 0) {
+        for (int base = 0; base <= a; base += 64) {
+            const int i = base + lane;
+            bool ise = false;
+            if (i <= a) {
+                const int tok = t[i];
+                for (int e = 0; e < n_eos; e++) ise |= tok == eos[e];
+            }
+            const unsigned long long b = __ballot(ise);
+            if (b) {
+                first_eos = base + __ffsll((long long)b) - 1;
+                break;
+            }
+        }
+    }
+    const bool hit = first_eos <= a;
+    const int n = hit ? first_eos + 1 : a + 1;
+    if (committed)
+        for (int i = lane; i < n; i += 64) committed[i] = t[i];
+    if (lane == 0) {
+        res[0] = a;
+        res[1] = t[a];
+        res[2] = K - a;
+        res[3] = hit ? 1 : 0;
+        res[4] = n;
+    }
+}
+
 }  // namespace dbf

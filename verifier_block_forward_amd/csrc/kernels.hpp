@@ -106,9 +106,31 @@ void launch_gemm_full(const FullArgs &a, hipStream_t s);
 constexpr int HEAD_NA = 8;  // 16*HEAD_NA vocabulary rows per wave unit
 int head_units(int V);
 int head_blocks(int V);  // workgroups of the head launch (8 wave units each)
-// h: F32 [M][K] hidden rows; part: [16][head_blocks(V)] top-2 records
+// Final RMSNorm folded into the head's staging: h then holds the pre-norm rows x,
+// the head forms x * s_m * w (s_m from the rows' sum-of-squares partials ssp
+// [16][ncb]) and workgroup 0 writes those rows to h_out.
+struct HeadNorm {
+    const float *w;    // final norm weight [K]
+    const float *ssp;  // [16][ncb]
+    int ncb;
+    float eps;
+    float *h_out;      // [M][K]
+};
+// h: F32 [M][K] hidden rows (normed, or pre-norm with nrm); part: [16][head_blocks(V)]
+// top-2 records
 void launch_head(const uint16_t *W, int tiled, const float *h, int V, int K, int M,
-                 float *logits, float4 *part, hipStream_t s);
+                 float *logits, float4 *part, const HeadNorm *nrm, hipStream_t s);
+// greedy accept walk after the argmax reduction (k_head_finish)
+struct AcceptArgs {
+    const int32_t *target;  // [K+1], or null: no walk
+    int K, first;           // drafts are the argmaxes of rows first .. first+K-1
+    const int32_t *eos;
+    int n_eos;
+    int32_t *result;        // [5]
+    int32_t *committed;     // [K+1] or null
+};
+void launch_head_finish(const float4 *part, int blocks, int M, int32_t *argmax, float *margin,
+                        const AcceptArgs &acc, hipStream_t s);
 
 // weight tiling (MFMA operand order, see gemm.hip)
 size_t tiled_elems(long long N, long long K);

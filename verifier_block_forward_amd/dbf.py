@@ -82,7 +82,9 @@ class BlockIO(C.Structure):
                 ("M", C.c_int32), ("R", C.c_int32), ("hidden_out", C.c_void_p),
                 ("h_final", C.c_void_p), ("layer_hidden", C.c_void_p),
                 ("ctx_layers", C.POINTER(C.c_void_p)), ("ctx_ld", C.c_int64), ("ctx_row0", C.c_int64),
-                ("moe_experts", C.c_void_p)]
+                ("moe_experts", C.c_void_p), ("lm_head", C.POINTER(Tensor)), ("argmax", C.c_void_p),
+                ("top2_margin", C.c_void_p), ("target", C.c_void_p), ("eos", C.c_void_p),
+                ("n_eos", C.c_int32), ("accept_result", C.c_void_p), ("committed", C.c_void_p)]
 
 
 _lib.draft_block_forward.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.POINTER(KVCache),
@@ -308,9 +310,13 @@ def make_cache(k, v, seq_len: int) -> KVCache:
 
 
 def make_io(M, R, h_final, tokens=None, x0=None, ctx=None, hidden_out=None,
-            layer_hidden=None, ctx_layers=None, ctx_row0=0, moe_experts=None) -> BlockIO:
+            layer_hidden=None, ctx_layers=None, ctx_row0=0, moe_experts=None, lm_head=None,
+            argmax=None, top2_margin=None, target=None, eos=None, accept_result=None,
+            committed=None) -> BlockIO:
     """ctx_layers: list of n_t device tensors [positions, >= H] F32 (captured target
-    layers); the R context rows are gathered from positions ctx_row0.."""
+    layers); the R context rows are gathered from positions ctx_row0..
+    lm_head (+ argmax, top2_margin) runs the shared head in the same call; target
+    (+ eos, accept_result, committed) also runs the greedy accept walk of the drafts."""
     torch = _torch()
     _need(h_final, "h_final", torch.float32, ndim=2)
     H = h_final.shape[1]
@@ -328,9 +334,21 @@ def make_io(M, R, h_final, tokens=None, x0=None, ctx=None, hidden_out=None,
                 raise ValueError(f"ctx_layers[{i}] must be a device F32 [positions, H] row-major tensor")
             if t.stride(0) != ctx_layers[0].stride(0):
                 raise ValueError("ctx_layers must share one row stride")
+    _need(argmax, "argmax", torch.int32, M, optional=True)
+    _need(top2_margin, "top2_margin", torch.float32, M, optional=True)
+    _need(target, "target", torch.int32, 2, optional=True)
+    _need(eos, "eos", torch.int32, optional=True)
+    _need(accept_result, "accept_result", torch.int32, 5, optional=True)
+    _need(committed, "committed", torch.int32, 2, optional=True)
     io = BlockIO(tokens=_ptr(tokens), x0=_ptr(x0), ctx=_ptr(ctx), M=M, R=R,
                  hidden_out=_ptr(hidden_out), h_final=_ptr(h_final),
-                 layer_hidden=_ptr(layer_hidden), moe_experts=_ptr(moe_experts))
+                 layer_hidden=_ptr(layer_hidden), moe_experts=_ptr(moe_experts),
+                 argmax=_ptr(argmax), top2_margin=_ptr(top2_margin), target=_ptr(target),
+                 eos=_ptr(eos), n_eos=0 if eos is None else eos.numel(),
+                 accept_result=_ptr(accept_result), committed=_ptr(committed))
+    if lm_head is not None:
+        io._lm_head = tensor(lm_head)  # the struct must outlive the call
+        io.lm_head = C.pointer(io._lm_head)
     if ctx_layers is not None:
         arr = (C.c_void_p * len(ctx_layers))(*[t.data_ptr() for t in ctx_layers])
         io._ctx_arr = arr  # the host pointer array must outlive the call
