@@ -325,7 +325,7 @@ def main():
     head_launch_us = per_kernel.get("k_head", [1, 0.0])
     head_us = head_launch_us[1] / max(head_launch_us[0], 1)
     head_gbps = ab["lm_head"] / (head_us * 1e-6) / 1e9 if head_us > 0 else 0.0
-    head_cnt = cnt.get("k_head")
+    head_cnt = cnt.get("k_head<true>" if fused else "k_head<false>")
 
     extra = {}
     if not args.no_extra:
