@@ -589,42 +589,49 @@ void launch_attn(const AttnArgs &a, hipStream_t s) {
 }
 
 // Merge the chunk partials of query (m, h), apply the optional sigmoid gate and
-// write the attention output row into the split tile of the O projection. Thread t
-// takes dim t % hd of the chunks congruent to t / hd modulo 256 / hd; it reads them
-// in batches of CMB_BATCH records with every load of a batch in flight at once and
-// folds each batch into a running (max, sum, acc) state; the chunk groups are then
-// merged through LDS in a fixed order. Rows m >= M and the padding columns are
-// written as zeros.
-constexpr int CMB_BATCH = 16;
-
-__global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
+// write the attention output row into the split tile of the O projection. With NT
+// threads, thread t takes dims 4 (t % (hd/4)) .. +3 (one float4) of the chunks
+// congruent to t / (hd/4) modulo 4 NT / hd; it reads them in batches of B records,
+// every load of a batch in flight at once (a batch past the last chunk re-reads its
+// first record and drops it), and folds each batch into a running (max, sum, acc)
+// state; the chunk groups are then merged through LDS in a fixed order. The host
+// picks NT and B from the chunk count so that a thread issues about as many loads
+// as it has chunks. The grid is M x nq; block (m, h) also writes zeros into the
+// padding rows m + M, m + 2M, ... < SPLIT_ROWS of its columns. (hd is 64, 128 or 256, so the
+// split tile of nq * hd columns has no padding columns.)
+template <int HD, int NT, int B>
+__global__ __launch_bounds__(NT) void k_attn_combine(CombineArgs a) {
     // the arguments into scalar registers in one round trip
     asm volatile("" ::"s"(a.part), "s"(a.n_chunks), "s"(a.M), "s"(a.nq), "s"(a.hd), "s"(a.g), "s"(a.xs));
-    __shared__ float sm_m[256], sm_l[256], sm_o[256];
+    __shared__ float4 sm_o[NT];
+    __shared__ float sm_m[NT], sm_l[NT];
     const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    const int hd = a.hd, K = a.nq * hd, rec = hd + ATT_PART_EXTRA;
-    const int ngrp = 256 / hd;
-    const int d = tid % hd, grp = tid / hd;
-    const bool valid = m < a.M;
-    // the gate value goes out with the partial loads instead of after the merge
-    const float gv = valid && a.g && grp == 0 ? a.g[(size_t)m * K + h * hd + d] : 0.f;
-    float mr = -INFINITY, lr = 0.f, orun = 0.f;
-    if (valid) {
+    constexpr int hd = HD, tpg = HD / 4, ngrp = NT / tpg;  // threads per chunk group, chunk groups
+    const int K = a.nq * hd, rec = hd + ATT_PART_EXTRA;
+    const int d4 = tid % tpg, grp = tid / tpg;
+    // the gate values go out with the partial loads instead of after the merge
+    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.g && grp == 0) gv = *(const float4 *)(a.g + (size_t)m * K + h * hd + 4 * d4);
+    float mr = -INFINITY, lr = 0.f;
+    f32x4 orun = {0.f, 0.f, 0.f, 0.f};
+    {
         const size_t stride = (size_t)a.M * a.nq * rec;
         const float *p = a.part + ((size_t)m * a.nq + h) * rec;
-        for (int c0 = grp; c0 < a.n_chunks; c0 += CMB_BATCH * ngrp) {
-            float mv[CMB_BATCH], lv[CMB_BATCH], ov[CMB_BATCH];
+        for (int c0 = grp; c0 < a.n_chunks; c0 += B * ngrp) {
+            float mv[B], lv[B];
+            f32x4 ov[B];
 #pragma unroll
-            for (int j = 0; j < CMB_BATCH; j++) {
+            for (int j = 0; j < B; j++) {
                 const int cc = c0 + j * ngrp;
                 const float *pc = p + (size_t)(cc < a.n_chunks ? cc : c0) * stride;
                 mv[j] = pc[hd];
                 lv[j] = cc < a.n_chunks ? pc[hd + 1] : 0.f;
-                ov[j] = pc[d];
+                const float4 o4 = *(const float4 *)(pc + 4 * d4);
+                ov[j] = f32x4{o4.x, o4.y, o4.z, o4.w};
             }
             float bm = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < CMB_BATCH; j++)
+            for (int j = 0; j < B; j++)
                 if (lv[j] > 0.f) bm = fmaxf(bm, mv[j]);
             const float mn = fmaxf(mr, bm);
             if (mn != -INFINITY) {
@@ -632,7 +639,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
                 orun *= sc;
                 lr *= sc;
 #pragma unroll
-                for (int j = 0; j < CMB_BATCH; j++) {
+                for (int j = 0; j < B; j++) {
                     const float e = lv[j] > 0.f ? exp2f(mv[j] - mn) : 0.f;
                     orun += ov[j] * e;
                     lr += lv[j] * e;
@@ -643,33 +650,63 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineArgs a) {
     }
     sm_m[tid] = mr;
     sm_l[tid] = lr;
-    sm_o[tid] = orun;
+    sm_o[tid] = make_float4(orun[0], orun[1], orun[2], orun[3]);
     __syncthreads();
     if (grp != 0) return;
-    float o = 0.f;
-    if (valid) {
+    float o[4];
+    {
         float mx = -INFINITY;
+#pragma unroll
         for (int q = 0; q < ngrp; q++)
-            if (sm_l[q * hd + d] > 0.f) mx = fmaxf(mx, sm_m[q * hd + d]);
-        float osum = 0.f, lsum = 0.f;
+            if (sm_l[q * tpg + d4] > 0.f) mx = fmaxf(mx, sm_m[q * tpg + d4]);
+        f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
+#pragma unroll
         for (int q = 0; q < ngrp; q++) {
-            const float lq = sm_l[q * hd + d];
-            const float e = lq > 0.f ? exp2f(sm_m[q * hd + d] - mx) : 0.f;
-            osum += sm_o[q * hd + d] * e;
+            const float lq = sm_l[q * tpg + d4];
+            const float e = lq > 0.f ? exp2f(sm_m[q * tpg + d4] - mx) : 0.f;
+            const float4 oq = sm_o[q * tpg + d4];
+            osum += f32x4{oq.x, oq.y, oq.z, oq.w} * e;
             lsum += lq * e;
         }
-        o = osum / lsum;
-        if (a.g) o *= sigmoidf_(gv);
+        const float gvv[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            o[i] = osum[i] / lsum;
+            if (a.g) o[i] *= sigmoidf_(gvv[i]);
+        }
     }
-    split_store(a.xs, m, h * hd + d, o);
-    if (h == a.nq - 1) {
-        const int Kp = (K + 31) & ~31;
-        for (int k = K + d; k < Kp; k += hd) split_store(a.xs, m, k, 0.f);
-    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) split_store(a.xs, m, h * hd + 4 * d4 + i, o[i]);
+    for (int r = m + a.M; r < SPLIT_ROWS; r += a.M)
+#pragma unroll
+        for (int i = 0; i < 4; i++) split_store(a.xs, r, h * hd + 4 * d4 + i, 0.f);
+}
+
+template <int HD>
+static void launch_combine_hd(const CombineArgs &a, hipStream_t s) {
+    // chunks per thread with 256 threads; past 8 the block takes 1024 threads
+    constexpr int g256 = 1024 / HD, g1024 = 4096 / HD;
+    const int per256 = (a.n_chunks + g256 - 1) / g256;
+    const int per1024 = (a.n_chunks + g1024 - 1) / g1024;
+    const dim3 grid(a.M, a.nq);
+    if (per256 <= 4)
+        launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 256, 4>, grid, dim3(256), 0, s, a);
+    else if (per256 <= 8)
+        launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 256, 8>, grid, dim3(256), 0, s, a);
+    else if (per1024 <= 8)
+        launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 1024, 8>, grid, dim3(1024), 0, s, a);
+    else
+        launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 1024, 16>, grid, dim3(1024), 0, s, a);
 }
 
 void launch_attn_combine(const CombineArgs &a, hipStream_t s) {
-    launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine, dim3(16, a.nq), dim3(256), 0, s, a);
+    if (a.hd == 64)
+        launch_combine_hd<64>(a, s);
+    else if (a.hd == 128)
+        launch_combine_hd<128>(a, s);
+    else
+        launch_combine_hd<256>(a, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -38,6 +38,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+constexpr int SPLIT_ROWS = 16;  // rows of a split tile
+
 // bytes of one split tile for K columns
 __host__ __device__ inline size_t split_tile_bytes(int K) {
     return (size_t)((K + 31) / 32) * 2 * 64 * 8 * sizeof(uint16_t);
