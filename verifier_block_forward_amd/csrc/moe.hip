@@ -21,32 +21,75 @@
 
 namespace dbf {
 
-// (value, index) with ties to the lower index
-__device__ __forceinline__ void better_pair(float &v, int &i, float v2, int i2) {
-    if (v2 > v || (v2 == v && i2 < i)) {
-        v = v2;
-        i = i2;
-    }
+// Selection keys: (value, index) as one 64-bit unsigned integer whose order is the
+// pick order -- the high word maps a float (NaN excluded, -0 folded into +0
+// beforehand) to an unsigned integer of the same order, the low word is ~index so
+// that equal values rank the lower index first. Key 0 is below every expert's key:
+// it marks an expert that is out of range or already picked.
+__device__ __forceinline__ unsigned order_key(float v) {
+    const unsigned u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(unsigned k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ void key_max(unsigned &h, unsigned &l, unsigned h2, unsigned l2) {
+    const unsigned long long a = ((unsigned long long)h << 32) | l;
+    const unsigned long long b = ((unsigned long long)h2 << 32) | l2;
+    const bool t = b > a;
+    h = t ? h2 : h;
+    l = t ? l2 : l;
+}
+
+// one DPP exchange step of the key maximum; lanes in rows ROWMASK leaves out keep
+// their own key
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void dpp_key_step(unsigned &h, unsigned &l) {
+    const unsigned h2 = __builtin_amdgcn_update_dpp(h, h, CTRL, ROWMASK, 0xF, false);
+    const unsigned l2 = __builtin_amdgcn_update_dpp(l, l, CTRL, ROWMASK, 0xF, false);
+    key_max(h, l, h2, l2);
+}
+
+// maximum key over the wave, returned in scalar registers: within each row of 16
+// lanes (lane xor 1, xor 2, then rotations by 4 and 8 leave the row maximum in
+// every lane of the row), then row 1 takes row 0's and row 3 row 2's (row_bcast
+// 15), then row 3 takes row 1's (row_bcast 31): lane 63 holds the maximum.
+__device__ __forceinline__ void wave_key_max(unsigned &h, unsigned &l) {
+    dpp_key_step<0xB1, 0xF>(h, l);   // quad_perm [1, 0, 3, 2]
+    dpp_key_step<0x4E, 0xF>(h, l);   // quad_perm [2, 3, 0, 1]
+    dpp_key_step<0x124, 0xF>(h, l);  // row_ror 4
+    dpp_key_step<0x128, 0xF>(h, l);  // row_ror 8
+    dpp_key_step<0x142, 0xA>(h, l);  // row_bcast 15 into rows 1 and 3
+    dpp_key_step<0x143, 0xC>(h, l);  // row_bcast 31 into rows 2 and 3
+    h = __builtin_amdgcn_readlane(h, 63);
+    l = __builtin_amdgcn_readlane(l, 63);
 }
 
 // Routing in one block of 1024 threads. Rows go in passes of up to 16 (and
 // rows * E <= ROUTE_Z logits): every thread sums the router partials of its
-// (row, expert) entries into LDS, then wave w picks the top_k of the pass's row w
-// with cross-lane shuffles only, one pick per round and no block barrier between
-// picks. The touched experts are compacted in ascending order with a ballot
-// prefix, and each (slot, row) coefficient is written exactly once. A NaN logit
-// ranks as -inf, so every pick is an in-range expert.
+// (row, expert) entries into LDS (the first pass also sums each row's shared-expert
+// gate logit, so those loads go out in the same round trip), then wave w picks the
+// top_k of the pass's row w with no block barrier between picks: lane l holds the
+// selection keys of experts l, l + 64, ... and its best one not yet picked; a pick
+// is the wave-wide maximum of those, after which the picked key is cleared and the
+// lanes rescan their (at most 16) keys. The touched experts are compacted in ascending order with a
+// ballot prefix, and each (slot, row) coefficient is written exactly once. A NaN
+// logit ranks as -inf, so every pick is an in-range expert.
 constexpr int ROUTE_THREADS = 1024;         // one thread per expert at E = 1024
 constexpr int ROUTE_WAVES = ROUTE_THREADS / 64;
 constexpr int ROUTE_Z = 8192;               // router logits held in LDS per pass
-constexpr int ROUTE_EPL = 1024 / 64;        // experts per lane at E = 1024
 
+// EPL: experts per lane, a power of two >= E / 64 (at most 16 at E = 1024)
+template <int EPL>
 __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
     // the arguments into scalar registers in one round trip
     asm volatile("" ::"s"(a.p_router), "s"(a.ks_router), "s"(a.p_sgi), "s"(a.ks_sgi), "s"(a.ssp), "s"(a.ncb),
                  "s"(a.H), "s"(a.eps), "s"(a.M), "s"(a.E), "s"(a.top_k), "s"(a.max_slots), "s"(a.nslots),
                  "s"(a.slot_expert), "s"(a.coef), "s"(a.shared_scale), "s"(a.sel));
     __shared__ float z[ROUTE_Z];            // unscaled router sums, [pass row][E]
+    __shared__ float gz[16];                // unscaled shared-expert gate sums
     __shared__ float rscale[16];
     __shared__ unsigned char used[1024];
     __shared__ int esel[16 * DBF_MAX_TOPK_DEV];
@@ -56,68 +99,103 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int E = a.E, K = a.top_k, M = a.M;
     const int rg = ROUTE_Z / E < ROUTE_WAVES ? ROUTE_Z / E : ROUTE_WAVES;  // >= 8
+    const int ks_max = a.ks_router > a.ks_sgi ? a.ks_router : a.ks_sgi;
     for (int e = tid; e < E; e += ROUTE_THREADS) used[e] = 0;
-    // row scale and shared-expert gate, one wave per row: the norm partials and the
-    // gate's split-K partials load together; the scale is finished after the first
-    // pass's router sums (rows <= 16 = ROUTE_WAVES, so one wave per row)
+    // row scale, one wave per row (rows <= 16 = ROUTE_WAVES): the first 128 norm
+    // partials load with the router partials; the scale is finished after them
     const float *sr = a.ssp + (size_t)(wv < M ? wv : 0) * a.ncb;
-    float f = 0.f, gsum = 0.f;
+    float f0 = 0.f, f1 = 0.f;  // added only after the router sums: no wait before them
     if (wv < M) {
-        f = row_scale_first(sr, a.ncb);
-        gsum = sum_partials(a.p_sgi, a.ks_sgi, 16, 1, wv, 0);
+        f0 = lane < a.ncb ? sr[lane] : 0.f;
+        f1 = lane + 64 < a.ncb ? sr[lane + 64] : 0.f;
     }
     for (int m0 = 0; m0 < M; m0 += rg) {
         const int rows = M - m0 < rg ? M - m0 : rg;
-        for (int i = tid; i < rows * E; i += ROUTE_THREADS) {
-            const int r = i / E;
-            z[i] = sum_partials(a.p_router, a.ks_router, 16, E, m0 + r, i - r * E);
+        const int nz = rows * E, nall = nz + (m0 == 0 ? M : 0);
+        for (int i = tid; i < nall; i += ROUTE_THREADS) {
+            const float *b[1];
+            int ks;
+            size_t stride;
+            float *dst;
+            if (i < nz) {
+                const int r = i / E;
+                b[0] = a.p_router + (size_t)(m0 + r) * E + (i - r * E);
+                ks = a.ks_router;
+                stride = (size_t)16 * E;
+                dst = &z[i];
+            } else {
+                b[0] = a.p_sgi + (i - nz);
+                ks = a.ks_sgi;
+                stride = 16;
+                dst = &gz[i - nz];
+            }
+            float o[1];
+            if (ks_max > PARTIAL_BATCH)
+                sum_partials_n<1, 24>(b, ks, stride, o);
+            else
+                sum_partials_n<1>(b, ks, stride, o);
+            *dst = o[0];
         }
+        __syncthreads();
         if (m0 == 0 && wv < M) {
-            const float s = row_scale_finish(f, sr, a.ncb, a.H, a.eps);
+            asm volatile("" : "+v"(f0));  // keeps the add (and its wait) from being hoisted
+            float s = f0 + f1;
+            for (int i = lane + 128; i < a.ncb; i += 64) s += sr[i];
+            s = wave_sum(s);
+            s = 1.0f / sqrtf(s / (float)a.H + a.eps);
             if (lane == 0) {
                 rscale[wv] = s;
-                a.shared_scale[wv] = sigmoidf_(s * gsum);
+                a.shared_scale[wv] = sigmoidf_(s * gz[wv]);
             }
         }
         __syncthreads();
         if (wv < rows) {
             const int m = m0 + wv;
             const float s = rscale[m];
-            float zr[ROUTE_EPL];
-            unsigned taken = 0;  // bit j: expert lane + 64 j is out of range or already picked
+            unsigned kh[EPL], kl[EPL];  // keys of experts lane + 64 j
 #pragma unroll
-            for (int j = 0; j < ROUTE_EPL; j++) {
+            for (int j = 0; j < EPL; j++) {
                 const int e = lane + 64 * j;
-                float v = e < E ? s * z[wv * E + e] : 0.f;
-                zr[j] = v != v ? -INFINITY : v;
-                if (e >= E) taken |= 1u << j;
+                // the read is clamped into the row, not branched around
+                float v = s * z[wv * E + (e < E ? e : E - 1)] + 0.f;  // + 0 folds -0 into +0
+                v = v != v ? -INFINITY : v;
+                kh[j] = e < E ? order_key(v) : 0u;
+                kl[j] = e < E ? ~(unsigned)e : 0u;
             }
+            unsigned bh = 0u, bl = 0u;  // this lane's best key
+#pragma unroll
+            for (int j = 0; j < EPL; j++) key_max(bh, bl, kh[j], kl[j]);
             float myv = 0.f;  // lane t keeps pick t
             int myi = 0;
             for (int t = 0; t < K; t++) {
-                float bv = -INFINITY;
-                int bi = 0x7fffffff;
-#pragma unroll
-                for (int j = 0; j < ROUTE_EPL; j++)
-                    if (!((taken >> j) & 1u)) better_pair(bv, bi, zr[j], lane + 64 * j);
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) {
-                    const float v2 = __shfl_xor(bv, o, 64);
-                    const int i2 = __shfl_xor(bi, o, 64);
-                    better_pair(bv, bi, v2, i2);
-                }
-                // all lanes agree on (bv, bi); bi < E because K <= E untaken entries existed
-                if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+                unsigned h = bh, l = bl;
+                wave_key_max(h, l);
+                // K <= E real keys existed, so the maximum is a real, untaken expert;
+                // the clamp only keeps an index in range whatever the keys hold
+                int e = (int)~l;
+                e = e < 0 ? 0 : (e >= E ? E - 1 : e);
                 if (lane == t) {
-                    myv = bv;
-                    myi = bi;
+                    myv = key_value(h);
+                    myi = e;
+                }
+                if (t + 1 < K) {
+                    // the low word names the expert: clear its key and rescan
+                    bh = 0u;
+                    bl = 0u;
+#pragma unroll
+                    for (int j = 0; j < EPL; j++) {
+                        const bool hit = kl[j] == l;
+                        kh[j] = hit ? 0u : kh[j];
+                        kl[j] = hit ? 0u : kl[j];
+                        key_max(bh, bl, kh[j], kl[j]);
+                    }
                 }
             }
             // renormalised top-k weights: softmax over the kept logits, summed in pick order
-            const float zmax = __shfl(myv, 0, 64);
+            const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myv), 0));
             const float ex = lane < K ? expf(myv - zmax) : 0.f;
             float den = 0.f;
-            for (int t = 0; t < K; t++) den += __shfl(ex, t, 64);
+            for (int t = 0; t < K; t++) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), t));
             if (lane < K) {
                 esel[m * DBF_MAX_TOPK_DEV + lane] = myi;
                 wsel[m * DBF_MAX_TOPK_DEV + lane] = ex / den;
@@ -164,7 +242,17 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_moe_route(MoeRouteArgs a) {
 }
 
 void launch_moe_route(const MoeRouteArgs &a, hipStream_t s) {
-    launch_k(PROF_ROWS, "k_moe_route", k_moe_route, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
+    const int epl = (a.E + 63) / 64;  // E <= 1024
+    if (epl <= 1)
+        launch_k(PROF_ROWS, "k_moe_route", k_moe_route<1>, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
+    else if (epl <= 2)
+        launch_k(PROF_ROWS, "k_moe_route", k_moe_route<2>, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
+    else if (epl <= 4)
+        launch_k(PROF_ROWS, "k_moe_route", k_moe_route<4>, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
+    else if (epl <= 8)
+        launch_k(PROF_ROWS, "k_moe_route", k_moe_route<8>, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
+    else
+        launch_k(PROF_ROWS, "k_moe_route", k_moe_route<16>, dim3(1), dim3(ROUTE_THREADS), 0, s, a);
 }
 
 // Expert (and shared-expert) SwiGLU: h = silu(s_m * sum P_gate) * (s_m * sum P_up),
