@@ -174,12 +174,14 @@ Plan make_plan(const dbf_config &c, int M, int R) {
 }
 
 // One projection launch: segments planned with the same na and lds (the first
-// segment's plan fixes the kernel).
+// segment's plan fixes the kernel). rows: activation rows that hold data (M block
+// rows, or R context rows), the default for every split tile added.
 struct SegList {
     GemmArgs a{};
-    int nbmax = 1, na = GEMM_NA;
+    int nbmax = 1, na = GEMM_NA, rows;
+    explicit SegList(int rows_) : rows(rows_) {}
     void add(const dbf_tensor &t, int N, int K, const GemmPlan &pl, float *out, const uint16_t *xs0,
-             const uint16_t *xs1 = nullptr) {
+             const uint16_t *xs1 = nullptr, int rows0 = 0, int rows1 = 0) {
         if (a.nseg == 0) {
             na = pl.na;
             a.lds_x = pl.lds;
@@ -196,6 +198,8 @@ struct SegList {
         s.ksplit = pl.ksplit;
         s.kslice_steps = pl.kslice_steps;
         s.tiles = pl.tiles;
+        s.mrows[0] = rows0 > 0 ? rows0 : rows;
+        s.mrows[1] = rows1 > 0 ? rows1 : rows;
         s.unit_begin = a.total_units;
         a.total_units += plan_units(pl);
         if (s.nb > nbmax) nbmax = s.nb;
@@ -456,7 +460,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             }
             t.xs = xs_T;
             launch_colsum2(a, t, st);
-            SegList sl;
+            SegList sl(R);
             sl.add(w->fc, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
             sl.launch(st);
             ColArgs h = col();
@@ -490,7 +494,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         h.xs = xs_h;
         h.ssp_out = ssp_h;
         launch_colsum2(e, h, st);  // embed_t and prev_hidden rows in one launch
-        SegList sl;
+        SegList sl(M);
         sl.add(w->eh_embed, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
         sl.add(w->eh_hidden, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
         sl.launch(st);
@@ -533,11 +537,11 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         float *pq = at<float>(ws, p.p_q), *pk = at<float>(ws, p.p_k), *pv = at<float>(ws, p.p_v);
         float *pg = at<float>(ws, p.p_g);
         {
-            SegList sl;
+            SegList sl(M);
             sl.add(L.wq, qt, H, p.q, pq, xs_blk);
             if (R > 0) {
-                sl.add(L.wk, kt, H, p.k, pk, xs_hctx, xs_blk);
-                sl.add(L.wv, kt, H, p.v, pv, xs_hctx, xs_blk);
+                sl.add(L.wk, kt, H, p.k, pk, xs_hctx, xs_blk, R, M);
+                sl.add(L.wv, kt, H, p.v, pv, xs_hctx, xs_blk, R, M);
             } else {
                 sl.add(L.wk, kt, H, p.k, pk, xs_blk);
                 sl.add(L.wv, kt, H, p.v, pv, xs_blk);
@@ -628,7 +632,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         }
         if (c.ffn_kind == DBF_FFN_DENSE) {
             {
-                SegList sl;
+                SegList sl(M);
                 sl.add(L.ffn_gate, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
                 sl.add(L.ffn_up, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
                 sl.launch(st);
@@ -645,7 +649,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 sa.I = p.I;
                 sa.xs = xs_ff;
                 launch_swiglu(sa, st);
-                SegList sd;
+                SegList sd(M);
                 sd.add(L.ffn_down, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
                 sd.launch(st);
             }
@@ -655,7 +659,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             int32_t *nsl = at<int32_t>(ws, p.moe_n), *slot_e = at<int32_t>(ws, p.moe_slot);
             float *coef = at<float>(ws, p.moe_coef), *sscale = at<float>(ws, p.moe_sscale);
             {
-                SegList sl;
+                SegList sl(M);
                 sl.add(L.router, E, H, p.router, at<float>(ws, p.p_router), xs_blk);
                 sl.add(L.sh_gate_inp, 1, H, p.sgi, at<float>(ws, p.p_sgi), xs_blk);
                 sl.add(L.sh_gate, Is, H, p.shg, at<float>(ws, p.p_shg), xs_blk);
@@ -685,7 +689,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 launch_moe_route(ra, st);
             }
             {
-                SegList sl;
+                SegList sl(M);
                 sl.add_grouped(L.exp_gate, Ie, H, p.eg, at<float>(ws, p.p_eg), xs_blk, 0, p.max_slots,
                                slot_e, nsl);
                 sl.add_grouped(L.exp_up, Ie, H, p.eg, at<float>(ws, p.p_eu), xs_blk, 0, p.max_slots,
@@ -714,7 +718,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 launch_moe_swiglu(sa, st);
             }
             {
-                SegList sl;
+                SegList sl(M);
                 sl.add_grouped(L.exp_down, H, Ie, p.ed, at<float>(ws, p.p_ed), at<uint16_t>(ws, p.xs_e),
                                (long long)(split_tile_bytes(Ie) / 2), p.max_slots, slot_e, nsl);
                 sl.add(L.sh_down, H, Is, p.shd, at<float>(ws, p.p_shd), at<uint16_t>(ws, p.xs_sh));

@@ -56,6 +56,34 @@ __device__ __forceinline__ int xcd_logical(int b, int n) {
 
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16((a), (b), (c), 0, 0, 0)
 
+// Write a wave's NA x NB accumulator tiles into a [rows][N] F32 partial: lane l
+// holds output columns row0 + 16 a + 4 (l / 16) + 0..3 of activation row l % 16 of
+// split tile b, stored as one float4 (N % 4 == 0; scalar stores at a ragged edge).
+// Rows at or past mr0 (tile 0) / mr1 (tile 1) hold no activation and are skipped:
+// with few rows most of the partial's bytes are never written.
+template <int NA, int NB>
+__device__ __forceinline__ void store_partials(float *out, int N, int nb, int row0, int lane, int mr0,
+                                               int mr1, const f32x4 (&acc)[NA][NB]) {
+    const int r = lane & 15, g = lane >> 4;
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        if (b >= nb || r >= (b == 0 ? mr0 : mr1)) continue;
+        float *orow = out + (size_t)(16 * b + r) * N;
+#pragma unroll
+        for (int a = 0; a < NA; a++) {
+            const int o = row0 + 16 * a + 4 * g;
+            if (vec && o + 3 < N) {
+                *(f32x4 *)(orow + o) = acc[a][b];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    if (o + j < N) orow[o + j] = acc[a][b][j];
+            }
+        }
+    }
+}
+
 // Accumulate the NA x NB tile product over k-steps [s0, s1), software-pipelined:
 // a ring of PIPE register stages holds the loads of k-steps s+1..s+PIPE while
 // step s feeds the matrix cores, so every wave keeps PIPE*(NA + 2*NB) 16-byte
@@ -151,7 +179,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     }
     const int tile = local % sg.tiles;
     const int ks = local / sg.tiles;
-    const int N = sg.N, K = sg.K;
+    const int N = sg.N, K = sg.K, mr0 = sg.mrows[0], mr1 = sg.mrows[1];
     const int S = (K + 31) >> 5;
     const int s0 = ks * sg.kslice_steps;
     int s1 = s0 + sg.kslice_steps;
@@ -197,19 +225,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     }
 
     const int nb = NB == 1 ? 1 : sg.nb;
-    float *out = outb + (size_t)ks * 16 * nb * N;
-#pragma unroll
-    for (int a = 0; a < NA; a++)
-#pragma unroll
-        for (int b = 0; b < NB; b++) {
-            if (b >= nb) continue;
-            const int m = 16 * b + r;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int o = row0 + 16 * a + 4 * g + j;
-                if (o < N) out[(size_t)m * N + o] = acc[a][b][j];
-            }
-        }
+    store_partials<NA, NB>(outb + (size_t)ks * 16 * nb * N, N, nb, row0, lane, mr0, mr1, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     }
     const int grp = local % groups, ks = local / groups;
     const int tile = grp * 4 + wv;
-    const int N = sg.N, K = sg.K;
+    const int N = sg.N, K = sg.K, mr0 = sg.mrows[0], mr1 = sg.mrows[1];
     const int S = (K + 31) >> 5;
     const int s0 = ks * sg.kslice_steps;
     int s1 = s0 + sg.kslice_steps;
@@ -356,19 +372,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
         }
     }
 #undef DBF_LOAD_W
-    float *out = outb + (size_t)ks * 16 * nb * N;
-#pragma unroll
-    for (int a = 0; a < NA; a++)
-#pragma unroll
-        for (int b = 0; b < NB; b++) {
-            if (b >= nb) continue;
-            const int m = 16 * b + r;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int o = row0 + 16 * a + 4 * g + j;
-                if (o < N) out[(size_t)m * N + o] = acc[a][b][j];
-            }
-        }
+    store_partials<NA, NB>(outb + (size_t)ks * 16 * nb * N, N, nb, row0, lane, mr0, mr1, acc);
 }
 
 // ---------------------------------------------------------------------------

@@ -46,7 +46,11 @@ struct GemmSeg {
     const int32_t *slot_expert;
     const int32_t *nslots;
     long long w_stride, xs_stride, out_stride;
-    int slots, pad_;
+    int slots;
+    // activation rows that hold data in xs0 / xs1: partial rows at or past them are
+    // not written (consumers read rows below them only)
+    int mrows[2];
+    int pad_;
 };
 
 struct GemmArgs {
