@@ -232,15 +232,18 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
 // Variant with the activation slice staged in LDS: the four waves of a workgroup
 // share (segment, k-slice) and own consecutive row tiles, so the slice's split
 // activations are read once per workgroup (not once per wave) and each wave's
-// registers hold only weights, in a ring of LPIPE stages. A launch of these
-// kernels asks for tens of MB at once; the ring is kept short (2 stages measured
-// best in the c1 step, against 1, 3 and 4) because more requests in flight only
-// lengthen the queue that the activation loads, which gate the first product,
-// wait in.
+// registers hold only weights, in a ring of LP stages. A launch of these kernels
+// asks for tens of MB at once; for long slices the ring is kept short (2 stages
+// measured best on the 18-20-step slices, against 1, 3, 4 and 6) because more
+// requests in flight only lengthen the queue that the activation loads, which gate
+// the first product, wait in. Slices of at most LPIPE_SHORT_MAX steps take a ring
+// of LPIPE_SHORT stages. Ring loads past the slice end are not issued.
 constexpr int LPIPE = 2;
+constexpr int LPIPE_SHORT = 6;
+constexpr int LPIPE_SHORT_MAX = 10;
 constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
 
-template <int NA, int NB>
+template <int NA, int NB, int LP>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     extern __shared__ __align__(16) uint4 xl[];  // NB * kslice_steps * 2 KiB (<= LDS_X_BYTES)
     const int lane = threadIdx.x & 63, wv = wave_id();
@@ -305,17 +308,20 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
 #pragma unroll
         for (int b = 0; b < NB; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8 wb[LPIPE][NA];
+    bf16x8 wb[LP][NA];
     const bool tiled = sg.tiled;
     // Loads only: columns past K (row-major weights) re-read column 0 here and are
     // zeroed where the stage is consumed. A select right after the load made the
-    // compiler wait for every load in flight at the end of each ring pass.
+    // compiler wait for every load in flight at the end of each ring pass. Steps
+    // past the slice are skipped by a wave-uniform branch.
 #define DBF_LOAD_W(u, step)                                                     \
     do {                                                                        \
-        const int sc_ = (step) < s1 ? (step) : s1 - 1;                          \
-        const bool in_ = tiled || 32 * sc_ + 8 * g < K;                         \
-        const int col_ = in_ ? wstep * sc_ : 0;                                 \
-        _Pragma("unroll") for (int a = 0; a < NA; a++) wb[u][a] = ldw16(wrow[a] + col_); \
+        const int sc_ = (step);                                                 \
+        if (sc_ < s1) {                                                         \
+            const bool in_ = tiled || 32 * sc_ + 8 * g < K;                     \
+            const int col_ = in_ ? wstep * sc_ : 0;                             \
+            _Pragma("unroll") for (int a = 0; a < NA; a++) wb[u][a] = ldw16(wrow[a] + col_); \
+        }                                                                       \
     } while (0)
     // Stage the activation slice (per tile, steps [s0, s1) are contiguous, 2 KiB each):
     // this thread's share is loaded first, the weight ring is issued behind it, and
@@ -331,14 +337,16 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
         const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
 #pragma unroll
         for (int q = 0; q < XPT; q++) {
-            const int i = threadIdx.x + 256 * q;
-            const int ic = i < xtot ? i : xtot - 1;  // always a valid address
-            const uint4 *sp = ic < per ? src0 + ic : src1 + (ic - per);  // pointer select
-            xr[q] = *(const u32x4 *)sp;
+            if (256 * q < xtot) {  // uniform: rounds wholly past the slice are skipped
+                const int i = threadIdx.x + 256 * q;
+                const int ic = i < xtot ? i : xtot - 1;  // always a valid address
+                const uint4 *sp = ic < per ? src0 + ic : src1 + (ic - per);  // pointer select
+                xr[q] = *(const u32x4 *)sp;
+            }
         }
     }
 #pragma unroll
-    for (int u = 0; u < LPIPE; u++) DBF_LOAD_W(u, s0 + u);
+    for (int u = 0; u < LP; u++) DBF_LOAD_W(u, s0 + u);
 #pragma unroll
     for (int q = 0; q < XPT; q++) {
         const int i = threadIdx.x + 256 * q;
@@ -347,9 +355,9 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     __syncthreads();
     if (tile >= sg.tiles) return;
 
-    for (int base = 0; base < n; base += LPIPE) {
+    for (int base = 0; base < n; base += LP) {
 #pragma unroll
-        for (int u = 0; u < LPIPE; u++) {
+        for (int u = 0; u < LP; u++) {
             const int j = base + u;
             if (j < n) {
                 const bool in_ = tiled || 32 * (s0 + j) + 8 * g < K;
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
                     }
                 }
             }
-            DBF_LOAD_W(u, s0 + base + u + LPIPE);
+            DBF_LOAD_W(u, s0 + base + u + LP);
         }
     }
 #undef DBF_LOAD_W
@@ -519,7 +527,13 @@ static void go(const GemmArgs &a, hipStream_t s) {
             const size_t b = (size_t)(NB > 1 ? a.seg[i].nb : 1) * a.seg[i].kslice_steps * 2048;
             if (b > lds) lds = b;
         }
-        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB>), dim3(a.total_units), dim3(256), lds, s, a);
+        int steps = 0;
+        for (int i = 0; i < a.nseg; i++)
+            if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
+        if (steps <= LPIPE_SHORT_MAX)
+            launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB, LPIPE_SHORT>), dim3(a.total_units), dim3(256), lds, s, a);
+        else
+            launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB, LPIPE>), dim3(a.total_units), dim3(256), lds, s, a);
     } else {
         const int blocks = (a.total_units + 3) / 4;
         int steps = 0;
