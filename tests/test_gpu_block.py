@@ -58,6 +58,24 @@ def test_block_small(orc, cfg):
     run_case(orc, cfg)
 
 
+# The chunk merge picks its block size and batch from the chunk count, and the chunk
+# count follows the context length (one query group per kv head, 256 chunks at most).
+# These contexts put each head dim into the ranges the other tests do not reach:
+# 128-dim heads with 33-64 and 65-256 chunks, 256-dim heads with 17-32 chunks.
+@pytest.mark.parametrize("cfg", [
+    small(name="combine_hd128_63chunks", hidden=264, n_q_heads=2, n_kv_heads=1, head_dim=128,
+          M=7, R=9, C=4000, n_layers=1),
+    small(name="combine_hd128_125chunks", hidden=264, n_q_heads=2, n_kv_heads=1, head_dim=128,
+          M=7, R=9, C=8000, n_layers=1),
+    small(name="combine_hd256_24chunks", hidden=256, n_q_heads=6, n_kv_heads=1, head_dim=256,
+          M=3, R=2, rotary_dim=64, C=1500, n_layers=1),
+    small(name="combine_mtp_hd256_gate", kind="mtp", R=0, M=1, has_attn_gate=True, n_layers=1,
+          n_target_hidden=0, hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=256, C=3000),
+], ids=lambda c: c.name)
+def test_block_combine_chunk_counts(orc, cfg):
+    run_case(orc, cfg)
+
+
 def test_block_c0(orc):
     run_case(orc, configs.C0)
 
@@ -231,6 +249,10 @@ def run_moe_case(orc, cfg, tiled=False):
     # E not a multiple of the wavefront; the largest E with M = 16 routes in two row passes
     small_moe(name="moe_e100", n_experts=100, top_k=5, M=7, seed=32),
     small_moe(name="moe_e1024_m16", n_experts=1024, top_k=16, M=16, C=40, seed=32),
+    # 8 experts per lane in the routing (257-512 experts)
+    small_moe(name="moe_e500", n_experts=500, top_k=8, M=5, seed=33),
+    # a router width that is not a multiple of 4: the partial stores' scalar edge
+    small_moe(name="moe_e101", n_experts=101, top_k=6, M=4, seed=34),
 ], ids=lambda c: c.name)
 def test_block_moe_small(orc, cfg):
     run_moe_case(orc, cfg)
