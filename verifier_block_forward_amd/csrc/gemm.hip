@@ -88,12 +88,15 @@ __device__ __forceinline__ void store_partials(float *out, int N, int nb, int ro
 // a ring of PIPE register stages holds the loads of k-steps s+1..s+PIPE while
 // step s feeds the matrix cores, so every wave keeps PIPE*(NA + 2*NB) 16-byte
 // loads in flight. Stages past s1 (or columns past K) re-read a valid address and
-// are zeroed or ignored, so the loop has no control flow around its loads.
+// are zeroed or ignored, so the loop has no control flow around its loads. Lanes
+// whose activation row r = lane % 16 holds no data (r >= mr[b]) take zeros
+// instead of loading: the matrix cores' output columns are independent, so those
+// rows' products, which nobody stores, are all that changes.
 template <int NA, int NB, int PIPE>
 __device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], int wstep,
-                                                bool tiled, const uint16_t *const xs[NB], int K,
-                                                int s0, int s1, int lane, f32x4 acc[NA][NB]) {
-    const int g = lane >> 4;
+                                                bool tiled, const uint16_t *const xs[NB], const int mr[NB],
+                                                int K, int s0, int s1, int lane, f32x4 acc[NA][NB]) {
+    const int g = lane >> 4, r16 = lane & 15;
     bf16x8 wb[PIPE][NA], xh[PIPE][NB], xl[PIPE][NB];
     const int n = s1 - s0;
 #define DBF_LOAD_STAGE(u, step)                                                 \
@@ -107,8 +110,13 @@ __device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], 
         }                                                                       \
         _Pragma("unroll") for (int b = 0; b < NB; b++) {                        \
             const uint16_t *x_ = xs[b] + ((size_t)sc_ * 2 * 64 + lane) * 8;     \
-            xh[u][b] = ld16(x_);                                                \
-            xl[u][b] = ld16(x_ + 64 * 8);                                       \
+            if (r16 < mr[b]) {                                                  \
+                xh[u][b] = ld16(x_);                                            \
+                xl[u][b] = ld16(x_ + 64 * 8);                                   \
+            } else {                                                            \
+                xh[u][b] = zero8();                                             \
+                xl[u][b] = zero8();                                             \
+            }                                                                   \
         }                                                                       \
     } while (0)
 #pragma unroll
@@ -217,11 +225,15 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
         f32x4 acc1[NA][1];
 #pragma unroll
         for (int a = 0; a < NA; a++) acc1[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs1, K, s0, s1, lane, acc1);
+        const int mrs1[1] = {mr0};
+        skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs1, mrs1, K, s0, s1, lane, acc1);
 #pragma unroll
         for (int a = 0; a < NA; a++) acc[a][0] = acc1[a][0];
     } else {
-        skinny_mainloop<NA, NB, PIPE>(wrow, wstep, sg.tiled, xs, K, s0, s1, lane, acc);
+        int mrs[NB];
+        mrs[0] = mr0;
+        if (NB > 1) mrs[NB - 1] = mr1;
+        skinny_mainloop<NA, NB, PIPE>(wrow, wstep, sg.tiled, xs, mrs, K, s0, s1, lane, acc);
     }
 
     const int nb = NB == 1 ? 1 : sg.nb;
@@ -335,13 +347,20 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     {
         const uint4 *src0 = (const uint4 *)(xsb0 + (size_t)s0 * 2 * 64 * 8);
         const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
+        // element i of a split tile belongs to activation row i % 16 (= threadIdx.x % 16
+        // here); rows that hold no data are staged as zeros without a load
+        const int xrow = threadIdx.x & 15;
 #pragma unroll
         for (int q = 0; q < XPT; q++) {
             if (256 * q < xtot) {  // uniform: rounds wholly past the slice are skipped
                 const int i = threadIdx.x + 256 * q;
                 const int ic = i < xtot ? i : xtot - 1;  // always a valid address
-                const uint4 *sp = ic < per ? src0 + ic : src1 + (ic - per);  // pointer select
-                xr[q] = *(const u32x4 *)sp;
+                const bool t0 = ic < per;
+                const uint4 *sp = t0 ? src0 + ic : src1 + (ic - per);  // pointer select
+                if (xrow < (t0 ? mr0 : mr1))
+                    xr[q] = *(const u32x4 *)sp;
+                else
+                    xr[q] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     }
@@ -440,7 +459,8 @@ __global__ __launch_bounds__(64 * FULL_W) void k_gemm_full(FullArgs a) {
     const int s0 = (S * wv) / FULL_W, s1 = (S * (wv + 1)) / FULL_W;
     if (s1 > s0) {
         const uint16_t *xs[1] = {a.xs};
-        skinny_mainloop<NT, 1, GEMM_PIPE>(wrow, wstep, a.tiled != 0, xs, K, s0, s1, lane, acc);
+        const int mrs[1] = {a.M};
+        skinny_mainloop<NT, 1, GEMM_PIPE>(wrow, wstep, a.tiled != 0, xs, mrs, K, s0, s1, lane, acc);
     }
 #pragma unroll
     for (int t = 0; t < NT; t++)
