@@ -111,3 +111,65 @@ def test_graph_replay_of_the_sampled_round():
         t.cuda.synchronize()
         for i, (got, want) in enumerate(zip(outs, ref)):
             assert t.equal(got, want), f"replay {rep}, output {i} differs from the eager call"
+
+
+@pytest.mark.parametrize("name", ["c0", "c4m4"])
+def test_graph_replay_of_the_fused_call(name):
+    """The single draft_block_forward call with the shared lm_head argmax and the
+    accept walk fused in (the form the benchmark times), captured once and replayed
+    three times with eager work in between: every replay equals the eager fused call
+    bit for bit, including the accept result and the committed tokens (the first
+    n_committed entries, the only ones the call writes)."""
+    from verifier_block_forward_amd import dbf
+    t = torch()
+    cfg = configs.get(name)
+    print(f"\n[graph fused] {name}", flush=True)
+    P = Prepared(cfg, tiled=True)
+    M, R, H, V = cfg.M, cfg.R, cfg.hidden, cfg.vocab
+    K = M - 1 if cfg.kind == "dflash" else 1
+    ck, cv = P.fresh_cache()
+    kv = dbf.make_cache(ck, cv, P.in_host["seq_len"])
+    outs = {"h_final": t.empty((M, H), dtype=t.float32, device="cuda"),
+            "hidden_out": t.empty((M, H), dtype=t.float32, device="cuda"),
+            "argmax": t.empty(M, dtype=t.int32, device="cuda"),
+            "margin": t.empty(M, dtype=t.float32, device="cuda"),
+            "result": t.zeros(5, dtype=t.int32, device="cuda"),
+            "committed": t.zeros(K + 1, dtype=t.int32, device="cuda")}
+    target_np, _ = synth.accept_targets(np.arange(K, dtype=np.int32), V, cfg.seed)
+    target = t.from_numpy(target_np).cuda()
+    io = dbf.make_io(M, R, outs["h_final"], tokens=P.inp.get("tokens"), x0=P.inp.get("x0"),
+                     ctx=P.inp.get("ctx"), hidden_out=outs["hidden_out"], lm_head=P.w_dev["lm_head"],
+                     argmax=outs["argmax"], top2_margin=outs["margin"], target=target,
+                     accept_result=outs["result"], committed=outs["committed"])
+
+    def step(stream):
+        dbf.draft_block_forward(P.ccfg, P.bw, kv, io, P.ws, stream)
+
+    tensors = list(outs.values()) + [ck, cv]
+    step(t.cuda.current_stream())
+    dbf.kv_rollback(kv, R + M)
+    t.cuda.synchronize()
+    ref = [x.clone() for x in tensors]
+
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step(t.cuda.current_stream())
+    dbf.kv_rollback(kv, R + M)
+    assert kv.seq_len == P.in_host["seq_len"]
+
+    for rep in range(3):
+        junk = t.randn(4096, device="cuda")
+        float((junk * 2).sum().item())  # eager work and a sync between replays
+        for k, x in outs.items():
+            x.fill_(float("nan") if x.is_floating_point() else -7)
+        g.replay()
+        t.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(tensors, ref)):
+            if got is outs["committed"]:
+                # only the committed prefix is written; the rest keeps the fill value
+                n = int(outs["result"][4])
+                assert t.equal(got[:n], want[:n]), f"{name}: replay {rep}, committed tokens differ"
+                assert bool((got[n:] == -7).all()), f"{name}: replay {rep} wrote past the committed tokens"
+                continue
+            assert t.equal(got, want), f"{name}: replay {rep}, output {i} differs from the eager call"
+        print(f"  replay {rep}: bitwise equal", flush=True)
