@@ -288,7 +288,8 @@ int lm_head_argmax_noalloc(const float *h, int32_t M, int32_t H, const dbf_tenso
  *   result [5] int32 out: {accept_count a, free_token = target[a],
  *          rollback = K - a, hit_eos, n_committed}.
  *   committed [K+1] int32 out or NULL: target[0..a] (the accepted drafts then the
- *          free token), cut after the first EOS (inclusive; hit_eos = 1 then).
+ *          free token), cut after the first EOS (inclusive; hit_eos = 1 then); the
+ *          first n_committed entries are written, the rest are left as they were.
  * a is the length of the longest prefix with drafts[i] == target[i]; EOS does not
  * change a or rollback. K in 1..1024. One wavefront; enqueued only. */
 int accept_prefix(const int32_t *drafts, const int32_t *target, int32_t K, const int32_t *eos,
