@@ -89,11 +89,12 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.Kin = c.kind == DBF_KIND_DFLASH ? c.n_target_hidden * c.hidden : c.hidden;
     p.rd = c.rotary_dim > 0 ? c.rotary_dim : c.head_dim;
     const int na = GEMM_NA;
-    p.in = gemm_plan(p.H, p.Kin, na, c.kind == DBF_KIND_MTP ? TARGET_UNITS / 2 : TARGET_UNITS);
     // Launch shapes measured on MI355X at the benchmark sizes: the wide projections
-    // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one)
-    // stream faster with the activation slice in LDS and a deep weight ring; the
-    // O, down and input projections with the plain split-K kernel.
+    // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one,
+    // and the MTP eh halves) stream faster with the activation slice in LDS; the
+    // down and DFlash fc projections with the plain split-K kernel, O whole-K.
+    p.in = c.kind == DBF_KIND_MTP ? gemm_plan_lds(p.H, p.Kin, 2, TARGET_UNITS / 4, 1)
+                                  : gemm_plan(p.H, p.Kin, na, TARGET_UNITS);
     const int nbq = R > 0 ? 2 : 1;  // K/V also project the context rows
     p.q = gemm_plan_lds(p.qt, p.H, 2, TARGET_UNITS / 4, nbq);
     p.k = gemm_plan_lds(p.kt, p.H, 2, TARGET_UNITS / 4, nbq);
