@@ -103,7 +103,10 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     if (c.ffn_kind == DBF_FFN_DENSE) {
         p.gate = gemm_plan_lds(p.I, p.H, 2, TARGET_UNITS / 4, 1);
         p.up = p.gate;
-        p.down = gemm_plan(p.H, p.I, na, TARGET_UNITS);
+        // with one to a few block rows the partials are small, so the long down
+        // projection takes about twice the waves, capped at 23 slices: its consumer
+        // then still sums them in one batch of loads
+        p.down = gemm_plan(p.H, p.I, na, c.kind == DBF_KIND_MTP ? 23 * ((p.H + 31) / 32) : TARGET_UNITS);
     }
     const int rows_kv = R > 0 ? 32 : 16;
     size_t off = 0;

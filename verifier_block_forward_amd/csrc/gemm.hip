@@ -140,12 +140,13 @@ __device__ __forceinline__ void skinny_mainloop(const uint16_t *const wrow[NA], 
 }
 
 // Stages in flight per wave, chosen per launch from its longest k-slice: 3 for
-// short slices (c1's O, down and fc: 6-20 steps; 2 and 4 were slower), 2 for
-// slices of GEMM_LONG_SLICE steps or more (c2's 24-42-step slices), where the
-// steady state dominates and a shorter queue of requests wins.
+// slices of up to 24 steps (the 16-row down and input projections: 12 and 20 steps;
+// the one-row 17408-deep down: 24; 2 and 4 were slower), 2 for slices of
+// GEMM_LONG_SLICE steps or more (e.g. 32-step MoE expert slices), where the steady
+// state dominates and a shorter queue of requests wins.
 constexpr int GEMM_PIPE = 3;
 constexpr int GEMM_PIPE_LONG = 2;
-constexpr int GEMM_LONG_SLICE = 24;
+constexpr int GEMM_LONG_SLICE = 25;
 
 template <int NA, int NB, int PIPE>
 __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
@@ -632,7 +633,8 @@ __device__ __forceinline__ Top2 shfl_top2(Top2 t, int mask) {
 // about 45 us (a fifth of the launch) before the other, which then ran alone at
 // half occupancy.
 // weight stages in flight per wave, and k-steps per staged chunk of the hidden
-// rows: 2 and 4 measured best with 8-wave workgroups (A/B in the c1 step against
+// rows: 2 and 4 measured best with 8-wave workgroups (A/B in the 5-layer, 16-row
+// DFlash step with its 262144 x 2816 head, against
 // 4/8, 1/8, 2/8, 2/16, 4/16, 4/4 and 3/12)
 constexpr int HEAD_PIPE = 2;
 constexpr int HEAD_XCH = 4;  // k-steps per staged chunk (a multiple of HEAD_PIPE)
