@@ -348,6 +348,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
     const float scale = 1.4426950408889634f / sqrtf((float)HD);
     const size_t head_off = (size_t)kvh * a.capacity * HD;
 
+    // the queries' loads go out ahead of the first K/V sub-tiles (loads return in
+    // issue order), and are split and staged after those are issued
+    constexpr int QIT = (QT * S + ATT_WAVES - 1) / ATT_WAVES;
+    float qraw[QIT][8];
+#pragma unroll
+    for (int i = 0; i < QIT; i++) {
+        const int idx = w + ATT_WAVES * i;
+        if (idx < QT * S) {
+            const int t = idx / S, st = idx % S;
+            const int gq = q0 + 16 * t + r16;
+            const int gqc = gq < NQ ? gq : NQ - 1;
+            const int h = kvh * G + gqc % G;
+            const float *src = a.q + (size_t)(gqc / G) * a.nq * HD + (size_t)h * HD + 32 * st + 8 * g;
+#pragma unroll
+            for (int j = 0; j < 8; j++) qraw[i][j] = src[j];
+        }
+    }
     KvRaw<HD, KVB> rb[PF];
 #pragma unroll
     for (int u = 0; u < PF; u++) {
@@ -366,19 +383,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
         qm[t] = (qv[t] ? gq : NQ - 1) / G;
     }
     // B operand of the score MFMA, written cooperatively: lane holds dims 32s+8g..+7
-    for (int idx = w; idx < QT * S; idx += ATT_WAVES) {
-        const int t = idx / S, st = idx % S;
-        const int gq = q0 + 16 * t + r16;
-        const int gqc = gq < NQ ? gq : NQ - 1;
-        const int h = kvh * G + gqc % G;
-        float v[8];
-        const float *src = a.q + (size_t)(gqc / G) * a.nq * HD + (size_t)h * HD + 32 * st + 8 * g;
 #pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = src[j] * scale;
-        bf16x8 hi, lo;
-        split8(v, hi, lo);
-        qsm[(idx * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4, hi);
-        qsm[(idx * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo);
+    for (int i = 0; i < QIT; i++) {
+        const int idx = w + ATT_WAVES * i;
+        if (idx < QT * S) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = qraw[i][j] * scale;
+            bf16x8 hi, lo;
+            split8(v, hi, lo);
+            qsm[(idx * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4, hi);
+            qsm[(idx * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4, lo);
+        }
     }
 
     // BF16 caches keep the query operands in registers where they fit (the F32
