@@ -258,6 +258,27 @@ def test_block_moe_small(orc, cfg):
     run_moe_case(orc, cfg)
 
 
+@pytest.mark.parametrize("E,top_k,M", [(16, 3, 3), (16, 1, 2), (100, 5, 4), (300, 7, 2)])
+def test_block_moe_router_ties(orc, E, top_k, M):
+    """Router rows duplicated in pairs (expert 2i+1 gets expert 2i's row): every
+    logit comes in an exactly equal pair on both sides, so with an odd top_k the
+    last pick is always a tie, which must go to the lower (even) index. The experts
+    themselves differ, so a wrong pick shows in the block output."""
+    cfg = small_moe(name=f"moe_ties_e{E}_k{top_k}", n_experts=E, top_k=top_k, M=M, seed=35)
+    w = synth.make_weights(cfg)
+    r = w["layers.0.router"]
+    r[1::2] = r[0:E - 1:2]
+    print(f"\n[moe ties] E={E} top_k={top_k} M={M}", flush=True)
+    prep = Prepared(cfg, weights=w)
+    got = prep.run()
+    want = orc.block_forward(cfg, prep.w_host, prep.in_host)
+    sel = want["moe_sel"][0]
+    assert (sel[:, -1] % 2 == 0).all(), sel  # the oracle's tied pick is the even twin
+    gk, gv = prep.cache_host(*got["cache"])
+    compare_block(cfg, got, want, cfg.C, cfg.C + cfg.M, (gk, gv), (want["cache_k"], want["cache_v"]))
+    assert got["moe_experts"][0] == len(np.unique(sel))
+
+
 def test_block_moe_tiled(orc):
     run_moe_case(orc, small_moe(name="moe_tiled", M=4), tiled=True)
 
