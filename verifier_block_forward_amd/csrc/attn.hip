@@ -325,6 +325,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
     using L = AttnLds<HD, QT, KVB>;
     constexpr int S = L::S, DT = L::DT, VTW = L::VTW;
     constexpr int PF = attn_prefetch<HD, KVB>();
+    // F32 caches run the key loop peeled (below); the two-slot BF16 variants
+    // measured slower that way: their unconditional refills push the registers to
+    // the limit and the transposed V reads then go out one at a time.
+    constexpr bool PEEL = !KVB;
     __shared__ __align__(16) unsigned char smem[L::BYTES];
     uint4 *qsm = (uint4 *)smem;
 
@@ -365,13 +369,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
             for (int j = 0; j < 8; j++) qraw[i][j] = src[j];
         }
     }
+    // (issued even past the wave's range: those rows are clamped to the last key,
+    // and every slot then has its loads in flight when the key loop starts)
     KvRaw<HD, KVB> rb[PF];
 #pragma unroll
     for (int u = 0; u < PF; u++) {
-        if (u < n_sub) {
-            attn_load_k<HD, KVB>(rb[u], a, head_off, k_lo + (long long)u * ATT_KT, n_all, g, r16);
-            attn_load_v<HD, KVB>(rb[u], a, head_off, k_lo + (long long)u * ATT_KT, n_all, g, r16);
-        }
+        attn_load_k<HD, KVB>(rb[u], a, head_off, k_lo + (long long)u * ATT_KT, n_all, g, r16);
+        attn_load_v<HD, KVB>(rb[u], a, head_off, k_lo + (long long)u * ATT_KT, n_all, g, r16);
     }
 
     int qm[QT];
@@ -419,102 +423,116 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
     // every query sees the keys up to lim_all; sub-tiles below it skip the mask
     const long long lim_all = a.n_ctx + (a.bidir ? a.M - 1 : 0);
 
-    for (int base = 0; base < n_sub; base += PF) {
+    // Sub-tile it from slot rbu; with more, the slot's loads of sub-tile it + PF go
+    // out as soon as its registers are free.
+    auto sub_tile = [&](KvRaw<HD, KVB> &rbu, const int it, const bool more) __attribute__((always_inline)) {
+        const long long kb = k_lo + (long long)it * ATT_KT;
+        const long long kb_next = kb + (long long)PF * ATT_KT;
+        if constexpr (KVB) attn_v_store<HD, VTW>(rbu, vth, g, r16);
+        f32x4 sc[QT];
 #pragma unroll
-        for (int u = 0; u < PF; u++) {
-            const int it = base + u;
-            if (it >= n_sub) break;
-            const long long kb = k_lo + (long long)it * ATT_KT;
-            const bool more = it + PF < n_sub;
-            const long long kb_next = kb + (long long)PF * ATT_KT;
-            if constexpr (KVB) attn_v_store<HD, VTW>(rb[u], vth, g, r16);
-            f32x4 sc[QT];
+        for (int t = 0; t < QT; t++) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < QT; t++) sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < S; st++) {
-                bf16x8 kh, kl;
-                attn_k_step<HD, KVB>(rb[u], st, kh, kl);
-#pragma unroll
-                for (int t = 0; t < QT; t++) {
-                    bf16x8 qh, ql;
-                    if constexpr (QREG) {
-                        qh = qreg[(t * S + st) * 2 + 0];
-                        ql = qreg[(t * S + st) * 2 + 1];
-                    } else {
-                        qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
-                        ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
-                    }
-                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, sc[t], 0, 0, 0);
-                    sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql, sc[t], 0, 0, 0);
-                    if constexpr (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh, sc[t], 0, 0, 0);
-                }
-            }
-            if (more) attn_load_k<HD, KVB>(rb[u], a, head_off, kb_next, n_all, g, r16);
-            // masked scores and their per-query max over the sub-tile
-            const bool full = kb + ATT_KT <= k_hi && kb + ATT_KT - 1 <= lim_all;  // wave-uniform
-            float sv[QT][4], mx[QT];
-            bool grow = false;
+        for (int st = 0; st < S; st++) {
+            bf16x8 kh, kl;
+            attn_k_step<HD, KVB>(rbu, st, kh, kl);
 #pragma unroll
             for (int t = 0; t < QT; t++) {
-                if (full) {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) sv[t][i] = sc[t][i];
+                bf16x8 qh, ql;
+                if constexpr (QREG) {
+                    qh = qreg[(t * S + st) * 2 + 0];
+                    ql = qreg[(t * S + st) * 2 + 1];
                 } else {
-                    const long long lim = a.n_ctx + (a.bidir ? a.M - 1 : qm[t]);  // last visible key
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const long long kp = kb + 4 * g + i;
-                        sv[t][i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
-                    }
+                    qh = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 0) * 64 + lane]);
+                    ql = __builtin_bit_cast(bf16x8, qsm[((t * S + st) * 2 + 1) * 64 + lane]);
                 }
-                mx[t] = group4_max(fmaxf(fmaxf(sv[t][0], sv[t][1]), fmaxf(sv[t][2], sv[t][3])));
-                grow |= mx[t] > m_run[t] + ATT_RESCALE;  // first finite score: m_run is -inf
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh, sc[t], 0, 0, 0);
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql, sc[t], 0, 0, 0);
+                if constexpr (!KVB) sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh, sc[t], 0, 0, 0);
             }
-            if (__ballot(grow)) {  // move the reference point of every query, rescale acc and l
+        }
+        if (more) attn_load_k<HD, KVB>(rbu, a, head_off, kb_next, n_all, g, r16);
+        // masked scores and their per-query max over the sub-tile
+        const bool full = kb + ATT_KT <= k_hi && kb + ATT_KT - 1 <= lim_all;  // wave-uniform
+        float sv[QT][4], mx[QT];
+        bool grow = false;
 #pragma unroll
-                for (int t = 0; t < QT; t++) {
-                    const float m_new = fmaxf(m_run[t], mx[t]);
-                    const float al = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[t] - m_new);
-                    l_run[t] *= al;
+        for (int t = 0; t < QT; t++) {
+            if (full) {
 #pragma unroll
-                    for (int d = 0; d < DT; d++) acc[t][d] *= al;
-                    m_run[t] = m_new;
-                }
-            }
-            s16x4 ph[QT], pl[QT];
-#pragma unroll
-            for (int t = 0; t < QT; t++) {
-                const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];  // all scores -inf: p = 0
-                float p[4], ps = 0.f;
+                for (int i = 0; i < 4; i++) sv[t][i] = sc[t][i];
+            } else {
+                const long long lim = a.n_ctx + (a.bidir ? a.M - 1 : qm[t]);  // last visible key
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    p[i] = __builtin_amdgcn_exp2f(sv[t][i] - m_use);
-                    ps += p[i];
-                }
-                split4(p[0], p[1], p[2], p[3], ph[t], pl[t]);
-                l_run[t] += ps;
-            }
-            if constexpr (KVB) wave_lds_sync();  // V rows of this sub-tile written by every lane
-#pragma unroll
-            for (int d = 0; d < DT; d++) {
-                s16x4 va, vb;
-                if constexpr (KVB) {
-                    va = attn_v_operand<VTW>(vth, d, g, r16);
-                } else {
-                    split4(rb[u].v[4 * d], rb[u].v[4 * d + 1], rb[u].v[4 * d + 2], rb[u].v[4 * d + 3], va, vb);
-                }
-#pragma unroll
-                for (int t = 0; t < QT; t++) {
-                    f32x4 o = acc[t][d];
-                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[t], o, 0, 0, 0);
-                    o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[t], o, 0, 0, 0);
-                    if constexpr (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, ph[t], o, 0, 0, 0);
-                    acc[t][d] = o;
+                    const long long kp = kb + 4 * g + i;
+                    sv[t][i] = (kp < k_hi && kp <= lim) ? sc[t][i] : -INFINITY;
                 }
             }
-            if constexpr (KVB) wave_lds_sync();  // V reads done before the next sub-tile overwrites them
-            if (more) attn_load_v<HD, KVB>(rb[u], a, head_off, kb_next, n_all, g, r16);
+            mx[t] = group4_max(fmaxf(fmaxf(sv[t][0], sv[t][1]), fmaxf(sv[t][2], sv[t][3])));
+            grow |= mx[t] > m_run[t] + ATT_RESCALE;  // first finite score: m_run is -inf
+        }
+        if (__ballot(grow)) {  // move the reference point of every query, rescale acc and l
+#pragma unroll
+            for (int t = 0; t < QT; t++) {
+                const float m_new = fmaxf(m_run[t], mx[t]);
+                const float al = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[t] - m_new);
+                l_run[t] *= al;
+#pragma unroll
+                for (int d = 0; d < DT; d++) acc[t][d] *= al;
+                m_run[t] = m_new;
+            }
+        }
+        s16x4 ph[QT], pl[QT];
+#pragma unroll
+        for (int t = 0; t < QT; t++) {
+            const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];  // all scores -inf: p = 0
+            float p[4], ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                p[i] = __builtin_amdgcn_exp2f(sv[t][i] - m_use);
+                ps += p[i];
+            }
+            split4(p[0], p[1], p[2], p[3], ph[t], pl[t]);
+            l_run[t] += ps;
+        }
+        if constexpr (KVB) wave_lds_sync();  // V rows of this sub-tile written by every lane
+#pragma unroll
+        for (int d = 0; d < DT; d++) {
+            s16x4 va, vb;
+            if constexpr (KVB) {
+                va = attn_v_operand<VTW>(vth, d, g, r16);
+            } else {
+                split4(rbu.v[4 * d], rbu.v[4 * d + 1], rbu.v[4 * d + 2], rbu.v[4 * d + 3], va, vb);
+            }
+#pragma unroll
+            for (int t = 0; t < QT; t++) {
+                f32x4 o = acc[t][d];
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[t], o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[t], o, 0, 0, 0);
+                if constexpr (!KVB) o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, ph[t], o, 0, 0, 0);
+                acc[t][d] = o;
+            }
+        }
+        if constexpr (KVB) wave_lds_sync();  // V reads done before the next sub-tile overwrites them
+        if (more) attn_load_v<HD, KVB>(rbu, a, head_off, kb_next, n_all, g, r16);
+    };
+    // The main loop refills every slot, so each slot's loads are in flight in a fixed
+    // order and the wait for one slot leaves the others' loads outstanding; the last
+    // sub-tiles, whose refills depend on the count, run after it (a conditional
+    // refill inside the loop makes every wait cover all slots).
+    const int n_main = (PEEL && n_sub > PF) ? (n_sub - PF) / PF * PF : 0;
+    int it0 = 0;
+    for (; it0 < n_main; it0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; u++) sub_tile(rb[u], it0 + u, true);
+    }
+    for (; it0 < n_sub; it0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; u++) {
+            const int it = it0 + u;
+            if (it >= n_sub) break;
+            sub_tile(rb[u], it, it + PF < n_sub);
         }
     }
 
