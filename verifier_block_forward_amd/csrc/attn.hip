@@ -536,23 +536,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
         }
     }
 
-    // merge the four waves' (m, l, acc) through LDS (the loop buffers are dead now)
+    // merge the four waves' (m, l, acc) through LDS (the loop buffers are dead now):
+    // wave w finishes the dims tiles [w DPW, (w+1) DPW) of every query tile, so
+    // each wave writes the other waves' tiles of its accumulator and reads the
+    // three other copies of its own
+    constexpr int DPW = DT / ATT_WAVES;
+    static_assert(DT % ATT_WAVES == 0, "every wave owns whole dims tiles");
 #pragma unroll
     for (int t = 0; t < QT; t++) l_run[t] = group4_sum(l_run[t]);
     __syncthreads();
-    float4 *accb = (float4 *)smem;                       // [3][QT][DT][64]
-    float2 *mlb = (float2 *)(smem + L::ACC_BYTES);      // [4][QT][64]
+    // [3][QT][DT][64]: writer v's copy of dims tile d, in slot v (v < owner) or
+    // v - 1 (v > owner) of the owner's three
+    float4 *accb = (float4 *)smem;
+    float2 *mlb = (float2 *)(smem + L::ACC_BYTES);  // [4][QT][64]
 #pragma unroll
     for (int t = 0; t < QT; t++) {
         mlb[(w * QT + t) * 64 + lane] = make_float2(m_run[t], l_run[t]);
-        if (w > 0)
 #pragma unroll
-            for (int d = 0; d < DT; d++)
-                accb[(((w - 1) * QT + t) * DT + d) * 64 + lane] =
-                    make_float4(acc[t][d][0], acc[t][d][1], acc[t][d][2], acc[t][d][3]);
+        for (int d = 0; d < DT; d++) {
+            const int own = d / DPW;
+            if (own == w) continue;
+            const int slot = w < own ? w : w - 1;
+            accb[((slot * QT + t) * DT + d) * 64 + lane] =
+                make_float4(acc[t][d][0], acc[t][d][1], acc[t][d][2], acc[t][d][3]);
+        }
     }
     __syncthreads();
-    if (w != 0) return;
 #pragma unroll
     for (int t = 0; t < QT; t++) {
         float mw[ATT_WAVES], lw[ATT_WAVES];
@@ -577,15 +586,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_wpe<HD
         float *o = a.part + ((size_t)c * a.M * a.nq + qidx) * (HD + ATT_PART_EXTRA);
 #pragma unroll
         for (int d = 0; d < DT; d++) {
-            f32x4 s4 = acc[t][d] * e[0];
+            if (d / DPW != w) continue;
+            // waves in order 0..3, this wave's own copy from its registers
+            f32x4 s4;
 #pragma unroll
-            for (int v = 1; v < ATT_WAVES; v++) {
-                const float4 q4 = accb[(((v - 1) * QT + t) * DT + d) * 64 + lane];
-                s4 += f32x4{q4.x, q4.y, q4.z, q4.w} * e[v];
+            for (int v = 0; v < ATT_WAVES; v++) {
+                f32x4 x;
+                if (v == w) {
+                    x = acc[t][d];
+                } else {
+                    const float4 q4 = accb[(((v < w ? v : v - 1) * QT + t) * DT + d) * 64 + lane];
+                    x = f32x4{q4.x, q4.y, q4.z, q4.w};
+                }
+                if (v == 0)
+                    s4 = x * e[0];
+                else
+                    s4 += x * e[v];
             }
             *(float4 *)(o + 16 * d + 4 * g) = make_float4(s4[0], s4[1], s4[2], s4[3]);
         }
-        if (g == 0) {
+        if (w == 0 && g == 0) {
             o[HD] = lsum > 0.f ? mx : -INFINITY;
             o[HD + 1] = lsum;
         }
