@@ -76,6 +76,21 @@ def test_block_combine_chunk_counts(orc, cfg):
     run_case(orc, cfg)
 
 
+# With 8 kv heads the planner makes about 32 chunks per head, so a 10,000-position
+# context gives the waves of the first 31 chunks five 16-key sub-tiles each: the F32
+# key loop runs four passes of its main loop (unconditional refills) and one tail
+# pass, and the two-slot BF16 loop two full passes and a half one. In the last chunk
+# one wave has two sub-tiles and two waves have none.
+@pytest.mark.parametrize("cfg", [
+    small(name="waves_5subtiles_f32", hidden=256, n_q_heads=16, n_kv_heads=8, head_dim=128,
+          M=16, R=4, C=10000, n_layers=1),
+    small(name="waves_5subtiles_bf16", hidden=256, n_q_heads=16, n_kv_heads=8, head_dim=128,
+          M=16, R=4, C=10000, n_layers=1, kv_dtype="bf16"),
+], ids=lambda c: c.name)
+def test_block_long_wave_shares(orc, cfg):
+    run_case(orc, cfg)
+
+
 def test_block_c0(orc):
     run_case(orc, configs.C0)
 
