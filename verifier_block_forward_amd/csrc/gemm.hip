@@ -148,8 +148,18 @@ constexpr int GEMM_PIPE = 3;
 constexpr int GEMM_PIPE_LONG = 2;
 constexpr int GEMM_LONG_SLICE = 25;
 
-template <int NA, int NB, int PIPE>
-__global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
+// W waves per workgroup take W consecutive units; with the tile index fastest they
+// share one k-slice of the activations, which the CU's vector cache then serves once.
+// Plain launches with slices of SPLITK_W_LONG_STEPS steps or more (the long down and
+// input projections) use 8 (c1 -0.3%, c2 -0.3% per step against 4), launches with
+// expert slots 2 (c4m4 -0.5%; 8 was +1.9% there), other plain launches 4.
+constexpr int SPLITK_W_LONG = 8;
+constexpr int SPLITK_W_LONG_STEPS = 8;
+constexpr int SPLITK_W_SLOTS = 2;
+constexpr int SPLITK_W = 4;
+
+template <int NA, int NB, int PIPE, int W>
+__global__ __launch_bounds__(64 * W) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
     // scalar wave index: the unit, the segment lookup and the segment's fields are
     // then scalar (kernel-argument loads, not vector loads)
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(256) void k_gemm_splitk(GemmArgs args) {
     for (int i = 0; i < GEMM_MAXSEG; i++) ub[i] = args.seg[i].unit_begin;
     const int nblk = gridDim.x, nseg = args.nseg, total = args.total_units;
     __builtin_amdgcn_sched_barrier(0);  // keep those loads ahead of their first use: one trip
-    const int unit = xcd_logical(blockIdx.x, nblk) * 4 + wv;
+    const int unit = xcd_logical(blockIdx.x, nblk) * W + wv;
     int si = 0;
 #pragma unroll
     for (int i = 1; i < GEMM_MAXSEG; i++)
@@ -540,6 +550,15 @@ GemmPlan gemm_plan_lds(int N, int K, int na, int target_units, int nbmax) {
     return p;
 }
 
+template <int NA, int NB, int W>
+static void go_splitk(const GemmArgs &a, bool long_slices, hipStream_t s) {
+    const dim3 grid((a.total_units + W - 1) / W), block(64 * W);
+    if (long_slices)
+        launch_k(PROF_PROJ, "k_gemm_splitk(long)", (k_gemm_splitk<NA, NB, GEMM_PIPE_LONG, W>), grid, block, 0, s, a);
+    else
+        launch_k(PROF_PROJ, "k_gemm_splitk", (k_gemm_splitk<NA, NB, GEMM_PIPE, W>), grid, block, 0, s, a);
+}
+
 template <int NA, int NB>
 static void go(const GemmArgs &a, hipStream_t s) {
     if (a.lds_x) {  // total_units counts workgroups
@@ -556,14 +575,19 @@ static void go(const GemmArgs &a, hipStream_t s) {
         else
             launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB, LPIPE>), dim3(a.total_units), dim3(256), lds, s, a);
     } else {
-        const int blocks = (a.total_units + 3) / 4;
         int steps = 0;
-        for (int i = 0; i < a.nseg; i++)
+        bool slots = false;
+        for (int i = 0; i < a.nseg; i++) {
             if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
-        if (steps >= GEMM_LONG_SLICE)
-            launch_k(PROF_PROJ, "k_gemm_splitk(long)", (k_gemm_splitk<NA, NB, GEMM_PIPE_LONG>), dim3(blocks), dim3(256), 0, s, a);
+            slots |= a.seg[i].slots > 0;
+        }
+        const bool lg = steps >= GEMM_LONG_SLICE;
+        if (slots)
+            go_splitk<NA, NB, SPLITK_W_SLOTS>(a, lg, s);
+        else if (steps >= SPLITK_W_LONG_STEPS)
+            go_splitk<NA, NB, SPLITK_W_LONG>(a, lg, s);
         else
-            launch_k(PROF_PROJ, "k_gemm_splitk", (k_gemm_splitk<NA, NB, GEMM_PIPE>), dim3(blocks), dim3(256), 0, s, a);
+            go_splitk<NA, NB, SPLITK_W>(a, lg, s);
     }
 }
 
