@@ -151,8 +151,9 @@ constexpr int GEMM_LONG_SLICE = 25;
 // W waves per workgroup take W consecutive units; with the tile index fastest they
 // share one k-slice of the activations, which the CU's vector cache then serves once.
 // Plain launches with slices of SPLITK_W_LONG_STEPS steps or more (the long down and
-// input projections) use 8 (c1 -0.3%, c2 -0.3% per step against 4), launches with
-// expert slots 2 (c4m4 -0.5%; 8 was +1.9% there), other plain launches 4.
+// input projections) use 8 (the 16-row DFlash and one-row dense MTP steps -0.3% each
+// against 4), launches with expert slots 2 (the four-row MoE MTP step -0.5%; 8 was
+// +1.9% there), other plain launches 4.
 constexpr int SPLITK_W_LONG = 8;
 constexpr int SPLITK_W_LONG_STEPS = 8;
 constexpr int SPLITK_W_SLOTS = 2;
