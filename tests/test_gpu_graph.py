@@ -15,7 +15,7 @@ from tests.gpu_harness import Prepared, torch
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["c0", "c4m4"])
+@pytest.mark.parametrize("name", ["c0", "c4m4", "c1"])
 def test_graph_replay_matches_eager(name):
     from verifier_block_forward_amd import dbf
     t = torch()
@@ -113,7 +113,7 @@ def test_graph_replay_of_the_sampled_round():
             assert t.equal(got, want), f"replay {rep}, output {i} differs from the eager call"
 
 
-@pytest.mark.parametrize("name", ["c0", "c4m4"])
+@pytest.mark.parametrize("name", ["c0", "c4m4", "c1"])
 def test_graph_replay_of_the_fused_call(name):
     """The single draft_block_forward call with the shared lm_head argmax and the
     accept walk fused in (the form the benchmark times), captured once and replayed
