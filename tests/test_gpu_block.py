@@ -91,6 +91,31 @@ def test_block_long_wave_shares(orc, cfg):
     run_case(orc, cfg)
 
 
+# The attention kernel takes 1, 2 or 4 query tiles (16 queries each) per workgroup,
+# capped by head dim and cache type (F32: 4 at 64 dims, 2 at 128, 1 at 256; BF16: 2
+# at 256 dims, else 4). These shapes reach the variants the other tests leave out:
+# four tiles at 64 dims (F32 and BF16, 52 of 64 queries used), four at 128 dims with
+# a BF16 cache (36 queries, and 72 queries over two query groups), one at 128 dims
+# with a BF16 cache, and BF16 caches at 256 dims with one and two tiles.
+@pytest.mark.parametrize("cfg", [
+    small(name="qt4_hd64_f32", n_q_heads=8, n_kv_heads=2, M=13, R=3, C=700),
+    small(name="qt4_hd64_bf16", n_q_heads=8, n_kv_heads=2, M=13, R=3, C=700, kv_dtype="bf16"),
+    small(name="qt4_hd128_bf16", hidden=264, n_q_heads=4, n_kv_heads=1, head_dim=128, M=9, R=5,
+          C=700, kv_dtype="bf16"),
+    small(name="qt4x2_hd128_bf16", hidden=264, n_q_heads=8, n_kv_heads=1, head_dim=128, M=9, R=5,
+          C=300, n_layers=1, kv_dtype="bf16"),
+    small(name="qt1_hd128_bf16", hidden=264, n_q_heads=2, n_kv_heads=1, head_dim=128, M=7, R=9,
+          C=700, kv_dtype="bf16"),
+    small(name="qt2_hd256_bf16", hidden=256, n_q_heads=6, n_kv_heads=1, head_dim=256, M=3, R=2,
+          rotary_dim=64, C=700, kv_dtype="bf16"),
+    small(name="qt1_hd256_bf16_mtp", kind="mtp", R=0, M=1, has_attn_gate=True, n_layers=1,
+          n_target_hidden=0, hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=256, C=900,
+          kv_dtype="bf16"),
+], ids=lambda c: c.name)
+def test_block_query_tile_variants(orc, cfg):
+    run_case(orc, cfg)
+
+
 def test_block_c0(orc):
     run_case(orc, configs.C0)
 
