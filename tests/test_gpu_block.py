@@ -61,7 +61,8 @@ def test_block_small(orc, cfg):
 # The chunk merge picks its block size and batch from the chunk count, and the chunk
 # count follows the context length (one query group per kv head, 256 chunks at most).
 # These contexts put each head dim into the ranges the other tests do not reach:
-# 128-dim heads with 33-64 and 65-256 chunks, 256-dim heads with 17-32 chunks.
+# 64-dim heads with 65-128 and 129-256 chunks, 128-dim heads with 33-64 and 65-256
+# chunks, 256-dim heads with 17-32 and 129-256 chunks.
 @pytest.mark.parametrize("cfg", [
     small(name="combine_hd128_63chunks", hidden=264, n_q_heads=2, n_kv_heads=1, head_dim=128,
           M=7, R=9, C=4000, n_layers=1),
@@ -71,6 +72,10 @@ def test_block_small(orc, cfg):
           M=3, R=2, rotary_dim=64, C=1500, n_layers=1),
     small(name="combine_mtp_hd256_gate", kind="mtp", R=0, M=1, has_attn_gate=True, n_layers=1,
           n_target_hidden=0, hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=256, C=3000),
+    small(name="combine_hd64_71chunks", C=9000, n_layers=1),
+    small(name="combine_hd64_157chunks", n_q_heads=2, n_kv_heads=1, C=10000, n_layers=1),
+    small(name="combine_mtp_hd256_141chunks", kind="mtp", R=0, M=1, has_attn_gate=True, n_layers=1,
+          n_target_hidden=0, hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=256, C=9000),
 ], ids=lambda c: c.name)
 def test_block_combine_chunk_counts(orc, cfg):
     run_case(orc, cfg)
