@@ -57,7 +57,6 @@ int check_t(const dbf_tensor &t, const char *name, int dtype, int ndim, int64_t 
     } while (0)
 
 constexpr int TARGET_UNITS = 2048;  // wave units per projection launch (256 CUs x 8)
-constexpr int GEMM_NA = 2;          // row tiles per wave of the plain split-K kernel
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -88,25 +87,24 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.I = c.intermediate;
     p.Kin = c.kind == DBF_KIND_DFLASH ? c.n_target_hidden * c.hidden : c.hidden;
     p.rd = c.rotary_dim > 0 ? c.rotary_dim : c.head_dim;
-    const int na = GEMM_NA;
     // Launch shapes measured on MI355X at the benchmark sizes: the wide projections
     // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one,
     // and the MTP eh halves) stream faster with the activation slice in LDS; the
     // down and DFlash fc projections with the plain split-K kernel, O whole-K.
-    p.in = c.kind == DBF_KIND_MTP ? gemm_plan_lds(p.H, p.Kin, 2, TARGET_UNITS / 4, 1)
-                                  : gemm_plan(p.H, p.Kin, na, TARGET_UNITS);
+    p.in = c.kind == DBF_KIND_MTP ? gemm_plan_lds(p.H, p.Kin, TARGET_UNITS / 4, 1)
+                                  : gemm_plan(p.H, p.Kin, TARGET_UNITS);
     const int nbq = R > 0 ? 2 : 1;  // K/V also project the context rows
-    p.q = gemm_plan_lds(p.qt, p.H, 2, TARGET_UNITS / 4, nbq);
-    p.k = gemm_plan_lds(p.kt, p.H, 2, TARGET_UNITS / 4, nbq);
+    p.q = gemm_plan_lds(p.qt, p.H, TARGET_UNITS / 4, nbq);
+    p.k = gemm_plan_lds(p.kt, p.H, TARGET_UNITS / 4, nbq);
     p.v = p.k;
     p.g = p.q;
     if (c.ffn_kind == DBF_FFN_DENSE) {
-        p.gate = gemm_plan_lds(p.I, p.H, 2, TARGET_UNITS / 4, 1);
+        p.gate = gemm_plan_lds(p.I, p.H, TARGET_UNITS / 4, 1);
         p.up = p.gate;
         // with one to a few block rows the partials are small, so the long down
         // projection takes about twice the waves, capped at 23 slices: its consumer
         // then still sums them in one batch of loads
-        p.down = gemm_plan(p.H, p.I, na, c.kind == DBF_KIND_MTP ? 23 * ((p.H + 31) / 32) : TARGET_UNITS);
+        p.down = gemm_plan(p.H, p.I, c.kind == DBF_KIND_MTP ? 23 * ((p.H + 31) / 32) : TARGET_UNITS);
     }
     const int rows_kv = R > 0 ? 32 : 16;
     size_t off = 0;
@@ -148,14 +146,14 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     if (c.ffn_kind == DBF_FFN_MOE) {
         const int E = c.n_experts, Ie = c.expert_intermediate, Is = c.shared_intermediate;
         p.max_slots = E < M * c.top_k ? E : M * c.top_k;  // >= 1: M >= 1, top_k >= 1
-        p.router = gemm_plan(E, p.H, na, TARGET_UNITS / 4);
-        p.sgi = gemm_plan(1, p.H, na, 64);
-        p.shg = gemm_plan(Is, p.H, na, TARGET_UNITS / 8);
+        p.router = gemm_plan(E, p.H, TARGET_UNITS / 4);
+        p.sgi = gemm_plan(1, p.H, 64);
+        p.shg = gemm_plan(Is, p.H, TARGET_UNITS / 8);
         int per_slot = TARGET_UNITS / (2 * p.max_slots);
-        p.eg = gemm_plan(Ie, p.H, na, per_slot < 1 ? 1 : per_slot);
+        p.eg = gemm_plan(Ie, p.H, per_slot < 1 ? 1 : per_slot);
         per_slot = TARGET_UNITS / p.max_slots;
-        p.ed = gemm_plan(p.H, Ie, na, per_slot < 1 ? 1 : per_slot);
-        p.shd = gemm_plan(p.H, Is, na, TARGET_UNITS / 8);
+        p.ed = gemm_plan(p.H, Ie, per_slot < 1 ? 1 : per_slot);
+        p.shd = gemm_plan(p.H, Is, TARGET_UNITS / 8);
         p.p_router = take((size_t)p.router.ksplit * 16 * E * f);
         p.p_sgi = take((size_t)p.sgi.ksplit * 16 * 1 * f);
         p.p_shg = take((size_t)p.shg.ksplit * 16 * Is * f);
@@ -177,19 +175,16 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     return p;
 }
 
-// One projection launch: segments planned with the same na and lds (the first
+// One projection launch: segments planned with the same lds flag (the first
 // segment's plan fixes the kernel). rows: activation rows that hold data (M block
 // rows, or R context rows), the default for every split tile added.
 struct SegList {
     GemmArgs a{};
-    int nbmax = 1, na = GEMM_NA, rows;
+    int nbmax = 1, rows;
     explicit SegList(int rows_) : rows(rows_) {}
     void add(const dbf_tensor &t, int N, int K, const GemmPlan &pl, float *out, const uint16_t *xs0,
              const uint16_t *xs1 = nullptr, int rows0 = 0, int rows1 = 0) {
-        if (a.nseg == 0) {
-            na = pl.na;
-            a.lds_x = pl.lds;
-        }
+        if (a.nseg == 0) a.lds_x = pl.lds;
         GemmSeg &s = a.seg[a.nseg++];
         s.W = (const uint16_t *)t.data;
         s.tiled = t.dtype == DBF_BF16_T16;
@@ -222,7 +217,7 @@ struct SegList {
         s.out_stride = (long long)pl.ksplit * 16 * N;
         a.total_units += (slots - 1) * plan_units(pl);
     }
-    void launch(hipStream_t st) { launch_gemm(a, na, nbmax, st); }
+    void launch(hipStream_t st) { launch_gemm(a, nbmax, st); }
 };
 
 int validate_config(const dbf_config *c) {

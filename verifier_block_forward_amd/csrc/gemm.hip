@@ -524,10 +524,10 @@ void launch_gemm_full(const FullArgs &a, hipStream_t s) {
         launch_k(PROF_PROJ, "k_gemm_full", k_gemm_full<W, 2>, dim3((Np + 31) / 32), dim3(64 * W), 0, s, a);
 }
 
-GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {
-    GemmPlan p{0, 0, 0, na, 0};
-    if (N < 1 || K < 1 || na < 1) return p;  // empty projection: no units
-    p.tiles = (N + 16 * na - 1) / (16 * na);
+GemmPlan gemm_plan(int N, int K, int target_units, int max_steps) {
+    GemmPlan p{0, 0, 0, 0};
+    if (N < 1 || K < 1) return p;  // empty projection: no units
+    p.tiles = (N + 16 * GEMM_NA - 1) / (16 * GEMM_NA);
     const int S = (K + 31) / 32;
     int ks = (target_units + p.tiles - 1) / p.tiles;
     const int ks_min = max_steps > 0 ? (S + max_steps - 1) / max_steps : 1;
@@ -545,8 +545,8 @@ GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps) {
     return p;
 }
 
-GemmPlan gemm_plan_lds(int N, int K, int na, int target_units, int nbmax) {
-    GemmPlan p = gemm_plan(N, K, na, target_units, nbmax > 1 ? LDS_X_STEPS_NB2 : LDS_X_STEPS_NB1);
+GemmPlan gemm_plan_lds(int N, int K, int target_units, int nbmax) {
+    GemmPlan p = gemm_plan(N, K, target_units, nbmax > 1 ? LDS_X_STEPS_NB2 : LDS_X_STEPS_NB1);
     p.lds = 1;
     return p;
 }
@@ -592,17 +592,12 @@ static void go(const GemmArgs &a, hipStream_t s) {
     }
 }
 
-void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s) {
+void launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s) {
     if (a.total_units <= 0) return;
-    if (nbmax == 1) {
-        if (na == 1) go<1, 1>(a, s);
-        else if (na == 2) go<2, 1>(a, s);
-        else go<4, 1>(a, s);
-    } else {
-        if (na == 1) go<1, 2>(a, s);
-        else if (na == 2) go<2, 2>(a, s);
-        else go<4, 2>(a, s);
-    }
+    if (nbmax == 1)
+        go<GEMM_NA, 1>(a, s);
+    else
+        go<GEMM_NA, 2>(a, s);
 }
 
 // ---------------------------------------------------------------------------

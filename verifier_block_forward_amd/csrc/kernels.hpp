@@ -63,22 +63,26 @@ struct GemmArgs {
 // Work decomposition of one segment: rows per wave unit = 16 * na; lds selects
 // the kernel with the activation slice staged in LDS (units are then workgroups of
 // four row tiles). Segments of one launch share na and lds.
+// Row tiles (16 weight rows each) per wave in every projection launch: two measured
+// best in both the split-K and the LDS-staged kernels (four, with twice the bytes
+// in flight per wave, were slower in each).
+constexpr int GEMM_NA = 2;
 struct GemmPlan {
-    int tiles, ksplit, kslice_steps, na, lds;
+    int tiles, ksplit, kslice_steps, lds;
 };
 // target_units: wave units (tiles x ksplit) to aim for; max_steps > 0 caps the
 // k-slice length (steps of 32 columns)
-GemmPlan gemm_plan(int N, int K, int na, int target_units, int max_steps = 0);
+GemmPlan gemm_plan(int N, int K, int target_units, int max_steps = 0);
 constexpr int LDS_X_STEPS_NB1 = 20;  // 40 KiB of split activations per workgroup
 constexpr int LDS_X_STEPS_NB2 = 10;
 // LDS-staged plan for a launch whose segments have up to nbmax split tiles
-GemmPlan gemm_plan_lds(int N, int K, int na, int target_units, int nbmax);
+GemmPlan gemm_plan_lds(int N, int K, int target_units, int nbmax);
 // units (waves, or workgroups for lds plans) of one matrix of the segment
 inline int plan_units(const GemmPlan &p) {
     return p.lds ? ((p.tiles + 3) / 4) * p.ksplit : p.tiles * p.ksplit;
 }
 
-void launch_gemm(const GemmArgs &a, int na, int nbmax, hipStream_t s);
+void launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Whole-K projection with the residual epilogue: one workgroup owns 16 or 32 output
