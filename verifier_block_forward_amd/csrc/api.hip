@@ -217,7 +217,11 @@ struct SegList {
         s.out_stride = (long long)pl.ksplit * 16 * N;
         a.total_units += (slots - 1) * plan_units(pl);
     }
-    void launch(hipStream_t st) { launch_gemm(a, nbmax, st); }
+    int launch(hipStream_t st) {
+        if (!launch_gemm(a, nbmax, st))
+            return fail(DBF_EINVAL, "internal: a split-K projection launch with two split tiles per segment");
+        return DBF_OK;
+    }
 };
 
 int validate_config(const dbf_config *c) {
@@ -461,7 +465,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             launch_colsum2(a, t, st);
             SegList sl(R);
             sl.add(w->fc, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
-            sl.launch(st);
+            CHECK(sl.launch(st));
             ColArgs h = col();
             h.M = R;
             h.p0 = at<float>(ws, p.p_in0);
@@ -496,7 +500,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         SegList sl(M);
         sl.add(w->eh_embed, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
         sl.add(w->eh_hidden, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
-        sl.launch(st);
+        CHECK(sl.launch(st));
         ColArgs x = col();
         x.M = M;
         x.p0 = at<float>(ws, p.p_in0);
@@ -546,7 +550,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 sl.add(L.wv, kt, H, p.v, pv, xs_blk);
             }
             if (c.has_attn_gate) sl.add(L.attn_gate, qt, H, p.g, pg, xs_blk);
-            sl.launch(st);
+            CHECK(sl.launch(st));
         }
         void *ck = (char *)cache->k + l * layer_stride;
         void *cv = (char *)cache->v + l * layer_stride;
@@ -634,7 +638,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 SegList sl(M);
                 sl.add(L.ffn_gate, p.I, H, p.gate, at<float>(ws, p.p_gate), xs_blk);
                 sl.add(L.ffn_up, p.I, H, p.up, at<float>(ws, p.p_up), xs_blk);
-                sl.launch(st);
+                CHECK(sl.launch(st));
                 SwigluArgs sa{};
                 sa.pg = at<float>(ws, p.p_gate);
                 sa.pu = at<float>(ws, p.p_up);
@@ -650,7 +654,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 launch_swiglu(sa, st);
                 SegList sd(M);
                 sd.add(L.ffn_down, H, p.I, p.down, at<float>(ws, p.p_down), xs_ff);
-                sd.launch(st);
+                CHECK(sd.launch(st));
             }
         } else {
             // MoE: router + shared-expert projections, routing, grouped experts, combine
@@ -663,7 +667,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 sl.add(L.sh_gate_inp, 1, H, p.sgi, at<float>(ws, p.p_sgi), xs_blk);
                 sl.add(L.sh_gate, Is, H, p.shg, at<float>(ws, p.p_shg), xs_blk);
                 sl.add(L.sh_up, Is, H, p.shg, at<float>(ws, p.p_shu), xs_blk);
-                sl.launch(st);
+                CHECK(sl.launch(st));
             }
             {
                 MoeRouteArgs ra{};
@@ -693,7 +697,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                                slot_e, nsl);
                 sl.add_grouped(L.exp_up, Ie, H, p.eg, at<float>(ws, p.p_eu), xs_blk, 0, p.max_slots,
                                slot_e, nsl);
-                sl.launch(st);
+                CHECK(sl.launch(st));
             }
             {
                 MoeSwigluArgs sa{};
@@ -721,7 +725,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 sl.add_grouped(L.exp_down, H, Ie, p.ed, at<float>(ws, p.p_ed), at<uint16_t>(ws, p.xs_e),
                                (long long)(split_tile_bytes(Ie) / 2), p.max_slots, slot_e, nsl);
                 sl.add(L.sh_down, H, Is, p.shd, at<float>(ws, p.p_shd), at<uint16_t>(ws, p.xs_sh));
-                sl.launch(st);
+                CHECK(sl.launch(st));
             }
         }
         {

@@ -158,8 +158,11 @@ constexpr int SPLITK_W_LONG = 8;
 constexpr int SPLITK_W_LONG_STEPS = 8;
 constexpr int SPLITK_W_SLOTS = 2;
 constexpr int SPLITK_W = 4;
+static_assert(SPLITK_W_LONG_STEPS <= GEMM_LONG_SLICE, "long slices always take SPLITK_W_LONG waves");
 
-template <int NA, int NB, int PIPE, int W>
+// One split tile per segment: the launches that also project the context rows (a
+// second split tile) are LDS-staged.
+template <int NA, int PIPE, int W>
 __global__ __launch_bounds__(64 * W) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
     // scalar wave index: the unit, the segment lookup and the segment's fields are
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_splitk(GemmArgs args) {
     }
     const int tile = local % sg.tiles;
     const int ks = local / sg.tiles;
-    const int N = sg.N, K = sg.K, mr0 = sg.mrows[0], mr1 = sg.mrows[1];
+    const int N = sg.N, K = sg.K, mr0 = sg.mrows[0];
     const int S = (K + 31) >> 5;
     const int s0 = ks * sg.kslice_steps;
     int s1 = s0 + sg.kslice_steps;
@@ -222,34 +225,13 @@ __global__ __launch_bounds__(64 * W) void k_gemm_splitk(GemmArgs args) {
             wrow[a] = Wbase + (size_t)row * K + 8 * g;
         }
     }
-    const uint16_t *xs[NB];
-    xs[0] = xsb0;
-    if (NB > 1) xs[NB - 1] = sg.nb > 1 ? sg.xs1 : xsb0;
-
-    f32x4 acc[NA][NB];
+    const uint16_t *xs[1] = {xsb0};
+    const int mrs[1] = {mr0};
+    f32x4 acc[NA][1];
 #pragma unroll
-    for (int a = 0; a < NA; a++)
-#pragma unroll
-        for (int b = 0; b < NB; b++) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (NB == 2 && sg.nb == 1) {
-        const uint16_t *xs1[1] = {xsb0};
-        f32x4 acc1[NA][1];
-#pragma unroll
-        for (int a = 0; a < NA; a++) acc1[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int mrs1[1] = {mr0};
-        skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs1, mrs1, K, s0, s1, lane, acc1);
-#pragma unroll
-        for (int a = 0; a < NA; a++) acc[a][0] = acc1[a][0];
-    } else {
-        int mrs[NB];
-        mrs[0] = mr0;
-        if (NB > 1) mrs[NB - 1] = mr1;
-        skinny_mainloop<NA, NB, PIPE>(wrow, wstep, sg.tiled, xs, mrs, K, s0, s1, lane, acc);
-    }
-
-    const int nb = NB == 1 ? 1 : sg.nb;
-    store_partials<NA, NB>(outb + (size_t)ks * 16 * nb * N, N, nb, row0, lane, mr0, mr1, acc);
+    for (int a = 0; a < NA; a++) acc[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs, mrs, K, s0, s1, lane, acc);
+    store_partials<NA, 1>(outb + (size_t)ks * 16 * N, N, 1, row0, lane, mr0, mr0, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -551,53 +533,62 @@ GemmPlan gemm_plan_lds(int N, int K, int target_units, int nbmax) {
     return p;
 }
 
-template <int NA, int NB, int W>
-static void go_splitk(const GemmArgs &a, bool long_slices, hipStream_t s) {
+template <int PIPE, int W>
+static void go_splitk(const GemmArgs &a, hipStream_t s) {
     const dim3 grid((a.total_units + W - 1) / W), block(64 * W);
-    if (long_slices)
-        launch_k(PROF_PROJ, "k_gemm_splitk(long)", (k_gemm_splitk<NA, NB, GEMM_PIPE_LONG, W>), grid, block, 0, s, a);
-    else
-        launch_k(PROF_PROJ, "k_gemm_splitk", (k_gemm_splitk<NA, NB, GEMM_PIPE, W>), grid, block, 0, s, a);
+    launch_k(PROF_PROJ, PIPE == GEMM_PIPE_LONG ? "k_gemm_splitk(long)" : "k_gemm_splitk",
+             (k_gemm_splitk<GEMM_NA, PIPE, W>), grid, block, 0, s, a);
 }
 
-template <int NA, int NB>
-static void go(const GemmArgs &a, hipStream_t s) {
-    if (a.lds_x) {  // total_units counts workgroups
-        size_t lds = 0;
-        for (int i = 0; i < a.nseg; i++) {
-            const size_t b = (size_t)(NB > 1 ? a.seg[i].nb : 1) * a.seg[i].kslice_steps * 2048;
-            if (b > lds) lds = b;
-        }
-        int steps = 0;
-        for (int i = 0; i < a.nseg; i++)
-            if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
-        if (steps <= LPIPE_SHORT_MAX)
-            launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB, LPIPE_SHORT>), dim3(a.total_units), dim3(256), lds, s, a);
-        else
-            launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<NA, NB, LPIPE>), dim3(a.total_units), dim3(256), lds, s, a);
-    } else {
-        int steps = 0;
-        bool slots = false;
-        for (int i = 0; i < a.nseg; i++) {
-            if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
-            slots |= a.seg[i].slots > 0;
-        }
-        const bool lg = steps >= GEMM_LONG_SLICE;
-        if (slots)
-            go_splitk<NA, NB, SPLITK_W_SLOTS>(a, lg, s);
-        else if (steps >= SPLITK_W_LONG_STEPS)
-            go_splitk<NA, NB, SPLITK_W_LONG>(a, lg, s);
-        else
-            go_splitk<NA, NB, SPLITK_W>(a, lg, s);
+// NB split tiles per segment at most. With two, slices are at most LDS_X_STEPS_NB2
+// steps, so those launches always take the short-slice ring.
+template <int NB>
+static void go_lds(const GemmArgs &a, hipStream_t s) {
+    static_assert(NB == 1 || LDS_X_STEPS_NB2 <= LPIPE_SHORT_MAX, "two-tile slices take the short ring");
+    size_t lds = 0;
+    int steps = 0;
+    for (int i = 0; i < a.nseg; i++) {
+        const size_t b = (size_t)(NB > 1 ? a.seg[i].nb : 1) * a.seg[i].kslice_steps * 2048;
+        if (b > lds) lds = b;
+        if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
     }
+    const dim3 grid(a.total_units);  // total_units counts workgroups
+    if (NB == 2 || steps <= LPIPE_SHORT_MAX)
+        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<GEMM_NA, NB, LPIPE_SHORT>), grid, dim3(256), lds, s, a);
+    else
+        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<GEMM_NA, 1, LPIPE>), grid, dim3(256), lds, s, a);
 }
 
-void launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s) {
-    if (a.total_units <= 0) return;
-    if (nbmax == 1)
-        go<GEMM_NA, 1>(a, s);
-    else
-        go<GEMM_NA, 2>(a, s);
+bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s) {
+    if (a.total_units <= 0) return true;
+    if (a.lds_x) {
+        if (nbmax == 1)
+            go_lds<1>(a, s);
+        else
+            go_lds<2>(a, s);
+        return true;
+    }
+    if (nbmax > 1) return false;  // the split-K kernel reads one split tile per segment
+    int steps = 0;
+    bool slots = false;
+    for (int i = 0; i < a.nseg; i++) {
+        if (a.seg[i].kslice_steps > steps) steps = a.seg[i].kslice_steps;
+        slots |= a.seg[i].slots > 0;
+    }
+    const bool lg = steps >= GEMM_LONG_SLICE;
+    if (slots) {
+        if (lg)
+            go_splitk<GEMM_PIPE_LONG, SPLITK_W_SLOTS>(a, s);
+        else
+            go_splitk<GEMM_PIPE, SPLITK_W_SLOTS>(a, s);
+    } else if (lg) {
+        go_splitk<GEMM_PIPE_LONG, SPLITK_W_LONG>(a, s);
+    } else if (steps >= SPLITK_W_LONG_STEPS) {
+        go_splitk<GEMM_PIPE, SPLITK_W_LONG>(a, s);
+    } else {
+        go_splitk<GEMM_PIPE, SPLITK_W>(a, s);
+    }
+    return true;
 }
 
 // ---------------------------------------------------------------------------

@@ -82,7 +82,8 @@ inline int plan_units(const GemmPlan &p) {
     return p.lds ? ((p.tiles + 3) / 4) * p.ksplit : p.tiles * p.ksplit;
 }
 
-void launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s);
+// false (nothing launched) for a split-K launch with two split tiles per segment
+bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Whole-K projection with the residual epilogue: one workgroup owns 16 or 32 output
