@@ -121,6 +121,14 @@ def test_block_query_tile_variants(orc, cfg):
     run_case(orc, cfg)
 
 
+# A plain split-K launch whose k-slices reach 25 steps or more takes the two-stage
+# ring with 8-wave workgroups. At H = 4096 with four target hidden states the fc
+# projection (4096 x 16384) is planned as 128 row-tile pairs x 16 slices of 32 steps.
+def test_block_long_plain_slices(orc):
+    run_case(orc, small(name="fc_long_slices", hidden=4096, n_target_hidden=4, n_layers=1,
+                        intermediate=512, n_q_heads=2, n_kv_heads=1, head_dim=64, M=3, R=2, C=40))
+
+
 def test_block_c0(orc):
     run_case(orc, configs.C0)
 
