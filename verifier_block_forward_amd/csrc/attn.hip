@@ -744,14 +744,16 @@ static void launch_combine_hd(const CombineArgs &a, hipStream_t s) {
     const int per256 = (a.n_chunks + g256 - 1) / g256;
     const int per1024 = (a.n_chunks + g1024 - 1) / g1024;
     const dim3 grid(a.M, a.nq);
-    if (per256 <= 4)
+    if (per256 <= 4) {
         launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 256, 4>, grid, dim3(256), 0, s, a);
-    else if (per256 <= 8)
+    } else if (per256 <= 8) {
         launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 256, 8>, grid, dim3(256), 0, s, a);
-    else if (per1024 <= 8)
+    } else if (per1024 <= 8) {
         launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 1024, 8>, grid, dim3(1024), 0, s, a);
-    else
+    } else if constexpr ((ATT_CHUNKS_MAX + g1024 - 1) / g1024 > 8) {
+        // only 256-dim heads reach 16 chunks per thread within ATT_CHUNKS_MAX chunks
         launch_k(PROF_ATTN, "k_attn_combine", k_attn_combine<HD, 1024, 16>, grid, dim3(1024), 0, s, a);
+    }
 }
 
 void launch_attn_combine(const CombineArgs &a, hipStream_t s) {
