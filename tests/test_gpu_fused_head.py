@@ -66,7 +66,9 @@ def run_pair(cfg, tiled=False, eos=None):
     for k in ha:
         assert np.array_equal(ha[k], hb[k]), f"{cfg.name}: fused {k} differs"
     assert kv2.seq_len == kv.seq_len
-    assert np.array_equal(ck.cpu().numpy(), ck2.cpu().numpy())
+    bits = (lambda c: c.view(t.int16)) if ck.dtype == t.bfloat16 else (lambda c: c)
+    assert np.array_equal(bits(ck).cpu().numpy(), bits(ck2).cpu().numpy())
+    assert np.array_equal(bits(cv).cpu().numpy(), bits(cv2).cpu().numpy())
     if not eos:
         assert int(hb["result"][0]) == j  # the seeded number of matching drafts
     return hb

@@ -65,3 +65,16 @@ def test_block_random_shape(orc, cfg):
         run_moe_case(orc, cfg)
     else:
         run_case(orc, cfg)
+
+
+# The shared head and the accept walk fused into the block call, against the
+# separate calls, bit for bit, on the first twelve of those shapes that have drafts
+# to check (MTP, or DFlash with two or more block rows); every third in the tiled
+# weight layout.
+FUSED = [c for c in CONFIGS if c.kind == "mtp" or c.M >= 2][:12]
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=lambda c: c.name)
+def test_fused_head_random_shape(cfg):
+    from tests.test_gpu_fused_head import run_pair
+    run_pair(cfg, tiled=CONFIGS.index(cfg) % 3 == 0)
