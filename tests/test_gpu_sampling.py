@@ -59,8 +59,16 @@ def gpu_sample(z, u, T):
     return tok.cpu().numpy(), prob.cpu().numpy()
 
 
+def _random_vmt(n=8, seed=4242):
+    """Seeded (V, M, T): V log-uniform over 2 .. 300,000 (segment counts 1 .. 256 and
+    segments past 1024 values), M in 1 .. 16, T in 0.5 .. 2."""
+    rng = np.random.default_rng(seed)
+    return [(int(np.exp(rng.uniform(np.log(2), np.log(300000)))), int(rng.integers(1, 17)),
+             round(float(rng.uniform(0.5, 2.0)), 3)) for _ in range(n)]
+
+
 @pytest.mark.parametrize("V,M,T", [(1000, 5, 1.0), (1025, 16, 0.7), (5000, 3, 1.6), (248320, 16, 1.0),
-                                   (262151, 4, 0.7), (1, 2, 1.0)])
+                                   (262151, 4, 0.7), (1, 2, 1.0)] + _random_vmt())
 def test_sample_tokens_match_the_oracle(V, M, T):
     print(f"\n[sample] V={V} M={M} T={T}", flush=True)
     rng = np.random.default_rng(V + M)
