@@ -38,8 +38,17 @@ def check_argmax(name, am, lg_oracle, am_o, mg_o):
             assert z[am[m]] >= z.max() - 1e-2, f"{name} row {m}: argmax {am[m]} not within 1e-2 of the max"
 
 
+def _random_mhv(n=6, seed=5151):
+    """Seeded (M, H, V): M in 1 .. 16, H a multiple of 8 in 8 .. 1024, V log-uniform
+    over 1 .. 300,000."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 17)), 8 * int(rng.integers(1, 129)),
+             int(np.exp(rng.uniform(0.0, np.log(300000))))) for _ in range(n)]
+
+
 @pytest.mark.parametrize("M,H,V", [(3, 264, 1000), (4, 256, 4096), (16, 200, 777), (1, 8, 65),
-                                   (16, 2816, 262144), (1, 5120, 248320), (4, 2048, 248320)])
+                                   (16, 2816, 262144), (1, 5120, 248320), (4, 2048, 248320)]
+                         + _random_mhv())
 @pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
 def test_lm_head_argmax_parity(orc, M, H, V, tiled):
     print(f"\n[lm_head] M={M} H={H} V={V} tiled={tiled}", flush=True)
