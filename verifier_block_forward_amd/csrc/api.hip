@@ -89,8 +89,9 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.rd = c.rotary_dim > 0 ? c.rotary_dim : c.head_dim;
     // Launch shapes measured on MI355X at the benchmark sizes: the wide projections
     // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one,
-    // and the MTP eh halves) stream faster with the activation slice in LDS; the
-    // down and DFlash fc projections with the plain split-K kernel, O whole-K.
+    // and the MTP eh halves) and the 16-row down projection stream faster with the
+    // activation slice in LDS; the DFlash fc and one-row MTP down projections with
+    // the plain split-K kernel, O whole-K.
     p.in = c.kind == DBF_KIND_MTP ? gemm_plan_lds(p.H, p.Kin, TARGET_UNITS / 4, 1)
                                   : gemm_plan(p.H, p.Kin, TARGET_UNITS);
     const int nbq = R > 0 ? 2 : 1;  // K/V also project the context rows
@@ -101,10 +102,13 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     if (c.ffn_kind == DBF_FFN_DENSE) {
         p.gate = gemm_plan_lds(p.I, p.H, TARGET_UNITS / 4, 1);
         p.up = p.gate;
-        // with one to a few block rows the partials are small, so the long down
+        // With one to a few block rows (MTP) the partials are small, so the long down
         // projection takes about twice the waves, capped at 23 slices: its consumer
-        // then still sums them in one batch of loads
-        p.down = gemm_plan(p.H, p.I, c.kind == DBF_KIND_MTP ? 23 * ((p.H + 31) / 32) : TARGET_UNITS);
+        // then still sums them in one batch of loads. The DFlash down projection is
+        // LDS-staged with the full target (at H 2816, I 8448: 22 slices of 12 steps,
+        // 484 workgroups; 14 slices of 20 steps were slower than split-K).
+        p.down = c.kind == DBF_KIND_MTP ? gemm_plan(p.H, p.I, 23 * ((p.H + 31) / 32))
+                                        : gemm_plan_lds(p.H, p.I, TARGET_UNITS, 1);
     }
     const int rows_kv = R > 0 ? 32 : 16;
     size_t off = 0;
