@@ -66,7 +66,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int H, qt, kt, I, Kin, rd;
     GemmPlan in, q, k, v, g, gate, up, down;
-    size_t xres, x1, xs_blk, xs_T, xs_hctx, xs_h, xs_o, xs_ff, qbuf, gbuf, attn;
+    size_t xres, x1, xs_blk, xs_hctx, xs_h, xs_o, xs_ff, qbuf, gbuf, attn;
     size_t ssp_x, ssp_x1, ssp_ctx, ssp_e, ssp_h;
     int ncb, ncb16;  // row-scale partials per row: 64-column (row kernels) and 16-column (O epilogue)
     size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_gate, p_up, p_down;
@@ -121,7 +121,6 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.xres = take((size_t)DBF_MAX_M * p.H * f);
     p.x1 = take((size_t)DBF_MAX_M * p.H * f);
     p.xs_blk = take(split_tile_bytes(p.H));
-    p.xs_T = take(split_tile_bytes(p.Kin));
     p.xs_hctx = take(split_tile_bytes(p.H));
     p.xs_h = take(split_tile_bytes(p.H));
     p.xs_o = take(split_tile_bytes(p.qt));
@@ -234,10 +233,16 @@ struct SegList {
         s.out_stride = (long long)pl.ksplit * 16 * N;
         a.total_units += (slots - 1) * plan_units(pl);
     }
+    // the launch's one segment reads F32 rows instead of its split tile
+    void f32_source(const GemmF32Src &s) {
+        a.xf = s;
+        a.xf_on = 1;
+    }
     int launch(hipStream_t st) {
         if (bad) return fail(DBF_EINVAL, "internal: projection launch: %s", bad);
         if (!launch_gemm(a, nbmax, st))
-            return fail(DBF_EINVAL, "internal: a split-K projection launch with two split tiles per segment");
+            return fail(DBF_EINVAL, "internal: a projection launch its kernels do not take (two split tiles "
+                                    "or an F32 source on anything but one plain split-K segment)");
         return DBF_OK;
     }
 };
@@ -432,7 +437,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     const float eps = (float)c.rms_eps;
     const long long P0 = cache->seq_len;
     float *xres = at<float>(ws, p.xres), *x1 = at<float>(ws, p.x1);
-    uint16_t *xs_blk = at<uint16_t>(ws, p.xs_blk), *xs_T = at<uint16_t>(ws, p.xs_T);
+    uint16_t *xs_blk = at<uint16_t>(ws, p.xs_blk);
     uint16_t *xs_hctx = at<uint16_t>(ws, p.xs_hctx), *xs_h = at<uint16_t>(ws, p.xs_h);
     uint16_t *xs_o = at<uint16_t>(ws, p.xs_o), *xs_ff = at<uint16_t>(ws, p.xs_ff);
     float *qbuf = at<float>(ws, p.qbuf), *gbuf = at<float>(ws, p.gbuf);
@@ -466,23 +471,22 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
         a.ssp_out = ssp_x;
         if (R == 0) launch_colsum(a, st);
         if (R > 0) {
-            // h_ctx = RMSNorm(T fc^T, hidden_norm): split T (in the same launch as the
-            // block rows), project, split(proj (.) hidden_norm)
-            ColArgs t = col();
-            t.M = R;
-            t.H = p.Kin;
-            t.base = io->ctx;
-            t.ldb = p.Kin;
-            if (!io->ctx) {  // gather the captured target layers on the device
-                for (int i = 0; i < c.n_target_hidden; i++) t.gsrc[i] = io->ctx_layers[i];
-                t.gH = H;
-                t.gld = io->ctx_ld;
-                t.grow0 = io->ctx_row0;
-            }
-            t.xs = xs_T;
-            launch_colsum2(a, t, st);
+            // h_ctx = RMSNorm(T fc^T, hidden_norm): the projection reads the F32 rows
+            // of T (or gathers the captured target layers) and splits them as it
+            // goes; then the block rows and split(proj (.) hidden_norm) in one launch
             SegList sl(R);
-            sl.add(w->fc, H, p.Kin, p.in, at<float>(ws, p.p_in0), xs_T);
+            sl.add(w->fc, H, p.Kin, p.in, at<float>(ws, p.p_in0), nullptr);
+            GemmF32Src src{};
+            if (io->ctx) {
+                src.xf = io->ctx;
+                src.xf_ld = p.Kin;
+            } else {
+                for (int i = 0; i < c.n_target_hidden; i++) src.xg[i] = io->ctx_layers[i];
+                src.xg_cols = H;
+                src.xg_ld = io->ctx_ld;
+                src.xg_row0 = io->ctx_row0;
+            }
+            sl.f32_source(src);
             CHECK(sl.launch(st));
             ColArgs h = col();
             h.M = R;
@@ -492,7 +496,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
             h.w = (const float *)w->hidden_norm.data;
             h.xs = xs_hctx;
             h.ssp_out = ssp_ctx;
-            launch_colsum(h, st);
+            launch_colsum2(a, h, st);
         }
     } else {
         // x = RMSNorm(e, enorm) eh_embed^T + RMSNorm(h, hnorm) eh_hidden^T (eps 1e-6)

@@ -74,36 +74,7 @@ int attn_qtiles(int hd, int nq_group, bool kv_bf16) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2_att __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_att __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_att __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_split __attribute__((ext_vector_type(4)));
-
-// Two F32 values split into BF16 hi (round to nearest even) and lo = BF16(x - hi),
-// each pair packed in one dword (first value in the low half). Converting the
-// pair as a vector makes one v_cvt_pk_bf16_f32 per pair instead of one per value
-// plus a repack.
-__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo) {
-    const f32x2_att f = {a, b};
-    const bf16x2_att h = __builtin_convertvector(f, bf16x2_att);
-    const f32x2_att hf = __builtin_convertvector(h, f32x2_att);
-    const bf16x2_att l = __builtin_convertvector(f - hf, bf16x2_att);
-    hi = __builtin_bit_cast(unsigned, h);
-    lo = __builtin_bit_cast(unsigned, l);
-}
-
-__device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo) {
-    u32x4_split h, l;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        unsigned a, b;
-        split2(v[2 * j], v[2 * j + 1], a, b);
-        h[j] = a;
-        l[j] = b;
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
 
 // four values (the 4-key operands of the P*V product) split into hi/lo
 __device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, s16x4 &hi, s16x4 &lo) {
@@ -709,13 +680,16 @@ __global__ __launch_bounds__(NT) void k_attn_combine(CombineArgs a) {
     if (grp != 0) return;
     float o[4];
     {
+        // unrolled 8 at a time: a full unroll over the 32 or 64 groups of the
+        // 1024-thread blocks held every group's record in registers at once and
+        // spilled (the additions keep their order either way)
         float mx = -INFINITY;
-#pragma unroll
+#pragma unroll 8
         for (int q = 0; q < ngrp; q++)
             if (sm_l[q * tpg + d4] > 0.f) mx = fmaxf(mx, sm_m[q * tpg + d4]);
         f32x4 osum = {0.f, 0.f, 0.f, 0.f};
         float lsum = 0.f;
-#pragma unroll
+#pragma unroll 8
         for (int q = 0; q < ngrp; q++) {
             const float lq = sm_l[q * tpg + d4];
             const float e = lq > 0.f ? exp2f(sm_m[q * tpg + d4] - mx) : 0.f;

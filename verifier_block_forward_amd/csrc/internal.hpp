@@ -51,6 +51,37 @@ __device__ __forceinline__ size_t split_index(int r, int k, int h) {
     return ((size_t)(s * 2 + h) * 64 + (g * 16 + r)) * 8 + j;
 }
 
+typedef float f32x2_split __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_split __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_split __attribute__((ext_vector_type(4)));
+
+// Two F32 values split into BF16 hi (round to nearest even) and lo = BF16(x - hi),
+// each pair packed in one dword (first value in the low half): the same values as
+// split_store, with one v_cvt_pk_bf16_f32 per pair instead of one per value plus
+// a repack.
+__device__ __forceinline__ void split2(float a, float b, unsigned &hi, unsigned &lo) {
+    const f32x2_split f = {a, b};
+    const bf16x2_split h = __builtin_convertvector(f, bf16x2_split);
+    const f32x2_split hf = __builtin_convertvector(h, f32x2_split);
+    const bf16x2_split l = __builtin_convertvector(f - hf, bf16x2_split);
+    hi = __builtin_bit_cast(unsigned, h);
+    lo = __builtin_bit_cast(unsigned, l);
+}
+
+// eight consecutive values (one lane's run of a k-step) into hi and lo operands
+__device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo) {
+    u32x4_split h, l;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        unsigned a, b;
+        split2(v[2 * j], v[2 * j + 1], a, b);
+        h[j] = a;
+        l[j] = b;
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 __device__ __forceinline__ void split_store(uint16_t *tile, int r, int k, float a) {
     uint16_t hi = f32_to_bf16(a);
     float rem = a - bf16_to_f32(hi);

@@ -53,16 +53,31 @@ struct GemmSeg {
     int pad_;
 };
 
+// F32 activation rows read by a split-K launch in place of a split tile, split
+// hi/lo as they are consumed: row m, column k is xf[m * xf_ld + k], or, with xf
+// null (the captured target layers gathered), xg[k / xg_cols][(xg_row0 + m) *
+// xg_ld + k % xg_cols]. xg_cols is a multiple of 8, so a lane's 8-column run lies
+// in one source.
+struct GemmF32Src {
+    const float *xf;
+    long long xf_ld;
+    const float *xg[8];
+    long long xg_ld;
+    int xg_cols, xg_row0;
+};
+
 struct GemmArgs {
     GemmSeg seg[GEMM_MAXSEG];
     int nseg;
     int total_units;  // wave units (lds_x = 0) or workgroup units (lds_x = 1)
     int lds_x;        // 1: k_gemm_lds (activation slice staged in LDS)
+    int xf_on;        // 1: the (single, plain, split-K) segment reads xf, not xs0
+    GemmF32Src xf;
 };
 
-// Work decomposition of one segment: rows per wave unit = 16 * na; lds selects
+// Work decomposition of one segment: rows per wave unit = 16 * GEMM_NA; lds selects
 // the kernel with the activation slice staged in LDS (units are then workgroups of
-// four row tiles). Segments of one launch share na and lds.
+// four row tiles). Segments of one launch share lds.
 // Row tiles (16 weight rows each) per wave in every projection launch: two measured
 // best in both the split-K and the LDS-staged kernels (four, with twice the bytes
 // in flight per wave, were slower in each).
@@ -82,7 +97,8 @@ inline int plan_units(const GemmPlan &p) {
     return p.lds ? ((p.tiles + 3) / 4) * p.ksplit : p.tiles * p.ksplit;
 }
 
-// false (nothing launched) for a split-K launch with two split tiles per segment
+// false (nothing launched) for a split-K launch with two split tiles per segment,
+// or an F32 activation source on anything but one plain split-K segment
 bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
@@ -157,11 +173,6 @@ struct ColArgs {
     int V;
     const float *base;        // [M][ldb] base rows, or null
     int ldb;
-    // gather mode (base == null, gsrc[0] set): column k of row m is
-    // gsrc[k / gH][(grow0 + m) * gld + k % gH] (captured target layers)
-    const float *gsrc[8];
-    int gH;
-    long long gld, grow0;
     const float *p0;          // split-K partials [ks0][rows0][H], or null
     int ks0, rows0;
     const float *ssp0;        // row-scale source for set 0 ([16][ncb_in]) or null (scale 1)

@@ -25,8 +25,8 @@ __device__ __forceinline__ int colsum_row_groups(const ColArgs &a) {
 }
 
 // Input modes: SRC_BASE when the rows come from `base` (or are zero), SRC_ANY for
-// the token gather and the captured-layer gather. The base-only form has no branch
-// joins between its independent loads, so the compiler issues them together.
+// the token gather. The base-only form has no branch joins between its independent
+// loads, so the compiler issues them together.
 constexpr int SRC_ANY = 0, SRC_BASE = 1;
 
 template <int SRC>
@@ -65,9 +65,6 @@ __device__ __forceinline__ void colsum_body(const ColArgs &a) {
             tok = a.tokens[m];
         } else if (a.base) {
             bv = a.base[(size_t)m * a.ldb + k];
-        } else if (a.gsrc[0]) {
-            const int t = k / a.gH;
-            bv = a.gsrc[t][(size_t)(a.grow0 + m) * a.gld + (k - t * a.gH)];
         }
         if (a.xs && a.w) wk = a.w[k];
     }
@@ -84,7 +81,7 @@ __device__ __forceinline__ void colsum_body(const ColArgs &a) {
                 const int t = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
                 v = bf16_to_f32(a.embed[(size_t)t * a.H + k]);
             } else {
-                v = bv;  // base or gathered value (0 when neither is given)
+                v = bv;  // base value (0 when there is none)
             }
             if (a.p0) v += sc0 * s0;
             if (a.p1) v += sc1 * s1;
@@ -114,7 +111,7 @@ static dim3 colsum_grid(const ColArgs &a) {
 }
 
 void launch_colsum(const ColArgs &a, hipStream_t s) {
-    if (!a.tokens && !a.gsrc[0])
+    if (!a.tokens)
         launch_k(PROF_ROWS, "k_colsum", k_colsum<SRC_BASE>, colsum_grid(a), dim3(256), 0, s, a);
     else
         launch_k(PROF_ROWS, "k_colsum", k_colsum<SRC_ANY>, colsum_grid(a), dim3(256), 0, s, a);
