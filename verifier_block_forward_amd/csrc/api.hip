@@ -88,12 +88,12 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.Kin = c.kind == DBF_KIND_DFLASH ? c.n_target_hidden * c.hidden : c.hidden;
     p.rd = c.rotary_dim > 0 ? c.rotary_dim : c.head_dim;
     // Launch shapes measured on MI355X at the benchmark sizes: the wide projections
-    // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one,
-    // and the MTP eh halves) and the 16-row down projection stream faster with the
-    // activation slice in LDS; the DFlash fc and one-row MTP down projections with
-    // the plain split-K kernel, O whole-K.
-    p.in = c.kind == DBF_KIND_MTP ? gemm_plan_lds(p.H, p.Kin, TARGET_UNITS / 4, 1)
-                                  : gemm_plan(p.H, p.Kin, TARGET_UNITS);
+    // of the normalized hidden rows (Q/K/V/gate in one launch, FFN gate+up in one),
+    // the input projections (MTP eh halves; DFlash fc, which stages its F32 context
+    // rows itself) and the 16-row down projection stream faster with the activation
+    // slice in LDS; the one-row MTP down projections with the plain split-K kernel,
+    // O whole-K.
+    p.in = gemm_plan_lds(p.H, p.Kin, TARGET_UNITS / 4, 1);
     const int nbq = R > 0 ? 2 : 1;  // K/V also project the context rows
     p.q = gemm_plan_lds(p.qt, p.H, TARGET_UNITS / 4, nbq);
     p.k = gemm_plan_lds(p.kt, p.H, TARGET_UNITS / 4, nbq);
@@ -242,7 +242,7 @@ struct SegList {
         if (bad) return fail(DBF_EINVAL, "internal: projection launch: %s", bad);
         if (!launch_gemm(a, nbmax, st))
             return fail(DBF_EINVAL, "internal: a projection launch its kernels do not take (two split tiles "
-                                    "or an F32 source on anything but one plain split-K segment)");
+                                    "or an F32 source on anything but one plain LDS-staged segment)");
         return DBF_OK;
     }
 };

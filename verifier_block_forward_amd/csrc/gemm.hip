@@ -150,57 +150,6 @@ __device__ __forceinline__ const float *f32_src_at(const GemmF32Src &s, int m, i
     return b + (size_t)(s.xg_row0 + m) * s.xg_ld + (k - t * s.xg_cols);
 }
 
-// skinny_mainloop for one tile of F32 activation rows read in place: lane
-// (r16, g) loads columns 32*step + 8g .. +7 of row r16 and splits them hi/lo
-// (split8: the values a split pass would have stored) when the stage is consumed.
-// The run is read element by element, so the rows need only 4-byte alignment; the
-// compiler issues it as 16-byte loads, which gfx950 serves at any 4-byte address.
-// Rows at or past mr and columns past K read as zeros.
-template <int NA, int PIPE>
-__device__ __forceinline__ void skinny_mainloop_f32(const uint16_t *const wrow[NA], int wstep, bool tiled,
-                                                    const GemmF32Src &src, int mr, int K, int s0, int s1,
-                                                    int lane, f32x4 acc[NA][1]) {
-    const int g = lane >> 4, r16 = lane & 15;
-    bf16x8 wb[PIPE][NA];
-    float xv[PIPE][8];
-    const int n = s1 - s0;
-#define DBF_LOAD_STAGE_F32(u, step)                                             \
-    do {                                                                        \
-        const int sc_ = (step) < s1 ? (step) : s1 - 1;                          \
-        const int xc_ = 32 * sc_ + 8 * g;                                       \
-        const bool in_ = tiled || xc_ < K;                                      \
-        const int col_ = in_ ? wstep * sc_ : 0;                                 \
-        _Pragma("unroll") for (int a = 0; a < NA; a++) {                        \
-            const bf16x8 v_ = ldw16(wrow[a] + col_);                            \
-            wb[u][a] = in_ ? v_ : zero8();                                      \
-        }                                                                       \
-        if (r16 < mr && xc_ < K) {                                              \
-            const float *x_ = f32_src_at(src, r16, xc_);                        \
-            _Pragma("unroll") for (int j = 0; j < 8; j++) xv[u][j] = x_[j];     \
-        } else {                                                                \
-            _Pragma("unroll") for (int j = 0; j < 8; j++) xv[u][j] = 0.f;       \
-        }                                                                       \
-    } while (0)
-#pragma unroll
-    for (int u = 0; u < PIPE; u++) DBF_LOAD_STAGE_F32(u, s0 + u);
-    for (int base = 0; base < n; base += PIPE) {
-#pragma unroll
-        for (int u = 0; u < PIPE; u++) {
-            if (base + u < n) {
-                bf16x8 xh, xl;
-                split8(xv[u], xh, xl);
-#pragma unroll
-                for (int a = 0; a < NA; a++) {
-                    acc[a][0] = MFMA(wb[u][a], xh, acc[a][0]);
-                    acc[a][0] = MFMA(wb[u][a], xl, acc[a][0]);
-                }
-            }
-            DBF_LOAD_STAGE_F32(u, s0 + base + u + PIPE);
-        }
-    }
-#undef DBF_LOAD_STAGE_F32
-}
-
 // Stages in flight per wave, chosen per launch from its longest k-slice: 3 for
 // slices of up to 24 steps (the 16-row down and input projections: 12 and 20 steps;
 // the one-row 17408-deep down: 24; 2 and 4 were slower), 2 for slices of
@@ -223,8 +172,8 @@ constexpr int SPLITK_W = 4;
 static_assert(SPLITK_W_LONG_STEPS <= GEMM_LONG_SLICE, "long slices always take SPLITK_W_LONG waves");
 
 // One split tile per segment: the launches that also project the context rows (a
-// second split tile) are LDS-staged. F32X: the activations are args.xf's F32 rows.
-template <int NA, int PIPE, int W, bool F32X>
+// second split tile) are LDS-staged.
+template <int NA, int PIPE, int W>
 __global__ __launch_bounds__(64 * W) void k_gemm_splitk(GemmArgs args) {
     const int lane = threadIdx.x & 63;
     // scalar wave index: the unit, the segment lookup and the segment's fields are
@@ -290,13 +239,9 @@ __global__ __launch_bounds__(64 * W) void k_gemm_splitk(GemmArgs args) {
     f32x4 acc[NA][1];
 #pragma unroll
     for (int a = 0; a < NA; a++) acc[a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (F32X) {
-        skinny_mainloop_f32<NA, PIPE>(wrow, wstep, sg.tiled, args.xf, mr0, K, s0, s1, lane, acc);
-    } else {
-        const uint16_t *xs[1] = {xsb0};
-        const int mrs[1] = {mr0};
-        skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs, mrs, K, s0, s1, lane, acc);
-    }
+    const uint16_t *xs[1] = {xsb0};
+    const int mrs[1] = {mr0};
+    skinny_mainloop<NA, 1, PIPE>(wrow, wstep, sg.tiled, xs, mrs, K, s0, s1, lane, acc);
     store_partials<NA, 1>(outb + (size_t)ks * 16 * N, N, 1, row0, lane, mr0, mr0, acc);
 }
 
@@ -315,7 +260,7 @@ constexpr int LPIPE_SHORT = 6;
 constexpr int LPIPE_SHORT_MAX = 10;
 constexpr int LDS_X_BYTES = 40 * 1024;  // per workgroup: NB * slice_steps * 2 KiB
 
-template <int NA, int NB, int LP>
+template <int NA, int NB, int LP, bool F32X = false>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     extern __shared__ __align__(16) uint4 xl[];  // NB * kslice_steps * 2 KiB (<= LDS_X_BYTES)
     const int lane = threadIdx.x & 63, wv = wave_id();
@@ -401,10 +346,35 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     // alone (loads complete in issue order) while the weight loads are in flight.
     constexpr int XPT = LDS_X_BYTES / 16 / 256;  // uint4 per thread at most
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // register-friendly
-    u32x4 xr[XPT];
+    u32x4 xr[F32X ? 1 : XPT];
     const int per = n * 128;  // uint4 per tile
     const int xtot = (NB > 1 && nb > 1) ? 2 * per : per;
-    {
+    // F32X: the slice comes from args.xf's F32 rows: run i (step i / 64, lane i % 64
+    // of the split layout) is 8 values of row (i % 16), split hi/lo (split8, the
+    // values a split pass would store) on their way into LDS. The runs are read
+    // element by element, so the rows need only 4-byte alignment (the compiler
+    // issues 16-byte loads, which gfx950 serves at any 4-byte address).
+    constexpr int RPT = LDS_X_BYTES / 32 / 256;  // runs per thread at most
+    float xv[F32X ? RPT : 1][8];
+    const int runs = n * 64;
+    if constexpr (F32X) {
+#pragma unroll
+        for (int q = 0; q < RPT; q++) {
+            if (256 * q < runs) {
+                const int i = threadIdx.x + 256 * q;
+                const int ic = i < runs ? i : runs - 1;
+                const int l = ic & 63, row = l & 15, col = 32 * (s0 + (ic >> 6)) + 8 * (l >> 4);
+                if (row < mr0 && col < K) {
+                    const float *x_ = f32_src_at(args.xf, row, col);
+#pragma unroll
+                    for (int j = 0; j < 8; j++) xv[q][j] = x_[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; j++) xv[q][j] = 0.f;
+                }
+            }
+        }
+    } else {
         const uint4 *src0 = (const uint4 *)(xsb0 + (size_t)s0 * 2 * 64 * 8);
         const uint4 *src1 = (const uint4 *)(sg.xs1 + (size_t)s0 * 2 * 64 * 8);
         // element i of a split tile belongs to activation row i % 16 (= threadIdx.x % 16
@@ -426,10 +396,24 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     }
 #pragma unroll
     for (int u = 0; u < LP; u++) DBF_LOAD_W(u, s0 + u);
+    if constexpr (F32X) {
 #pragma unroll
-    for (int q = 0; q < XPT; q++) {
-        const int i = threadIdx.x + 256 * q;
-        if (i < xtot) *(u32x4 *)&xl[i] = xr[q];
+        for (int q = 0; q < RPT; q++) {
+            const int i = threadIdx.x + 256 * q;
+            if (i < runs) {
+                bf16x8 hi, lo;
+                split8(xv[q], hi, lo);
+                const int sl = i >> 6, l = i & 63;
+                xl[(sl * 2 + 0) * 64 + l] = __builtin_bit_cast(uint4, hi);
+                xl[(sl * 2 + 1) * 64 + l] = __builtin_bit_cast(uint4, lo);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < XPT; q++) {
+            const int i = threadIdx.x + 256 * q;
+            if (i < xtot) *(u32x4 *)&xl[i] = xr[q];
+        }
     }
     __syncthreads();
     if (tile >= sg.tiles) return;
@@ -599,16 +583,16 @@ GemmPlan gemm_plan_lds(int N, int K, int target_units, int nbmax) {
     return p;
 }
 
-template <int PIPE, int W, bool F32X = false>
+template <int PIPE, int W>
 static void go_splitk(const GemmArgs &a, hipStream_t s) {
     const dim3 grid((a.total_units + W - 1) / W), block(64 * W);
     launch_k(PROF_PROJ, PIPE == GEMM_PIPE_LONG ? "k_gemm_splitk(long)" : "k_gemm_splitk",
-             (k_gemm_splitk<GEMM_NA, PIPE, W, F32X>), grid, block, 0, s, a);
+             (k_gemm_splitk<GEMM_NA, PIPE, W>), grid, block, 0, s, a);
 }
 
 // NB split tiles per segment at most. With two, slices are at most LDS_X_STEPS_NB2
 // steps, so those launches always take the short-slice ring.
-template <int NB>
+template <int NB, bool F32X = false>
 static void go_lds(const GemmArgs &a, hipStream_t s) {
     static_assert(NB == 1 || LDS_X_STEPS_NB2 <= LPIPE_SHORT_MAX, "two-tile slices take the short ring");
     size_t lds = 0;
@@ -620,22 +604,16 @@ static void go_lds(const GemmArgs &a, hipStream_t s) {
     }
     const dim3 grid(a.total_units);  // total_units counts workgroups
     if (NB == 2 || steps <= LPIPE_SHORT_MAX)
-        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<GEMM_NA, NB, LPIPE_SHORT>), grid, dim3(256), lds, s, a);
+        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<GEMM_NA, NB, LPIPE_SHORT, F32X>), grid, dim3(256), lds, s, a);
     else
-        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<GEMM_NA, 1, LPIPE>), grid, dim3(256), lds, s, a);
+        launch_k(PROF_PROJ, "k_gemm_lds", (k_gemm_lds<GEMM_NA, 1, LPIPE, F32X>), grid, dim3(256), lds, s, a);
 }
 
 bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s) {
     if (a.total_units <= 0) return true;
-    if (a.xf_on) {  // one plain split-K segment reading F32 rows
-        if (a.lds_x || nbmax > 1 || a.nseg != 1 || a.seg[0].slots > 0) return false;
-        const int steps = a.seg[0].kslice_steps;
-        if (steps >= GEMM_LONG_SLICE)
-            go_splitk<GEMM_PIPE_LONG, SPLITK_W_LONG, true>(a, s);
-        else if (steps >= SPLITK_W_LONG_STEPS)
-            go_splitk<GEMM_PIPE, SPLITK_W_LONG, true>(a, s);
-        else
-            go_splitk<GEMM_PIPE, SPLITK_W, true>(a, s);
+    if (a.xf_on) {  // one plain LDS-staged segment reading F32 rows
+        if (!a.lds_x || nbmax > 1 || a.nseg != 1 || a.seg[0].slots > 0) return false;
+        go_lds<1, true>(a, s);
         return true;
     }
     if (a.lds_x) {

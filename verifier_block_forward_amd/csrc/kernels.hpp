@@ -53,8 +53,8 @@ struct GemmSeg {
     int pad_;
 };
 
-// F32 activation rows read by a split-K launch in place of a split tile, split
-// hi/lo as they are consumed: row m, column k is xf[m * xf_ld + k], or, with xf
+// F32 activation rows read by an LDS-staged launch in place of a split tile, split
+// hi/lo as they are staged: row m, column k is xf[m * xf_ld + k], or, with xf
 // null (the captured target layers gathered), xg[k / xg_cols][(xg_row0 + m) *
 // xg_ld + k % xg_cols]. xg_cols is a multiple of 8, so a lane's 8-column run lies
 // in one source.
@@ -71,7 +71,7 @@ struct GemmArgs {
     int nseg;
     int total_units;  // wave units (lds_x = 0) or workgroup units (lds_x = 1)
     int lds_x;        // 1: k_gemm_lds (activation slice staged in LDS)
-    int xf_on;        // 1: the (single, plain, split-K) segment reads xf, not xs0
+    int xf_on;        // 1: the (single, plain, LDS-staged) segment reads xf, not xs0
     GemmF32Src xf;
 };
 
@@ -98,7 +98,7 @@ inline int plan_units(const GemmPlan &p) {
 }
 
 // false (nothing launched) for a split-K launch with two split tiles per segment,
-// or an F32 activation source on anything but one plain split-K segment
+// or an F32 activation source on anything but one plain LDS-staged segment
 bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
