@@ -66,7 +66,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int H, qt, kt, I, Kin, rd;
     GemmPlan in, q, k, v, g, gate, up, down;
-    size_t xres, x1, xs_blk, xs_hctx, xs_h, xs_o, xs_ff, qbuf, gbuf, attn;
+    size_t xres, x1, xs_blk, xs_hctx, xs_o, xs_ff, qbuf, gbuf, attn;
     size_t ssp_x, ssp_x1, ssp_ctx, ssp_e, ssp_h;
     int ncb, ncb16;  // row-scale partials per row: 64-column (row kernels) and 16-column (O epilogue)
     size_t p_in0, p_in1, p_q, p_k, p_v, p_g, p_gate, p_up, p_down;
@@ -122,7 +122,6 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.x1 = take((size_t)DBF_MAX_M * p.H * f);
     p.xs_blk = take(split_tile_bytes(p.H));
     p.xs_hctx = take(split_tile_bytes(p.H));
-    p.xs_h = take(split_tile_bytes(p.H));
     p.xs_o = take(split_tile_bytes(p.qt));
     p.xs_ff = take(split_tile_bytes(p.I > 0 ? p.I : 32));
     p.ncb = (p.H + 63) / 64;
@@ -130,8 +129,10 @@ Plan make_plan(const dbf_config &c, int M, int R) {
     p.ssp_x = take((size_t)16 * p.ncb * f);
     p.ssp_x1 = take((size_t)16 * p.ncb16 * f);
     p.ssp_ctx = take((size_t)16 * p.ncb * f);
-    p.ssp_e = take((size_t)16 * p.ncb * f);
-    p.ssp_h = take((size_t)16 * p.ncb * f);
+    // MTP: per-k-slice sums of squares of the e and h rows, written by the eh launch
+    const int n_ssq = p.ncb > p.in.ksplit ? p.ncb : p.in.ksplit;
+    p.ssp_e = take((size_t)16 * n_ssq * f);
+    p.ssp_h = take((size_t)16 * n_ssq * f);
     p.qbuf = take((size_t)DBF_MAX_M * p.qt * f);
     p.gbuf = take((size_t)DBF_MAX_M * p.qt * f);
     p.attn = take((size_t)ATT_CHUNKS_MAX * DBF_MAX_M * c.n_q_heads * (c.head_dim + ATT_PART_EXTRA) * f);
@@ -233,9 +234,9 @@ struct SegList {
         s.out_stride = (long long)pl.ksplit * 16 * N;
         a.total_units += (slots - 1) * plan_units(pl);
     }
-    // the launch's one segment reads F32 rows instead of its split tile
-    void f32_source(const GemmF32Src &s) {
-        a.xf = s;
+    // segment seg (0 or 1) reads F32 rows instead of its split tile
+    void f32_source(int seg, const GemmF32Src &s) {
+        a.xf[seg] = s;
         a.xf_on = 1;
     }
     int launch(hipStream_t st) {
@@ -438,7 +439,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     const long long P0 = cache->seq_len;
     float *xres = at<float>(ws, p.xres), *x1 = at<float>(ws, p.x1);
     uint16_t *xs_blk = at<uint16_t>(ws, p.xs_blk);
-    uint16_t *xs_hctx = at<uint16_t>(ws, p.xs_hctx), *xs_h = at<uint16_t>(ws, p.xs_h);
+    uint16_t *xs_hctx = at<uint16_t>(ws, p.xs_hctx);
     uint16_t *xs_o = at<uint16_t>(ws, p.xs_o), *xs_ff = at<uint16_t>(ws, p.xs_ff);
     float *qbuf = at<float>(ws, p.qbuf), *gbuf = at<float>(ws, p.gbuf);
     float *attn_part = at<float>(ws, p.attn);
@@ -486,7 +487,7 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
                 src.xg_ld = io->ctx_ld;
                 src.xg_row0 = io->ctx_row0;
             }
-            sl.f32_source(src);
+            sl.f32_source(0, src);
             CHECK(sl.launch(st));
             ColArgs h = col();
             h.M = R;
@@ -501,29 +502,31 @@ int draft_block_forward(const dbf_config *cfg, const dbf_weights *w, dbf_kv_cach
     } else {
         // x = RMSNorm(e, enorm) eh_embed^T + RMSNorm(h, hnorm) eh_hidden^T (eps 1e-6)
         float *ssp_e = at<float>(ws, p.ssp_e), *ssp_h = at<float>(ws, p.ssp_h);
-        ColArgs e = col();
-        e.M = M;
-        e.tokens = io->tokens;  // chained steps: embed_t = embed[token]
-        e.embed = (const uint16_t *)w->embed.data;
-        e.V = c.vocab;
-        e.base = io->x0;
-        e.ldb = H;
-        e.w = (const float *)w->enorm.data;
-        e.xs = xs_blk;
-        e.ssp_out = ssp_e;
-        ColArgs h = e;
-        h.tokens = nullptr;  // prev_hidden rows are given, never gathered
-        h.embed = nullptr;
-        h.base = io->ctx;
-        h.w = (const float *)w->hnorm.data;
-        h.xs = xs_h;
-        h.ssp_out = ssp_h;
-        launch_colsum2(e, h, st);  // embed_t and prev_hidden rows in one launch
+        // The eh launch stages e (embed[token] for chained steps, else x0) and h
+        // (prev_hidden) itself, enorm / hnorm applied, and writes each k-slice's
+        // sums of squares of the raw rows; the pass after it forms the row scales.
         SegList sl(M);
-        sl.add(w->eh_embed, H, H, p.in, at<float>(ws, p.p_in0), xs_blk);
-        sl.add(w->eh_hidden, H, H, p.in, at<float>(ws, p.p_in1), xs_h);
+        sl.add(w->eh_embed, H, H, p.in, at<float>(ws, p.p_in0), nullptr);
+        sl.add(w->eh_hidden, H, H, p.in, at<float>(ws, p.p_in1), nullptr);
+        GemmF32Src se{}, sh{};
+        se.xf = io->x0;
+        se.xf_ld = H;
+        se.tokens = io->tokens;
+        se.embed = (const uint16_t *)w->embed.data;
+        se.V = c.vocab;
+        se.w = (const float *)w->enorm.data;
+        se.ssq = ssp_e;
+        se.ssq_ld = p.in.ksplit;
+        sh.xf = io->ctx;  // prev_hidden rows are given, never gathered
+        sh.xf_ld = H;
+        sh.w = (const float *)w->hnorm.data;
+        sh.ssq = ssp_h;
+        sh.ssq_ld = p.in.ksplit;
+        sl.f32_source(0, se);
+        sl.f32_source(1, sh);
         CHECK(sl.launch(st));
         ColArgs x = col();
+        x.ncb_in = p.in.ksplit;  // the row-scale partials are per k-slice
         x.M = M;
         x.p0 = at<float>(ws, p.p_in0);
         x.ks0 = p.in.ksplit;

@@ -357,17 +357,34 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
     constexpr int RPT = LDS_X_BYTES / 32 / 256;  // runs per thread at most
     float xv[F32X ? RPT : 1][8];
     const int runs = n * 64;
+    // every run of this thread is of row threadIdx.x % 16 (256 q + i keeps i % 16)
+    float ssq_part = 0.f;
     if constexpr (F32X) {
+        const GemmF32Src &xs_ = args.xf[si];
 #pragma unroll
         for (int q = 0; q < RPT; q++) {
             if (256 * q < runs) {
                 const int i = threadIdx.x + 256 * q;
                 const int ic = i < runs ? i : runs - 1;
                 const int l = ic & 63, row = l & 15, col = 32 * (s0 + (ic >> 6)) + 8 * (l >> 4);
-                if (row < mr0 && col < K) {
-                    const float *x_ = f32_src_at(args.xf, row, col);
+                if (row < mr0 && col < K && i < runs) {
+                    if (xs_.tokens) {
+                        int t = xs_.tokens[row];
+                        t = t < 0 ? 0 : (t >= xs_.V ? xs_.V - 1 : t);
+                        const uint16_t *e_ = xs_.embed + (size_t)t * xs_.xf_ld + col;
 #pragma unroll
-                    for (int j = 0; j < 8; j++) xv[q][j] = x_[j];
+                        for (int j = 0; j < 8; j++) xv[q][j] = bf16_to_f32(e_[j]);
+                    } else {
+                        const float *x_ = f32_src_at(xs_, row, col);
+#pragma unroll
+                        for (int j = 0; j < 8; j++) xv[q][j] = x_[j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; j++) ssq_part += xv[q][j] * xv[q][j];
+                    if (xs_.w) {
+#pragma unroll
+                        for (int j = 0; j < 8; j++) xv[q][j] *= xs_.w[col + j];
+                    }
                 } else {
 #pragma unroll
                     for (int j = 0; j < 8; j++) xv[q][j] = 0.f;
@@ -407,6 +424,18 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs args) {
                 xl[(sl * 2 + 0) * 64 + l] = __builtin_bit_cast(uint4, hi);
                 xl[(sl * 2 + 1) * 64 + l] = __builtin_bit_cast(uint4, lo);
             }
+        }
+        const GemmF32Src &xs_ = args.xf[si];
+        if (xs_.ssq && grp == 0) {  // the slice's sum of squares per row, in a fixed order
+            __shared__ float ssq_w[4][16];
+            float v = ssq_part;
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if ((threadIdx.x & 63) < 16) ssq_w[wv][threadIdx.x & 15] = v;
+            __syncthreads();
+            if (threadIdx.x < 16 && (int)threadIdx.x < mr0)
+                xs_.ssq[(size_t)threadIdx.x * xs_.ssq_ld + ks] =
+                    (ssq_w[0][threadIdx.x] + ssq_w[1][threadIdx.x]) + (ssq_w[2][threadIdx.x] + ssq_w[3][threadIdx.x]);
         }
     } else {
 #pragma unroll
@@ -611,8 +640,10 @@ static void go_lds(const GemmArgs &a, hipStream_t s) {
 
 bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s) {
     if (a.total_units <= 0) return true;
-    if (a.xf_on) {  // one plain LDS-staged segment reading F32 rows
-        if (!a.lds_x || nbmax > 1 || a.nseg != 1 || a.seg[0].slots > 0) return false;
+    if (a.xf_on) {  // one or two plain LDS-staged segments reading F32 rows
+        if (!a.lds_x || nbmax > 1 || a.nseg > 2) return false;
+        for (int i = 0; i < a.nseg; i++)
+            if (a.seg[i].slots > 0) return false;
         go_lds<1, true>(a, s);
         return true;
     }

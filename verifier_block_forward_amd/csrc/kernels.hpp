@@ -58,12 +58,23 @@ struct GemmSeg {
 // null (the captured target layers gathered), xg[k / xg_cols][(xg_row0 + m) *
 // xg_ld + k % xg_cols]. xg_cols is a multiple of 8, so a lane's 8-column run lies
 // in one source.
+// With tokens set, row m is instead the BF16 row embed[clamp(tokens[m], 0, V-1)]
+// (xf_ld columns). With w set, column k is multiplied by w[k] after it is read.
+// With ssq set, the workgroups of the segment's first row-tile group write, for
+// each row m and k-slice ks, the sum of squares of the row's values over the slice
+// (before w) to ssq[m * ssq_ld + ks].
 struct GemmF32Src {
     const float *xf;
     long long xf_ld;
     const float *xg[8];
     long long xg_ld;
     int xg_cols, xg_row0;
+    const int32_t *tokens;
+    const uint16_t *embed;
+    int V;
+    const float *w;
+    float *ssq;
+    int ssq_ld;
 };
 
 struct GemmArgs {
@@ -71,8 +82,8 @@ struct GemmArgs {
     int nseg;
     int total_units;  // wave units (lds_x = 0) or workgroup units (lds_x = 1)
     int lds_x;        // 1: k_gemm_lds (activation slice staged in LDS)
-    int xf_on;        // 1: the (single, plain, LDS-staged) segment reads xf, not xs0
-    GemmF32Src xf;
+    int xf_on;        // 1: the plain LDS-staged segments read xf[segment], not xs0
+    GemmF32Src xf[2];
 };
 
 // Work decomposition of one segment: rows per wave unit = 16 * GEMM_NA; lds selects
@@ -98,7 +109,7 @@ inline int plan_units(const GemmPlan &p) {
 }
 
 // false (nothing launched) for a split-K launch with two split tiles per segment,
-// or an F32 activation source on anything but one plain LDS-staged segment
+// or F32 activation sources on anything but one or two plain LDS-staged segments
 bool launch_gemm(const GemmArgs &a, int nbmax, hipStream_t s);
 
 // ---------------------------------------------------------------------------
